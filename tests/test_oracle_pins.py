@@ -1,0 +1,453 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics
+fix, never against the oracle itself or the GPU path.
+
+Citations are to the DFlash-TfM summary page, section "Verifica dell'Albero
+Senza Rollback per GDN" (rollback-free tree verification for GDN): the state
+update formula, the topological order, the ancestor interaction matrices X
+and Y, the system (I+X)U = beta V solved without updating the state, and the
+delayed commit along the accepted branch.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import gdn_synth as gs
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+EXACT = dict(rtol=0, atol=0)
+
+
+def _rand_set(seed, parent, H=2, dk=6, dv=5):
+    return gs.make_set(np.asarray(parent)[None, :] if np.ndim(parent) == 1 else parent,
+                       H, dk, dv, "fp32", seed)
+
+
+# ---------------------------------------------------------------------------
+# 1. the hand-worked example (pencil arithmetic, fixture carries the steps)
+# ---------------------------------------------------------------------------
+def _golden():
+    with open(os.path.join(GOLDEN, "hand_tree3_d2.json")) as f:
+        g = json.load(f)
+    n = len(g["parent"])
+    q = np.array(g["q"], float).reshape(1, n, 1, 2)
+    k = np.array(g["k"], float).reshape(1, n, 1, 2)
+    v = np.array(g["v"], float).reshape(1, n, 1, 2)
+    a = np.array(g["alpha"], float).reshape(1, n, 1)
+    b = np.array(g["beta"], float).reshape(1, n, 1)
+    p = np.array(g["parent"], np.int32).reshape(1, n)
+    S0 = np.array(g["S0"], float).reshape(1, 1, 2, 2)
+    return g, q, k, v, a, b, p, S0
+
+
+@pytest.mark.parametrize("memo", [True, False])
+def test_golden_hand_example_verify(memo):
+    g, q, k, v, a, b, p, S0 = _golden()
+    out, st = oracle.verify(q, k, v, a, b, p, S0, memo=memo)
+    assert st[0] == 0
+    np.testing.assert_allclose(out[0, :, 0, :], np.array(g["out"]), rtol=0, atol=1e-14)
+    ob, _ = oracle.brute_verify(q, k, v, a, b, p, S0)
+    np.testing.assert_allclose(ob[0, :, 0, :], np.array(g["out"]), rtol=0, atol=1e-14)
+
+
+def test_golden_hand_example_commit_and_index():
+    g, q, k, v, a, b, p, S0 = _golden()
+    for key, want in g["commit"].items():
+        path = np.array([want["path"]], np.int32)
+        S, st = oracle.commit(S0, path, np.array([path.shape[1]], np.int32), k, v, a, b, p)
+        assert st[0] == 0
+        np.testing.assert_allclose(S[0, 0], np.array(want["S"]), rtol=0, atol=1e-14)
+    depth, anc, st = oracle.index(p)
+    assert depth[0].tolist() == g["depth"]
+    assert anc[0, :, 0].tolist() == g["anc_bits"]
+
+
+# ---------------------------------------------------------------------------
+# 2. brute force: every root-to-leaf branch run separately
+# ---------------------------------------------------------------------------
+def test_memo_equals_literal_bitwise():
+    ts = gs.make_config(1, heads=4)
+    o1, _ = oracle.verify_set(ts, memo=True)
+    o2, _ = oracle.verify_set(ts, memo=False)
+    assert np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("chain", [False, True])
+def test_config0_vs_branch_brute_force(chain):
+    ts = gs.make_config(0, chain=chain)
+    out, st = oracle.verify_set(ts)
+    ob, sb = oracle.brute_verify(ts.q, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, ts.S0)
+    assert st.tolist() == sb.tolist() == [0]
+    assert oracle.rel_err(out, ob) < 1e-13
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small_trees_vs_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 13))
+    parent = gs.random_recursive_tree(rng, n)
+    if seed % 3 == 0 and n > 3:                      # a forest: several roots
+        parent[n // 2] = -1
+    ts = _rand_set(100 + seed, parent, H=3, dk=int(rng.integers(1, 9)), dv=int(rng.integers(1, 9)))
+    out, _ = oracle.verify_set(ts)
+    ob, _ = oracle.brute_verify(ts.q, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, ts.S0)
+    assert oracle.rel_err(out, ob) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# 3. chain tree == ordinary sequential GDN decoding
+# ---------------------------------------------------------------------------
+def test_chain_equals_sequential_decoding():
+    n, H, d = 24, 2, 8
+    ts = _rand_set(7, gs.chain_tree(n), H=H, dk=d, dv=d)
+    out, _ = oracle.verify_set(ts)
+    for h in range(H):
+        S = ts.S0[0, h].astype(float)
+        for t in range(n):
+            kk, vv = ts.k[0, t, h].astype(float), ts.v[0, t, h].astype(float)
+            a, b = float(ts.alpha[0, t, h]), float(ts.beta[0, t, h])
+            # token-by-token decoding: decay, erase along k, write v along k
+            S = a * S - a * b * np.outer(kk, kk @ S) + b * np.outer(kk, vv)
+            np.testing.assert_allclose(out[0, t, h], S.T @ ts.q[0, t, h], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# 4. closed forms
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_closed_form_query_equals_key_beta_one(seed):
+    """q_i = k_i, beta = 1, |k| = 1: S_i^T k_i = alpha (S_p^T (I - k k^T) k) + v = v_i
+    for every alpha and S0, on any tree."""
+    rng = np.random.default_rng(seed)
+    parent = gs.random_recursive_tree(rng, 16)
+    ts = _rand_set(seed, parent, H=2, dk=7, dv=5)
+    k = ts.k.astype(float)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    out, _ = oracle.verify(k, k, ts.v, ts.alpha, np.ones_like(ts.beta), ts.parent, ts.S0)
+    np.testing.assert_allclose(out, ts.v.astype(float), rtol=0, atol=1e-13)
+
+
+def test_closed_form_single_node():
+    """n = 1: o = alpha S0^T q + beta (q.k) (v - alpha S0^T k)."""
+    ts = _rand_set(3, np.array([-1]), H=4, dk=9, dv=6)
+    out, _ = oracle.verify_set(ts)
+    for h in range(4):
+        q, k, v = (x[0, 0, h].astype(float) for x in (ts.q, ts.k, ts.v))
+        a, b = float(ts.alpha[0, 0, h]), float(ts.beta[0, 0, h])
+        S0 = ts.S0[0, h].astype(float)
+        want = a * S0.T @ q + b * (q @ k) * (v - a * S0.T @ k)
+        np.testing.assert_allclose(out[0, 0, h], want, rtol=1e-13, atol=1e-14)
+
+
+def test_beta_zero_alpha_one_is_plain_matmul():
+    ts = gs.make_config(1, heads=3)
+    out, _ = oracle.verify(ts.q, ts.k, ts.v, np.ones_like(ts.alpha), np.zeros_like(ts.beta),
+                           ts.parent, ts.S0)
+    want = np.einsum("bnhk,bhkv->bnhv", ts.q.astype(float), ts.S0.astype(float))
+    assert oracle.rel_err(out, want) < 1e-13
+
+
+def test_beta_zero_gives_path_decay_times_readout():
+    ts = gs.make_config(1, heads=2)
+    out, _ = oracle.verify(ts.q, ts.k, ts.v, ts.alpha, np.zeros_like(ts.beta), ts.parent, ts.S0)
+    for i in range(ts.parent.shape[1]):
+        decay = np.ones(2)
+        for t in gs.path_to(ts.parent[0], i):
+            decay *= ts.alpha[0, t, :2]
+        for h in range(2):
+            want = decay[h] * ts.S0[0, h].astype(float).T @ ts.q[0, i, h]
+            np.testing.assert_allclose(out[0, i, h], want, rtol=1e-12, atol=1e-14)
+
+
+def test_orthonormal_keys_write_rows():
+    """alpha = 1, beta = 1, S0 = 0 and k_s = e_{depth(s)}: the keys on any path
+    are orthonormal, so S_i = sum_{s on path(i)} e_{depth(s)} v_s^T and
+    o_i = sum_s q_i[depth(s)] v_s."""
+    rng = np.random.default_rng(5)
+    parent = gs.random_recursive_tree(rng, 20, max_depth=6)
+    ts = _rand_set(5, parent, H=1, dk=8, dv=4)
+    depth = gs._depths(parent)
+    k = np.zeros_like(ts.k, dtype=float)
+    for i in range(20):
+        k[0, i, 0, depth[i]] = 1.0
+    out, _ = oracle.verify(ts.q, k, ts.v, np.ones_like(ts.alpha), np.ones_like(ts.beta),
+                           ts.parent, np.zeros_like(ts.S0))
+    for i in range(20):
+        want = sum(ts.q[0, i, 0, depth[s]] * ts.v[0, s, 0].astype(float)
+                   for s in gs.path_to(parent, i))
+        np.testing.assert_allclose(out[0, i, 0], want, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# 5. the chunked form (independent derivation: X, Y, (I+X)U = RHS, output)
+# ---------------------------------------------------------------------------
+def chunked_form(q, k, v, alpha, beta, parent, S0):
+    """Own algebra from the update formula: with u_t = beta_t (v_t - alpha_t S_{t-1}^T k_t)
+    the state is S_t = alpha_t S_{t-1} + k_t u_t^T; with g_i the log-decay summed
+    over the path of i,
+        u_i + beta_i sum_{s in anc(i)} e^{g_i-g_s} (k_i.k_s) u_s = beta_i (v_i - e^{g_i} S0^T k_i)
+        o_i = e^{g_i} S0^T q_i + sum_{s in anc*(i)} e^{g_i-g_s} (q_i.k_s) u_s."""
+    batch, n, H, dk = q.shape
+    out = np.zeros(v.shape, float)
+    for b in range(batch):
+        paths = [gs.path_to(parent[b], i) for i in range(n)]
+        for h in range(H):
+            Q, K, V = (x[b, :, h].astype(float) for x in (q, k, v))
+            la = np.log(alpha[b, :, h].astype(float))
+            g = np.array([la[p].sum() for p in paths])
+            bt = beta[b, :, h].astype(float)
+            X = np.zeros((n, n))
+            Y = np.zeros((n, n))
+            for i in range(n):
+                for s in paths[i]:
+                    w = np.exp(g[i] - g[s])
+                    Y[i, s] = w * Q[i] @ K[s]
+                    if s != i:
+                        X[i, s] = bt[i] * w * K[i] @ K[s]
+            S = S0[b, h].astype(float)
+            rhs = bt[:, None] * (V - np.exp(g)[:, None] * (K @ S))
+            U = np.linalg.solve(np.eye(n) + X, rhs)
+            out[b, :, h] = np.exp(g)[:, None] * (Q @ S) + Y @ U
+    return out
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_chunked_form_matches_oracle(cfg):
+    ts = gs.make_config(cfg, heads=4)
+    out, _ = oracle.verify_set(ts)
+    want = chunked_form(ts.q, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, ts.S0)
+    assert oracle.rel_err(out, want) < 1e-11
+
+
+def test_chunked_form_deep_chain_and_bushes():
+    n = 40
+    for parent in (gs.chain_tree(n), gs.star_tree(n), gs.kary_bfs_tree(n, 4)):
+        ts = _rand_set(11, parent, H=2, dk=8, dv=8)
+        out, _ = oracle.verify_set(ts)
+        want = chunked_form(ts.q, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, ts.S0)
+        assert oracle.rel_err(out, want) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# 6. structural invariants
+# ---------------------------------------------------------------------------
+def _relabel(parent, rng):
+    n = len(parent)
+    placed, order = set(), []
+    ready = [i for i in range(n) if parent[i] < 0]
+    while ready:
+        j = ready.pop(int(rng.integers(0, len(ready))))
+        order.append(j)
+        placed.add(j)
+        ready += [c for c in range(n) if parent[c] == j]
+    perm = np.array(order)            # new id -> old id
+    inv = np.empty(n, int)
+    inv[perm] = np.arange(n)
+    newp = np.array([-1 if parent[o] < 0 else inv[parent[o]] for o in perm], np.int32)
+    return perm, newp
+
+
+def test_relabeling_permutes_outputs():
+    rng = np.random.default_rng(9)
+    ts = gs.make_config(1, heads=3)
+    out, _ = oracle.verify_set(ts)
+    perm, newp = _relabel(ts.parent[0], rng)
+    assert not np.array_equal(perm, np.arange(len(perm)))
+    assert all(newp[i] < i for i in range(len(newp)))
+    sl = lambda x: x[:, perm]
+    o2, _ = oracle.verify(sl(ts.q), sl(ts.k), sl(ts.v), sl(ts.alpha), sl(ts.beta),
+                          newp[None], ts.S0)
+    assert np.array_equal(o2, out[:, perm])
+
+
+def test_non_descendants_unaffected():
+    ts = gs.make_config(1, heads=2)
+    out, _ = oracle.verify_set(ts)
+    par = ts.parent[0]
+    j = 5
+    desc = {i for i in range(len(par)) if j in set(gs.path_to(par, i))}
+    q, k, v = ts.q.copy(), ts.k.copy(), ts.v.copy()
+    a, b = ts.alpha.copy(), ts.beta.copy()
+    k[0, j] = np.roll(k[0, j], 3, axis=-1)
+    v[0, j] *= -2.0
+    a[0, j] *= 0.5
+    b[0, j] = 1.0 - b[0, j]
+    o2, _ = oracle.verify(q, k, v, a, b, ts.parent, ts.S0)
+    for i in range(len(par)):
+        same = np.array_equal(o2[0, i], out[0, i])
+        assert same == (i not in desc), i
+
+
+def test_linear_in_v_and_state():
+    ts = gs.make_config(1, heads=2)
+    rng = np.random.default_rng(1)
+    V2 = rng.standard_normal(ts.v.shape)
+    S2 = rng.standard_normal(ts.S0.shape)
+    f = lambda V, S: oracle.verify(ts.q, ts.k, V, ts.alpha, ts.beta, ts.parent, S)[0]
+    lhs = f(ts.v + 0.5 * V2, ts.S0 + 0.5 * S2)
+    rhs = f(ts.v, ts.S0) + 0.5 * f(V2, S2)
+    assert oracle.rel_err(lhs, rhs) < 1e-12
+
+
+def test_output_depends_only_on_own_path_prefix():
+    """Every node of the batch tree equals a chain run along its own path."""
+    ts = gs.make_config(1, heads=2)
+    out, _ = oracle.verify_set(ts)
+    for i in (0, 7, 19, 31):
+        p = gs.path_to(ts.parent[0], i)
+        sl = lambda x: x[:, p]
+        o2, _ = oracle.verify(sl(ts.q), sl(ts.k), sl(ts.v), sl(ts.alpha), sl(ts.beta),
+                              gs.chain_tree(len(p))[None], ts.S0)
+        assert np.array_equal(o2[0, -1], out[0, i])
+
+
+# ---------------------------------------------------------------------------
+# 7. commit: state along the accepted path, then verify from it
+# ---------------------------------------------------------------------------
+def _subtree(parent, a):
+    """descendants of a (excluding a) re-rooted under the committed state"""
+    d = [i for i in range(len(parent)) if i != a and a in set(gs.path_to(parent, i))]
+    m = {o: j for j, o in enumerate(d)}
+    newp = np.array([-1 if parent[o] == a else m[parent[o]] for o in d], np.int32)
+    return np.array(d, int), newp
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_commit_then_verify_subtree(cfg):
+    ts = gs.make_config(cfg) if cfg == 0 else gs.make_config(cfg, heads=3)
+    out, _ = oracle.verify_set(ts)
+    par = ts.parent[0]
+    # pick an interior node with descendants
+    a = next(i for i in range(1, len(par)) if (par == i).any())
+    path = gs.path_to(par, a)[None]
+    S_a, st = oracle.commit(ts.S0, path, np.array([path.shape[1]], np.int32), ts.k, ts.v,
+                            ts.alpha, ts.beta, ts.parent)
+    assert st[0] == 0
+    # committed state reads out node a's verify output
+    for h in range(ts.q.shape[2]):
+        np.testing.assert_allclose(S_a[0, h].T @ ts.q[0, a, h], out[0, a, h], rtol=1e-13, atol=1e-14)
+    d, newp = _subtree(par, a)
+    sl = lambda x: x[:, d]
+    o2, _ = oracle.verify(sl(ts.q), sl(ts.k), sl(ts.v), sl(ts.alpha), sl(ts.beta),
+                          newp[None], S_a)
+    assert np.array_equal(o2, out[:, d])
+
+
+def test_commit_composition():
+    ts = gs.make_config(1, heads=3)
+    par = ts.parent[0]
+    leaf = int(ts.accepted[0])
+    full = gs.path_to(par, leaf)
+    a = int(full[len(full) // 2])
+    p1 = gs.path_to(par, a)
+    S1, _ = oracle.commit(ts.S0, p1[None], np.array([len(p1)], np.int32), ts.k, ts.v,
+                          ts.alpha, ts.beta, ts.parent)
+    d, newp = _subtree(par, a)
+    m = {o: j for j, o in enumerate(d)}
+    p2 = np.array([m[o] for o in full[len(p1):]], np.int32)
+    sl = lambda x: x[:, d]
+    S12, _ = oracle.commit(S1, p2[None], np.array([len(p2)], np.int32), sl(ts.k), sl(ts.v),
+                           sl(ts.alpha), sl(ts.beta), newp[None])
+    Sf, _ = oracle.commit(ts.S0, full[None], np.array([len(full)], np.int32), ts.k, ts.v,
+                          ts.alpha, ts.beta, ts.parent)
+    assert np.array_equal(S12, Sf)
+
+
+def test_commit_vs_brute_and_empty_path():
+    ts = gs.make_config(1, heads=2)
+    path, plen = ts.paths()
+    S, st = oracle.commit_set(ts)
+    Sb, sb = oracle.brute_commit(ts.S0, path, plen, ts.k, ts.v, ts.alpha, ts.beta, ts.parent)
+    assert st[0] == sb[0] == 0
+    assert oracle.rel_err(S, Sb) < 1e-13
+    S0, st = oracle.commit(ts.S0, path, np.zeros(1, np.int32), ts.k, ts.v, ts.alpha,
+                           ts.beta, ts.parent)
+    assert st[0] == 0 and np.array_equal(S0, ts.S0.astype(float))
+
+
+# ---------------------------------------------------------------------------
+# 8. faults and tree indexing
+# ---------------------------------------------------------------------------
+def test_verify_bad_parent_faults_only_that_sequence():
+    ts = gs.make_config(2, batch=3, heads=2)
+    par = ts.parent.copy()
+    par[1, 10] = 12                     # parent after child
+    out, st = oracle.verify(ts.q, ts.k, ts.v, ts.alpha, ts.beta, par, ts.S0)
+    assert st.tolist() == [0, 1, 0]
+    assert np.isnan(out[1]).all() and np.isfinite(out[[0, 2]]).all()
+    par[2, 0] = -2
+    _, st = oracle.verify(ts.q, ts.k, ts.v, ts.alpha, ts.beta, par, ts.S0)
+    assert st.tolist() == [0, 1, 1]
+
+
+@pytest.mark.parametrize("case", ["unconnected", "not_root", "id_range", "too_long",
+                                  "negative", "not_increasing"])
+def test_commit_bad_path_leaves_state(case):
+    ts = gs.make_config(2, batch=2, heads=2)
+    path, plen = ts.paths(max_path=16)
+    p = path.copy()
+    L = plen.copy()
+    if case == "unconnected":
+        p[0, 2] = p[0, 3] if L[0] > 3 else 63
+    elif case == "not_root":
+        p[0, 0] = p[0, 1]
+    elif case == "id_range":
+        p[0, 1] = 64
+    elif case == "too_long":
+        L[0] = 17
+    elif case == "negative":
+        L[0] = -1
+    elif case == "not_increasing":
+        par = ts.parent.copy()
+        par[0, 1], par[0, 2] = 2, 0      # 0 -> 2 -> 1 (1's parent is later)
+        p[0, :3] = [0, 2, 1]
+        L[0] = 3
+        S, st = oracle.commit(ts.S0, p, L, ts.k, ts.v, ts.alpha, ts.beta, par)
+        assert st.tolist() == [2, 0]
+        assert np.array_equal(S[0], ts.S0[0].astype(float))
+        return
+    S, st = oracle.commit(ts.S0, p, L, ts.k, ts.v, ts.alpha, ts.beta, ts.parent)
+    Sb, sb = oracle.brute_commit(ts.S0, p, L, ts.k, ts.v, ts.alpha, ts.beta, ts.parent)
+    assert st.tolist() == sb.tolist() == [2, 0]
+    assert np.array_equal(S[0], ts.S0[0].astype(float))
+    assert not np.array_equal(S[1], ts.S0[1].astype(float))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_path_and_index_vs_brute(seed):
+    rng = np.random.default_rng(seed)
+    batch, n = 6, int(rng.integers(1, 70))
+    par = np.stack([gs.random_recursive_tree(rng, n) for _ in range(batch)])
+    acc = rng.integers(0, n, size=batch).astype(np.int32)
+    if n > 4:
+        par[1, n - 1] = n - 1            # self parent: malformed
+        par[2, 3] = -3
+        acc[1] = n - 1
+        acc[3] = n                       # out of range
+    for mp in (1, 4, n + 1):
+        a = oracle.path(par, acc, mp)
+        b = oracle.brute_path(par, acc, mp)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+    a = oracle.index(par)
+    b = oracle.brute_index(par)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_generators_topological_and_deterministic():
+    for i in range(5):
+        t1 = gs.make_config(i)
+        t2 = gs.make_config(i)
+        assert np.array_equal(t1.parent, t2.parent)
+        assert np.array_equal(t1.q, t2.q) and np.array_equal(t1.S0, t2.S0)
+        for par in t1.parent:
+            assert par[0] == -1 and all(-1 <= par[j] < j for j in range(len(par)))
+    d, _, _ = oracle.index(gs.make_config(2).parent)
+    assert d.max() <= 12
+    d, _, _ = oracle.index(gs.make_config(1).parent)
+    assert d.max() <= 8
+    d, _, _ = oracle.index(gs.make_config(3).parent)
+    assert d[:16].max() == 127 and d[32:].max() <= 16
