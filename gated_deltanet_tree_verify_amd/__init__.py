@@ -1,0 +1,223 @@
+"""Rollback-free tree verification and commit for Gated DeltaNet on MI355X.
+
+Thin Python binding over the C ABI of libgdntree.so (include/gdn_tree.h).
+Every function here only marshals arguments: it checks torch tensors, takes
+their device pointers and the current HIP stream, and calls the entry point
+of the same name.  All computation runs in the library's HIP kernels; there
+is no CPU or PyTorch fallback, and a missing library raises.
+
+    verify(q, k, v, alpha, beta, parent, S0)        -> out   (gdn_tree_verify)
+    commit(S, path, path_len, k, v, alpha, beta, parent)     (gdn_tree_commit, in place)
+    path(parent, accepted, max_path)                -> (path, path_len)
+    index(parent)                                   -> (depth, anc)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["load", "lib_path", "verify", "commit", "path", "index", "status_string",
+           "GdnError", "FAULT_BAD_PARENT", "FAULT_BAD_PATH", "DTYPE_F32", "DTYPE_BF16",
+           "MAX_NODES", "MAX_DIM", "build"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libgdntree.so"
+
+FAULT_BAD_PARENT = 1
+FAULT_BAD_PATH = 2
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+MAX_NODES = 128
+MAX_DIM = 128
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GdnError(RuntimeError):
+    """A negative gdn_status returned by the library."""
+
+    def __init__(self, fn: str, code: int, text: str):
+        super().__init__(f"{fn}: {text} (status {code})")
+        self.code = code
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libgdntree.so in-tree (hipcc, gfx950)."""
+    from . import _build as _b
+    return _b.build(verbose=verbose)
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdntree.so from the package directory (raises if absent)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = lib_path()
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is not built; run gated_deltanet_tree_verify_amd.build()")
+        lib = ctypes.CDLL(p)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        lib.gdn_tree_verify.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, P, P]
+        lib.gdn_tree_verify.restype = I
+        lib.gdn_tree_commit.argtypes = [P, P, P, I, P, P, I, P, P, P, I, I, I, I, I, P, P]
+        lib.gdn_tree_commit.restype = I
+        lib.gdn_tree_path.argtypes = [P, P, P, P, I, I, I, P, P]
+        lib.gdn_tree_path.restype = I
+        lib.gdn_tree_index.argtypes = [P, P, P, I, I, P, P]
+        lib.gdn_tree_index.restype = I
+        lib.gdn_status_string.argtypes = [I]
+        lib.gdn_status_string.restype = ctypes.c_char_p
+        lib.gdn_tree_abi_version.argtypes = []
+        lib.gdn_tree_abi_version.restype = I
+        _lib = lib
+        return lib
+
+
+def status_string(code: int) -> str:
+    return load().gdn_status_string(int(code)).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, code):
+    if code != 0:
+        raise GdnError(fn, code, status_string(code))
+
+
+def _need(t, name, dtypes, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _qkv_dtype(q):
+    torch = _torch()
+    return DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F32
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def verify(q, k, v, alpha, beta, parent, S0, out=None, status=None, stream=None):
+    """gdn_tree_verify: fp32 out [batch][n][H][d_v]; S0 is never written."""
+    torch = _torch()
+    lib = load()
+    qk = (torch.bfloat16, torch.float32)
+    _need(q, "q", qk)
+    batch, n, H, dk = q.shape
+    _need(k, "k", (q.dtype,), q.shape)
+    _need(v, "v", (q.dtype,))
+    if tuple(v.shape[:3]) != (batch, n, H):
+        raise ValueError("v must be [batch][n][H][d_v]")
+    dv = v.shape[3]
+    _need(alpha, "alpha", (torch.float32,), (batch, n, H))
+    _need(beta, "beta", (torch.float32,), (batch, n, H))
+    _need(parent, "parent", (torch.int32,), (batch, n))
+    _need(S0, "S0", (torch.float32,), (batch, H, dk, dv))
+    if out is None:
+        out = torch.empty((batch, n, H, dv), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), (batch, n, H, dv))
+    if status is not None:
+        _need(status, "status", (torch.int32,), (batch,))
+    rc = lib.gdn_tree_verify(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(alpha), _ptr(beta),
+                             _ptr(parent), _ptr(S0), _ptr(out), batch, n, H, dk, dv,
+                             _ptr(status), _stream(stream))
+    _check("gdn_tree_verify", rc)
+    return out
+
+
+def commit(S, path, path_len, k, v, alpha, beta, parent, status=None, stream=None):
+    """gdn_tree_commit: advances S [batch][H][d_k][d_v] in place; returns S."""
+    torch = _torch()
+    lib = load()
+    _need(k, "k", (torch.bfloat16, torch.float32))
+    batch, n, H, dk = k.shape
+    _need(v, "v", (k.dtype,))
+    dv = v.shape[3]
+    _need(S, "S", (torch.float32,), (batch, H, dk, dv))
+    _need(path, "path", (torch.int32,))
+    if path.dim() != 2 or path.shape[0] != batch:
+        raise ValueError("path must be [batch][max_path]")
+    _need(path_len, "path_len", (torch.int32,), (batch,))
+    _need(alpha, "alpha", (torch.float32,), (batch, n, H))
+    _need(beta, "beta", (torch.float32,), (batch, n, H))
+    _need(parent, "parent", (torch.int32,), (batch, n))
+    if status is not None:
+        _need(status, "status", (torch.int32,), (batch,))
+    rc = lib.gdn_tree_commit(_ptr(S), _ptr(path), _ptr(path_len), int(path.shape[1]), _ptr(k),
+                             _ptr(v), _qkv_dtype(k), _ptr(alpha), _ptr(beta), _ptr(parent),
+                             batch, n, H, dk, dv, _ptr(status), _stream(stream))
+    _check("gdn_tree_commit", rc)
+    return S
+
+
+def path(parent, accepted, max_path, out=None, path_len=None, status=None, stream=None):
+    """gdn_tree_path: (path int32 [batch][max_path], path_len int32 [batch])."""
+    torch = _torch()
+    lib = load()
+    _need(parent, "parent", (torch.int32,))
+    batch, n = parent.shape
+    _need(accepted, "accepted", (torch.int32,), (batch,))
+    if out is None:
+        out = torch.empty((batch, max_path), dtype=torch.int32, device=parent.device)
+    if path_len is None:
+        path_len = torch.empty((batch,), dtype=torch.int32, device=parent.device)
+    _need(out, "path", (torch.int32,), (batch, max_path))
+    _need(path_len, "path_len", (torch.int32,), (batch,))
+    if status is not None:
+        _need(status, "status", (torch.int32,), (batch,))
+    rc = lib.gdn_tree_path(_ptr(parent), _ptr(accepted), _ptr(out), _ptr(path_len), batch, n,
+                           int(max_path), _ptr(status), _stream(stream))
+    _check("gdn_tree_path", rc)
+    return out, path_len
+
+
+def index(parent, status=None, stream=None):
+    """gdn_tree_index: (depth int32 [batch][n], anc int32 bit patterns [batch][n][ceil(n/32)])."""
+    torch = _torch()
+    lib = load()
+    _need(parent, "parent", (torch.int32,))
+    batch, n = parent.shape
+    W = (n + 31) // 32
+    depth = torch.empty((batch, n), dtype=torch.int32, device=parent.device)
+    anc = torch.empty((batch, n, W), dtype=torch.int32, device=parent.device)
+    if status is not None:
+        _need(status, "status", (torch.int32,), (batch,))
+    rc = lib.gdn_tree_index(_ptr(parent), _ptr(depth), _ptr(anc), batch, n, _ptr(status),
+                            _stream(stream))
+    _check("gdn_tree_index", rc)
+    return depth, anc

@@ -1,0 +1,101 @@
+// C-ABI front end of libgdntree.so: host-side argument validation, kernel
+// selection and asynchronous launch on the caller's stream.  The declared
+// contract (layouts, ownership, errors) is in include/gdn_tree.h.
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dim_ok(int d) { return d >= 8 && d <= GDN_MAX_DIM && d % 8 == 0; }
+
+gdn_status shape_status(int batch, int n, int H, int dk, int dv) {
+    if (batch < 1 || n < 1 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_INVALID_ARG;
+    if (n > GDN_MAX_NODES || !dim_ok(dk) || !dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
+    // element offsets are formed in 64-bit, but grid.x = batch * H must fit
+    if ((long long)batch * H > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_tree_verify(const void *q, const void *k, const void *v, gdn_dtype qkv_dtype,
+                           const float *alpha, const float *beta, const int32_t *parent,
+                           const float *S0, float *out, int batch, int n, int H, int d_k,
+                           int d_v, int32_t *status, void *stream) {
+    if (!q || !k || !v || !alpha || !beta || !parent || !S0 || !out) return GDN_ERR_INVALID_ARG;
+    if (qkv_dtype != GDN_DTYPE_F32 && qkv_dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, alpha, beta, parent, S0, out, status};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+    const gdn_status st = shape_status(batch, n, H, d_k, d_v);
+    if (st != GDN_OK) return st;
+    gdn::VerifyArgs a{q, k, v, qkv_dtype, alpha, beta, parent, S0, out,
+                      batch, n, H, d_k, d_v, status};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gdn::verify_mfma_supports(a)) return from_hip(gdn::launch_verify_mfma(a, s));
+    return from_hip(gdn::launch_verify_generic(a, s));
+}
+
+gdn_status gdn_tree_commit(float *S, const int32_t *path, const int32_t *path_len, int max_path,
+                           const void *k, const void *v, gdn_dtype qkv_dtype, const float *alpha,
+                           const float *beta, const int32_t *parent, int batch, int n, int H,
+                           int d_k, int d_v, int32_t *status, void *stream) {
+    if (!S || !path || !path_len || !k || !v || !alpha || !beta || !parent)
+        return GDN_ERR_INVALID_ARG;
+    if (qkv_dtype != GDN_DTYPE_F32 && qkv_dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID_ARG;
+    if (max_path < 1) return GDN_ERR_INVALID_ARG;
+    const void *ptrs[] = {S, path, path_len, k, v, alpha, beta, parent, status};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+    const gdn_status st = shape_status(batch, n, H, d_k, d_v);
+    if (st != GDN_OK) return st;
+    gdn::CommitArgs a{S, path, path_len, max_path, k, v, qkv_dtype, alpha, beta, parent,
+                      batch, n, H, d_k, d_v, status};
+    return from_hip(gdn::launch_commit(a, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_tree_path(const int32_t *parent, const int32_t *accepted, int32_t *path,
+                         int32_t *path_len, int batch, int n, int max_path, int32_t *status,
+                         void *stream) {
+    if (!parent || !accepted || !path || !path_len) return GDN_ERR_INVALID_ARG;
+    if (batch < 1 || n < 1 || max_path < 1) return GDN_ERR_INVALID_ARG;
+    if (n > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    const void *ptrs[] = {parent, accepted, path, path_len, status};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_path(parent, accepted, path, path_len, batch, n, max_path, status,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_tree_index(const int32_t *parent, int32_t *depth, uint32_t *anc, int batch, int n,
+                          int32_t *status, void *stream) {
+    if (!parent || !depth || !anc) return GDN_ERR_INVALID_ARG;
+    if (batch < 1 || n < 1) return GDN_ERR_INVALID_ARG;
+    if (n > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    const void *ptrs[] = {parent, depth, anc, status};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_index(parent, depth, anc, batch, n, status,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+const char *gdn_status_string(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size)";
+        case GDN_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case GDN_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int gdn_tree_abi_version(void) { return GDN_TREE_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI front end (api.hip) and the kernel
+// launchers.  Not installed; the public surface is include/gdn_tree.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_tree.h"
+
+namespace gdn {
+
+struct VerifyArgs {
+    const void *q, *k, *v;
+    gdn_dtype dtype;
+    const float *alpha, *beta;
+    const int32_t *parent;
+    const float *S0;
+    float *out;
+    int batch, n, H, dk, dv;
+    int32_t *status;
+};
+
+struct CommitArgs {
+    float *S;
+    const int32_t *path, *path_len;
+    int max_path;
+    const void *k, *v;
+    gdn_dtype dtype;
+    const float *alpha, *beta;
+    const int32_t *parent;
+    int batch, n, H, dk, dv;
+    int32_t *status;
+};
+
+// every launcher returns the launch's hipError_t (hipGetLastError after it)
+hipError_t launch_verify_generic(const VerifyArgs &a, hipStream_t s);
+bool verify_mfma_supports(const VerifyArgs &a);
+hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s);
+hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
+hipError_t launch_path(const int32_t *parent, const int32_t *accepted,
+                       int32_t *path, int32_t *path_len, int batch, int n,
+                       int max_path, int32_t *status, hipStream_t s);
+hipError_t launch_index(const int32_t *parent, int32_t *depth, uint32_t *anc,
+                        int batch, int n, int32_t *status, hipStream_t s);
+
+}  // namespace gdn

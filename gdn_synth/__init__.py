@@ -40,7 +40,7 @@ __all__ = [
     "Workload", "TensorSet", "CONFIGS", "make_set", "make_config",
     "random_recursive_tree", "chain_tree", "star_tree", "kary_bfs_tree",
     "best_first_tree", "mixed_tree_batch", "pick_leaf", "leaves",
-    "to_bf16_bits", "bf16_bits_to_f32", "path_to",
+    "to_bf16_bits", "bf16_bits_to_f32", "path_to", "select", "slice_set",
 ]
 
 
@@ -375,3 +375,13 @@ def slice_set(ts: TensorSet, batch: int | None, heads: int | None) -> TensorSet:
                      accepted=np.ascontiguousarray(ts.accepted[b]),
                      q_bits=c(ts.q_bits, 2), k_bits=c(ts.k_bits, 2),
                      v_bits=c(ts.v_bits, 2), meta=dict(ts.meta))
+
+
+def select(ts: TensorSet, seqs) -> TensorSet:
+    """the batch elements `seqs` of a set (sequences are independent)"""
+    seqs = np.asarray(seqs)
+    f = lambda x: None if x is None else np.ascontiguousarray(x[seqs])
+    return TensorSet(dtype=ts.dtype, parent=f(ts.parent), q=f(ts.q), k=f(ts.k), v=f(ts.v),
+                     alpha=f(ts.alpha), beta=f(ts.beta), S0=f(ts.S0), accepted=f(ts.accepted),
+                     q_bits=f(ts.q_bits), k_bits=f(ts.k_bits), v_bits=f(ts.v_bits),
+                     meta=dict(ts.meta))

@@ -1,0 +1,140 @@
+/*
+ * gdn_tree.h -- C ABI of libgdntree.so: rollback-free tree verification and
+ * state commit for Gated DeltaNet (GDN) layers on AMD MI355X (gfx950).
+ *
+ * The operations follow the DFlash-TfM summary page, section "Verifica
+ * dell'Albero Senza Rollback per GDN" (rollback-free tree verification for
+ * GDN):
+ *   - the GDN state update S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1}
+ *     + beta_t k_t v_t^T, with S of shape d_k x d_v;
+ *   - the draft tree is topologically sorted;
+ *   - outputs for every tree node are computed from the committed state
+ *     without updating it, through ancestor interaction matrices X, Y and
+ *     the system (I + X) U = beta V;
+ *   - the state is committed later, along the accepted branch only, so no
+ *     rollback is ever needed.
+ * The output of node i is o_i = S_i^T q_i, where S_i is the state after the
+ * update of node i along its root-to-node path (the pages do not print the
+ * readout; this is the reading adopted).  No scaling of q is applied.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are caller-owned DEVICE pointers, C-contiguous,
+ *     16-byte aligned.  The library allocates no device memory and never
+ *     frees caller memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Host-detected errors are returned synchronously as a
+ *     negative gdn_status and launch nothing.
+ *   - Device-detected tree faults are written, without any host sync, to
+ *     the optional int32 array status[batch] (may be NULL): status[b] is
+ *     OVERWRITTEN with the OR of the GDN_FAULT_* flags found for batch
+ *     element b, 0 when none.
+ *   - Shapes: 1 <= batch, 1 <= H, 1 <= n <= GDN_MAX_NODES, and
+ *     d_k, d_v multiples of 8 in [8, GDN_MAX_DIM].  n is uniform over the
+ *     batch; the trees may differ per sequence.
+ *   - Functions are stateless and thread-safe.  Calls that overlap on the
+ *     same output memory race.
+ *
+ * Tensor layouts (row-major):
+ *   q, k    [batch][n][H][d_k]    bf16 or fp32 (qkv_dtype)
+ *   v       [batch][n][H][d_v]    same dtype as q, k
+ *   alpha   [batch][n][H]         fp32, the decay alpha_t
+ *   beta    [batch][n][H]         fp32, the write strength beta_t
+ *   parent  [batch][n]            int32; -1 = child of the committed state;
+ *                                 valid trees have -1 <= parent[i] < i
+ *   S0, S   [batch][H][d_k][d_v]  fp32 state
+ *   out     [batch][n][H][d_v]    fp32
+ */
+#ifndef GDN_TREE_H
+#define GDN_TREE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_TREE_ABI_VERSION 1
+#define GDN_MAX_NODES 128
+#define GDN_MAX_DIM 128
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size          */
+    GDN_ERR_UNSUPPORTED = -2, /* shape or dtype outside the supported set   */
+    GDN_ERR_HIP = -3          /* the HIP runtime refused a launch           */
+} gdn_status;
+
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
+
+/* device-detected fault flags (status[b]) */
+#define GDN_FAULT_BAD_PARENT 1 /* some parent[i] outside [-1, i)             */
+#define GDN_FAULT_BAD_PATH 2   /* path not a root-connected increasing chain,
+                                  an id outside [0, n), or a length outside
+                                  [0, max_path]                             */
+
+/*
+ * Tree verify (the rollback-free verification of the section above).
+ * For every batch element b, head h and node i, writes
+ *   out[b][i][h][:] = S_i^T q[b][i][h][:]
+ * where S_i is S0[b][h] advanced by the GDN update along root..i.
+ * S0 is READ-ONLY: verify never writes the committed state.
+ * `out` must not alias any input.  A batch element whose parent row is
+ * malformed gets GDN_FAULT_BAD_PARENT and all its out rows set to NaN.
+ * Arithmetic: products and sums in fp32 (bf16 inputs are widened exactly).
+ */
+gdn_status gdn_tree_verify(const void *q, const void *k, const void *v,
+                           gdn_dtype qkv_dtype, const float *alpha,
+                           const float *beta, const int32_t *parent,
+                           const float *S0, float *out, int batch, int n,
+                           int H, int d_k, int d_v, int32_t *status,
+                           void *stream);
+
+/*
+ * State commit along the accepted branch (the delayed commitment of the
+ * section above).  For each batch element b with m = path_len[b]:
+ *   S[b][h] <- GDN update applied for t = path[b][0], ..., path[b][m-1]
+ * in place, for every head h.  path is [batch][max_path] int32, root first;
+ * path_len is [batch] int32.  k, v, alpha, beta, parent are the tensors of
+ * the verify call that produced the tree.  m = 0 is a no-op.  A batch
+ * element whose path is invalid (see GDN_FAULT_BAD_PATH) gets that flag and
+ * its S is left bit-unchanged.  Commit is not idempotent: do not replay it.
+ */
+gdn_status gdn_tree_commit(float *S, const int32_t *path,
+                           const int32_t *path_len, int max_path,
+                           const void *k, const void *v, gdn_dtype qkv_dtype,
+                           const float *alpha, const float *beta,
+                           const int32_t *parent, int batch, int n, int H,
+                           int d_k, int d_v, int32_t *status, void *stream);
+
+/*
+ * Accepted path: path[b][0..m) = root .. accepted[b] (root first), the rest
+ * of the row -1, path_len[b] = m.  The walk goes up from accepted[b]; a
+ * parent outside [-1, node) stops it with GDN_FAULT_BAD_PARENT; an accepted
+ * id outside [0, n) or m > max_path gives GDN_FAULT_BAD_PATH.  A faulted row
+ * is all -1 with path_len 0.  Integer work, bit-exact.  1 <= max_path.
+ */
+gdn_status gdn_tree_path(const int32_t *parent, const int32_t *accepted,
+                         int32_t *path, int32_t *path_len, int batch, int n,
+                         int max_path, int32_t *status, void *stream);
+
+/*
+ * Tree indexing: depth[b][i] (root = 0) and the ancestor-or-self bitmask
+ * anc[b][i][ceil(n/32)] (bit s%32 of word s/32 is set iff s == i or s is an
+ * ancestor of i).  A malformed tree gives GDN_FAULT_BAD_PARENT, depth -1
+ * and anc 0 for every node of that batch element.  Bit-exact.
+ */
+gdn_status gdn_tree_index(const int32_t *parent, int32_t *depth,
+                          uint32_t *anc, int batch, int n, int32_t *status,
+                          void *stream);
+
+/* human-readable text for a gdn_status value (never NULL) */
+const char *gdn_status_string(int status);
+
+/* GDN_TREE_ABI_VERSION of the loaded library */
+int gdn_tree_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_TREE_H */

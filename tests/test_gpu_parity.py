@@ -1,0 +1,318 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Gates (max|gpu - ref| / max|ref| over a whole output tensor):
+  2e-3 for bf16 q/k/v with fp32 state and accumulation, 1e-5 all-fp32;
+  integer outputs (status, depth, ancestor masks, paths) bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_synth as gs
+import oracle
+from gpu_util import dev, host, upload
+
+pytestmark = pytest.mark.gpu
+
+BF16_GATE = 2e-3
+FP32_GATE = 1e-5
+
+
+def gate(ts):
+    return BF16_GATE if ts.dtype == "bf16" else FP32_GATE
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_verify(g, ts, status=True):
+    d = upload(ts)
+    st = torch.full((ts.parent.shape[0],), -7, dtype=torch.int32, device="cuda") if status else None
+    out = g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S0"], status=st)
+    torch.cuda.synchronize()
+    return host(out), (host(st) if status else None), d
+
+
+# ---------------------------------------------------------------------------
+# verify parity on the five workloads
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("chain", [False, True])
+def test_verify_tiny_fp32(gpu_lib, chain):
+    say("verify tiny fp32 chain=", chain)
+    ts = gs.make_config(0, chain=chain)
+    out, st, _ = run_verify(gpu_lib, ts)
+    ref, rst = oracle.verify_set(ts)
+    assert st.tolist() == rst.tolist() == [0]
+    assert oracle.rel_err(out, ref) <= FP32_GATE
+
+
+def test_verify_layer_b1_n32(gpu_lib):
+    say("verify b1 n32 bf16")
+    ts = gs.make_config(1)
+    out, st, _ = run_verify(gpu_lib, ts)
+    ref, rst = oracle.verify_set(ts)
+    assert st.tolist() == rst.tolist()
+    err = oracle.rel_err(out, ref)
+    say("rel err", err)
+    assert err <= BF16_GATE
+
+
+def test_verify_layer_b16_n64_full(gpu_lib):
+    """the benchmarked workload, whole output tensor"""
+    say("verify b16 n64 bf16 full")
+    ts = gs.make_config(2)
+    out, st, _ = run_verify(gpu_lib, ts)
+    ref, rst = oracle.verify_set(ts)
+    assert st.tolist() == rst.tolist() == [0] * 16
+    err = oracle.rel_err(out, ref)
+    say("rel err", err)
+    assert err <= BF16_GATE
+
+
+def test_verify_layer_b64_n128_sampled(gpu_lib):
+    """full launch; the oracle checks chains, stars, 16-ary and random trees"""
+    say("verify b64 n128 bf16")
+    ts = gs.make_config(3)
+    out, st, _ = run_verify(gpu_lib, ts)
+    assert st.tolist() == [0] * 64
+    pick = [0, 15, 16, 23, 24, 31, 32, 47, 63]
+    sub = gs.select(ts, pick)
+    ref, _ = oracle.verify_set(sub)
+    for j, b in enumerate(pick):
+        err = oracle.rel_err(out[b], ref[j])
+        say("seq", b, "rel err", err)
+        assert err <= BF16_GATE, b
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_stack_layer_verify_commit(gpu_lib, layer):
+    say("stack layer", layer)
+    ts = gs.make_config(4, layer=layer)
+    out, st, d = run_verify(gpu_lib, ts)
+    path, plen = ts.paths(max_path=13)
+    S = d["S0"].clone()
+    cst = torch.full((32,), -7, dtype=torch.int32, device="cuda")
+    gpu_lib.commit(S, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                   status=cst)
+    torch.cuda.synchronize()
+    pick = list(range(0, 32, 4))
+    sub = gs.select(ts, pick)
+    ref, _ = oracle.verify_set(sub)
+    assert oracle.rel_err(out[pick], ref) <= BF16_GATE
+    Sref, rst = oracle.commit_set(sub, path_arr=path[pick], path_len=plen[pick])
+    assert host(cst).tolist() == [0] * 32
+    assert oracle.rel_err(host(S)[pick], Sref) <= BF16_GATE
+
+
+# ---------------------------------------------------------------------------
+# shapes: ragged n, every supported head dim, n = 1, forests
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,dk,dv,dtype,H,batch", [
+    (1, 16, 16, "fp32", 2, 3),
+    (1, 128, 128, "bf16", 4, 2),
+    (37, 32, 64, "fp32", 3, 2),
+    (37, 128, 128, "bf16", 5, 3),
+    (64, 128, 128, "bf16", 3, 2),
+    (100, 64, 48, "bf16", 2, 2),
+    (128, 128, 128, "bf16", 2, 2),
+    (128, 8, 128, "fp32", 1, 1),
+    (65, 128, 128, "bf16", 2, 2),
+    (17, 24, 40, "fp32", 2, 2),
+])
+def test_verify_shapes(gpu_lib, n, dk, dv, dtype, H, batch):
+    say("shape", n, dk, dv, dtype, H, batch)
+    rng = np.random.default_rng(n * 1000 + dk + dv)
+    par = np.stack([gs.random_recursive_tree(rng, n, max_depth=int(rng.integers(1, 20)))
+                    for _ in range(batch)])
+    if batch > 1 and n > 4:
+        par[1, n // 2] = -1                   # forest: a second root
+    ts = gs.make_set(par, H, dk, dv, dtype, seed=n + dk)
+    out, st, _ = run_verify(gpu_lib, ts)
+    ref, rst = oracle.verify_set(ts)
+    assert st.tolist() == rst.tolist() == [0] * batch
+    assert oracle.rel_err(out, ref) <= gate(ts)
+
+
+@pytest.mark.parametrize("shape", ["chain", "star", "bfs16"])
+def test_verify_extreme_trees_n128(gpu_lib, shape):
+    say("extreme", shape)
+    par = {"chain": gs.chain_tree(128), "star": gs.star_tree(128),
+           "bfs16": gs.kary_bfs_tree(128, 16)}[shape]
+    ts = gs.make_set(np.stack([par, par]), 4, 128, 128, "bf16", seed=5)
+    out, _, _ = run_verify(gpu_lib, ts)
+    ref, _ = oracle.verify_set(ts)
+    assert oracle.rel_err(out, ref) <= BF16_GATE
+
+
+def test_verify_fp32_gate_at_d128(gpu_lib):
+    """all-fp32 inputs at the full head size meet the fp32 gate"""
+    ts = gs.make_set(gs.make_trees(1, np.random.default_rng(3)), 4, 128, 128, "fp32", seed=3)
+    out, _, _ = run_verify(gpu_lib, ts)
+    ref, _ = oracle.verify_set(ts)
+    assert oracle.rel_err(out, ref) <= FP32_GATE
+
+
+# ---------------------------------------------------------------------------
+# commit parity, commit-then-verify, invariants
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_commit_parity(gpu_lib, cfg):
+    say("commit cfg", cfg)
+    ts = gs.make_config(cfg)
+    d = upload(ts)
+    path, plen = ts.paths(max_path=ts.parent.shape[1])
+    S = d["S0"].clone()
+    st = torch.full((ts.parent.shape[0],), -7, dtype=torch.int32, device="cuda")
+    gpu_lib.commit(S, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                   status=st)
+    torch.cuda.synchronize()
+    Sref, rst = oracle.commit_set(ts, path_arr=path, path_len=plen)
+    assert host(st).tolist() == rst.tolist()
+    assert oracle.rel_err(host(S), Sref) <= gate(ts)
+
+
+def test_commit_deep_chain_n128(gpu_lib):
+    ts = gs.make_set(np.stack([gs.chain_tree(128)] * 2), 2, 128, 128, "bf16", seed=8,
+                     accepted=np.array([127, 64], np.int32))
+    d = upload(ts)
+    path, plen = ts.paths(max_path=128)
+    S = d["S0"].clone()
+    gpu_lib.commit(S, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"])
+    Sref, _ = oracle.commit_set(ts, path_arr=path, path_len=plen)
+    assert oracle.rel_err(host(S), Sref) <= BF16_GATE
+
+
+def test_commit_then_verify_subtree(gpu_lib):
+    """the committed state, verified over the re-rooted subtree below the
+    accepted node, reproduces the original verify outputs of that subtree"""
+    ts = gs.make_config(1)
+    par = ts.parent[0]
+    a = next(i for i in range(1, len(par)) if (par == i).sum() >= 2)
+    out, _, d = run_verify(gpu_lib, ts)
+    p = gs.path_to(par, a)[None].astype(np.int32)
+    S = d["S0"].clone()
+    gpu_lib.commit(S, dev(p), dev(np.array([p.shape[1]], np.int32)), d["k"], d["v"], d["alpha"],
+                   d["beta"], d["parent"])
+    desc = [i for i in range(len(par)) if i != a and a in set(gs.path_to(par, i))]
+    m = {o: j for j, o in enumerate(desc)}
+    newp = np.array([-1 if par[o] == a else m[par[o]] for o in desc], np.int32)[None]
+    sl = lambda x: x[:, desc].contiguous()
+    o2 = gpu_lib.verify(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["alpha"]), sl(d["beta"]),
+                        dev(newp), S)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(host(o2), out[:, desc]) <= BF16_GATE
+
+
+def test_verify_leaves_state_untouched_and_is_deterministic(gpu_lib):
+    ts = gs.make_config(2)
+    d = upload(ts)
+    before = d["S0"].clone()
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S0"])
+    o1 = gpu_lib.verify(*args)
+    o2 = gpu_lib.verify(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(d["S0"], before)
+    assert torch.equal(o1, o2)
+
+
+def test_relabeling_on_gpu(gpu_lib):
+    ts = gs.make_config(1)
+    out, _, d = run_verify(gpu_lib, ts)
+    rng = np.random.default_rng(2)
+    par = ts.parent[0]
+    n = len(par)
+    order, ready = [], [0]
+    while ready:
+        j = ready.pop(int(rng.integers(0, len(ready))))
+        order.append(j)
+        ready += [c for c in range(n) if par[c] == j]
+    perm = np.array(order)
+    inv = np.empty(n, int)
+    inv[perm] = np.arange(n)
+    newp = np.array([-1 if par[o] < 0 else inv[par[o]] for o in perm], np.int32)[None]
+    sl = lambda x: x[:, perm].contiguous()
+    o2 = gpu_lib.verify(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["alpha"]), sl(d["beta"]),
+                        dev(newp), d["S0"])
+    assert oracle.rel_err(host(o2), out[:, perm]) <= BF16_GATE
+
+
+# ---------------------------------------------------------------------------
+# faults
+# ---------------------------------------------------------------------------
+def test_verify_bad_parent(gpu_lib):
+    ts = gs.make_config(2, batch=3)
+    ts.parent[1, 10] = 12
+    ts.parent[2, 0] = -2
+    out, st, _ = run_verify(gpu_lib, ts)
+    ref, rst = oracle.verify_set(ts)
+    assert st.tolist() == rst.tolist() == [0, 1, 1]
+    assert np.isnan(out[1:]).all() and np.isfinite(out[0]).all()
+    assert oracle.rel_err(out[0], ref[0]) <= BF16_GATE
+
+
+def test_commit_bad_paths_leave_state(gpu_lib):
+    ts = gs.make_config(2, batch=4)
+    d = upload(ts)
+    path, plen = ts.paths(max_path=16)
+    path[0, 1] = 64                     # id out of range
+    path[1, 0] = path[1, 1]             # not starting at a root
+    plen[2] = 17                        # longer than max_path
+    S = d["S0"].clone()
+    st = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    gpu_lib.commit(S, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                   status=st)
+    torch.cuda.synchronize()
+    Sref, rst = oracle.commit_set(ts, path_arr=path, path_len=plen)
+    assert host(st).tolist() == rst.tolist() == [2, 2, 2, 0]
+    assert torch.equal(S[:3], d["S0"][:3])
+    assert oracle.rel_err(host(S)[3], Sref[3]) <= BF16_GATE
+
+
+def test_commit_empty_path_is_noop(gpu_lib):
+    ts = gs.make_config(1)
+    d = upload(ts)
+    S = d["S0"].clone()
+    gpu_lib.commit(S, dev(np.full((1, 4), -1, np.int32)), dev(np.zeros(1, np.int32)), d["k"],
+                   d["v"], d["alpha"], d["beta"], d["parent"])
+    torch.cuda.synchronize()
+    assert torch.equal(S, d["S0"])
+
+
+# ---------------------------------------------------------------------------
+# integer work: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_index_and_path_bit_exact(gpu_lib, cfg):
+    ts = gs.make_config(cfg)
+    par = ts.parent
+    depth, anc = gpu_lib.index(dev(par))
+    rd, ra, rs = oracle.index(par)
+    assert np.array_equal(host(depth), rd)
+    assert np.array_equal(host(anc).view(np.uint32), ra)
+    for mp in (1, 5, 13, par.shape[1]):
+        st = torch.full((par.shape[0],), -7, dtype=torch.int32, device="cuda")
+        p, pl = gpu_lib.path(dev(par), dev(ts.accepted), mp, status=st)
+        rp, rpl, rps = oracle.path(par, ts.accepted, mp)
+        assert np.array_equal(host(p), rp) and np.array_equal(host(pl), rpl)
+        assert np.array_equal(host(st), rps)
+
+
+def test_index_and_path_malformed(gpu_lib):
+    rng = np.random.default_rng(4)
+    par = np.stack([gs.random_recursive_tree(rng, 77) for _ in range(8)])
+    par[1, 76] = 76
+    par[2, 5] = -4
+    par[3, 40] = 50
+    acc = rng.integers(0, 77, size=8).astype(np.int32)
+    acc[1], acc[4], acc[5] = 76, 77, -1
+    st = torch.full((8,), -7, dtype=torch.int32, device="cuda")
+    depth, anc = gpu_lib.index(dev(par), status=st)
+    rd, ra, rs = oracle.index(par)
+    assert np.array_equal(host(depth), rd) and np.array_equal(host(anc).view(np.uint32), ra)
+    assert np.array_equal(host(st), rs)
+    for mp in (3, 77):
+        p, pl = gpu_lib.path(dev(par), dev(acc), mp, status=st)
+        rp, rpl, rps = oracle.path(par, acc, mp)
+        assert np.array_equal(host(p), rp) and np.array_equal(host(pl), rpl)
+        assert np.array_equal(host(st), rps)
