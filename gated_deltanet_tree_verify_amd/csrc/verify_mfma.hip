@@ -21,8 +21,10 @@
 // Every intermediate n x 32 tile stays in registers: an accumulator tile in
 // the 32x32 MFMA result layout is fed straight back as the B operand of the
 // next product, with the A operand's columns stored in the matching permuted
-// order.  Only the 64x128 Q and K tiles, the 32x32 interaction blocks and
-// the block inverses live in LDS (~75 KB, two workgroups per CU).
+// order.  Gram tiles are computed transposed so that each lane already holds
+// the operand fragment that the solve reads back, and leaves it with one
+// 16-byte LDS write.  V and the output rows move through LDS so that global
+// traffic is whole-row 16-byte accesses.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -38,15 +40,33 @@ constexpr int kThreads = 256;   // four waves
 constexpr int kQK = kD + 8;     // LDS row stride of the Q/K tiles (bf16)
 constexpr int kBL = 40;         // LDS row stride of 32x32 operand blocks (bf16)
 
-struct Smem {
-    uint16_t q[kN][kQK];
-    uint16_t k[kN][kQK];
-    float d[2][32][32];                 // strictly-lower X of the two diagonal blocks
+// LDS layout (79 KB, two workgroups per CU).  The V tile is staged once and
+// moved into registers before the solve blocks are built in the same bytes;
+// the Q/K tiles are reused to stage the output rows.
+struct SolveBlocks {
+    float d[2][32][32];                        // strictly-lower X_bb (fp32); later also Z
+    float tinv[4][16][16];                     // inverses of the 16x16 diagonal sub-blocks
     uint16_t th[2][32][kBL], tl[2][32][kBL];   // T_b = (I + X_bb)^{-1}, hi / lo
     uint16_t xh[32][kBL], xl[32][kBL];         // -X_10, hi / lo
     uint16_t yh[3][32][kBL], yl[3][32][kBL];   // Y_00, Y_10, Y_11, hi / lo
+};
+struct QKTiles {
+    uint16_t q[kN][kQK];
+    uint16_t k[kN][kQK];
+};
+struct Smem {
+    union {
+        QKTiles t;
+        float o[kN][kD + 4];                   // output rows, staged for 16-byte stores
+    } a;
+    union {
+        uint16_t v[kN][kQK];
+        SolveBlocks s;
+    } b;
     unsigned long long anc[kN];                // ancestor-or-self bitmask per node
-    float g[kN], eg[kN], beta[kN];
+    float g[kN];                               // log2 of the path decay product
+    float eg[kN];                              // path decay product e^{g}
+    float beta[kN];
     int bad;
 };
 
@@ -66,12 +86,6 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 }
 
 // x = hi + lo + O(2^-17 |x|), hi and lo bf16 (round to nearest even)
-__device__ __forceinline__ void split_bits(float x, uint16_t &hi, uint16_t &lo) {
-    const __bf16 h = static_cast<__bf16>(x);
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = bf16_bits(x - static_cast<float>(h));
-}
-
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -83,6 +97,10 @@ __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ __forceinline__ void st8(uint16_t *p, const bf16x8 &x) {
+    *reinterpret_cast<bf16x8 *>(p) = x;
 }
 
 // C += A * B for fp32 A (hi/lo blocks in LDS, permuted columns) and an fp32
@@ -115,15 +133,20 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     const int m = l & 31, h = l >> 5;        // row / column within a 32x32 tile, lane half
     const int bh = blockIdx.x, b = bh / H, hd = bh % H;
     const int col = 32 * w + m;              // this lane's d_v column
+    const size_t rstride = (size_t)H * kD;   // elements between consecutive nodes
+    const size_t base = ((size_t)b * n * H + hd) * kD;   // node 0 of this (sequence, head)
 
-    // ---- 1. issue loads: Q/K tiles (to LDS), gates and parents, the S0 slab
-    uint4 qk[8];
+    // ---- 1. loads: Q, K, V tiles (16-byte rows chunks, to LDS), gates and
+    //         parents (wave 3, one lane per node), this wave's S0 slab
+    uint4 st[12];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int e = tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
-        const size_t off = (((size_t)b * n + row) * H + hd) * kD + c8;
-        qk[it] = row < n ? *reinterpret_cast<const uint4 *>(q + off) : make_uint4(0, 0, 0, 0);
-        qk[4 + it] = row < n ? *reinterpret_cast<const uint4 *>(k + off) : make_uint4(0, 0, 0, 0);
+        const size_t off = base + row * rstride + c8;
+        const bool in = row < n;
+        st[it] = in ? *reinterpret_cast<const uint4 *>(q + off) : make_uint4(0, 0, 0, 0);
+        st[4 + it] = in ? *reinterpret_cast<const uint4 *>(k + off) : make_uint4(0, 0, 0, 0);
+        st[8 + it] = in ? *reinterpret_cast<const uint4 *>(v + off) : make_uint4(0, 0, 0, 0);
     }
     int p = -1;
     float la = 0.f, bt = 0.f;
@@ -131,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     if (node_ok) {
         const size_t row = ((size_t)b * n + l) * H + hd;
         p = parent[(size_t)b * n + l];
-        la = logf(alpha[row]);
+        la = log2f(alpha[row]);
         bt = beta[row];
     }
     const float *s0p = S0 + (size_t)bh * kD * kD + col;
@@ -144,27 +167,32 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int e = tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
-        *reinterpret_cast<uint4 *>(&sm.q[row][c8]) = qk[it];
-        *reinterpret_cast<uint4 *>(&sm.k[row][c8]) = qk[4 + it];
+        *reinterpret_cast<uint4 *>(&sm.a.t.q[row][c8]) = st[it];
+        *reinterpret_cast<uint4 *>(&sm.a.t.k[row][c8]) = st[4 + it];
+        *reinterpret_cast<uint4 *>(&sm.b.v[row][c8]) = st[8 + it];
     }
     __syncthreads();
 
-    // ---- 2. Gram tiles (waves 0-2) and tree topology (wave 3)
-    const int mt = (w == 2) ? 1 : (w == 1 ? 1 : 0);   // tiles (0,0) (1,0) (1,1)
+    // ---- 2. transposed Gram tiles (waves 0-2), topology (wave 3), V -> registers
+    // Wave w owns block (mt, nt) = (0,0), (1,0), (1,1) of the node x node
+    // matrices and computes it transposed: lane (node i = 32 mt + m, half h)
+    // holds k_s.q_i and k_s.k_i for s = 32 nt + crow(r, h), exactly the
+    // operand order the solve and output products read back.
+    const int mt = (w == 0) ? 0 : 1;
     const int nt = (w == 2) ? 1 : 0;
     f32x16 gc = {}, ga = {};
     if (w < 3) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            const bf16x8 aq = lds8(&sm.q[32 * mt + m][16 * kk + 8 * h]);
-            const bf16x8 ak = lds8(&sm.k[32 * mt + m][16 * kk + 8 * h]);
-            const bf16x8 bk = lds8(&sm.k[32 * nt + m][16 * kk + 8 * h]);
-            gc = mfma(aq, bk, gc);
-            ga = mfma(ak, bk, ga);
+            const bf16x8 ks = lds8(&sm.a.t.k[32 * nt + m][16 * kk + 8 * h]);
+            const bf16x8 qi = lds8(&sm.a.t.q[32 * mt + m][16 * kk + 8 * h]);
+            const bf16x8 ki = lds8(&sm.a.t.k[32 * mt + m][16 * kk + 8 * h]);
+            gc = mfma(ks, qi, gc);
+            ga = mfma(ks, ki, ga);
         }
     } else {
         // pointer jumping, one lane per node: after round r every node has
-        // folded in its nearest 2^(r+1) path nodes (mask bits and log decays)
+        // folded in its nearest 2^(r+1) path nodes (mask bits, log2 decays)
         const bool badi = node_ok && !parent_ok(p, l);
         const unsigned long long badm = __ballot(badi);
         unsigned long long anc = node_ok ? (1ull << l) : 0ull;
@@ -184,75 +212,93 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
         }
         sm.anc[l] = anc;
         sm.g[l] = gs;
-        sm.eg[l] = node_ok ? expf(gs) : 0.f;
+        sm.eg[l] = node_ok ? exp2f(gs) : 0.f;
         sm.beta[l] = bt;
         if (l == 0) {
             sm.bad = badm != 0ull;
             if (hd == 0 && status) status[b] = badm ? kFaultBadParent : 0;
         }
     }
+    uint32_t vpk[2][8];   // V in this lane's result-tile layout, bf16 pairs
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+            vpk[t][r / 2] = (uint32_t)sm.b.v[32 * t + crow(r, h)][col] |
+                            ((uint32_t)sm.b.v[32 * t + crow(r + 1, h)][col] << 16);
     __syncthreads();
 
-    float *orow = out + ((size_t)b * n * H + hd) * kD + col;   // + i * H * kD
     if (sm.bad) {
+        float *orow = out + base + col;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = 32 * t + crow(r, h);
-                if (i < n) orow[(size_t)i * H * kD] = __builtin_nanf("");
+                if (i < n) orow[(size_t)i * rstride] = __builtin_nanf("");
             }
         return;
     }
 
-    // ---- 3. mask + decay the Gram tiles into X and Y blocks
+    // ---- 3. mask + decay the Gram tiles into the X and Y blocks
+    SolveBlocks &sb = sm.b.s;
     if (w < 3) {
-        const int s = 32 * nt + m;
-        const float gsv = sm.g[s];
-        const int yb = (w == 0) ? 0 : (w == 1 ? 1 : 2);
+        const int il = m, i = 32 * mt + m;
+        const unsigned long long anc = sm.anc[i];
+        const float gi = sm.g[i], bi = sm.beta[i];
+        float y[16], x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int il = crow(r, h), i = 32 * mt + il;
-            const bool star = (sm.anc[i] >> s) & 1ull;
-            const float wt = star ? expf(sm.g[i] - gsv) : 0.f;
-            const float y = wt * gc[r];
-            const float x = (star && s != i) ? sm.beta[i] * wt * ga[r] : 0.f;
-            uint16_t yh, yl;
-            split_bits(y, yh, yl);
-            sm.yh[yb][il][perm(m)] = yh;
-            sm.yl[yb][il][perm(m)] = yl;
-            if (w == 1) {
-                uint16_t xh, xl;
-                split_bits(-x, xh, xl);
-                sm.xh[il][perm(m)] = xh;
-                sm.xl[il][perm(m)] = xl;
-            } else {
-                sm.d[mt][il][m] = x;
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 g4 = *reinterpret_cast<const float4 *>(&sm.g[32 * nt + 8 * q4 + 4 * h]);
+            const float gs4[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e, s = 32 * nt + crow(r, h);
+                const bool star = (anc >> s) & 1ull;
+                const float wt = star ? exp2f(gi - gs4[e]) : 0.f;
+                y[r] = wt * gc[r];
+                x[r] = (star && s != i) ? bi * wt * ga[r] : 0.f;
             }
         }
-    }
-    // values of V in the result layout of this lane's tiles
-    const uint16_t *vp = v + ((size_t)b * n * H + hd) * kD + col;
-    float vv[2][16];
+        const int yb = w;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 32 * t + crow(r, h);
-            vv[t][r] = i < n ? to_f32(vp[(size_t)i * H * kD]) : 0.f;
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 hi, lo;
+            split8(&y[8 * kk], hi, lo);
+            st8(&sb.yh[yb][il][16 * kk + 8 * h], hi);
+            st8(&sb.yl[yb][il][16 * kk + 8 * h], lo);
         }
+        if (w == 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = -x[r];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 hi, lo;
+                split8(&x[8 * kk], hi, lo);
+                st8(&sb.xh[il][16 * kk + 8 * h], hi);
+                st8(&sb.xl[il][16 * kk + 8 * h], lo);
+            }
+        } else {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<float4 *>(&sb.d[mt][il][8 * q4 + 4 * h]) =
+                    make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+        }
+    }
     __syncthreads();
 
-    // ---- 4. block inverses T_b = (I + X_bb)^{-1} (wave 3: lane = block, column)
+    // ---- 4. block inverses T_b = (I + X_bb)^{-1}, tiled: the four 16x16
+    //         diagonal sub-blocks by forward substitution (wave 3, lane =
+    //         sub-block, column), then T21 = -C^{-1} (B A^{-1}) by all threads
     if (w == 3) {
-        const int blk = h, c = m;
-        float t[32];
+        const int sbk = l >> 4, c = l & 15, blk = sbk >> 1, o16 = 16 * (sbk & 1);
+        float t[16];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
+        for (int r = 0; r < 16; ++r) {
             float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
             for (int s4 = 0; s4 < r; s4 += 4) {
-                const float4 xr = *reinterpret_cast<const float4 *>(&sm.d[blk][r][s4]);
+                const float4 xr = *reinterpret_cast<const float4 *>(&sb.d[blk][o16 + r][o16 + s4]);
                 acc = fmaf(-xr.x, t[s4], acc);
                 if (s4 + 1 < r) acc = fmaf(-xr.y, t[s4 + 1], acc);
                 if (s4 + 2 < r) acc = fmaf(-xr.z, t[s4 + 2], acc);
@@ -261,12 +307,44 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
             t[r] = acc;
         }
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            uint16_t th, tl;
-            split_bits(t[r], th, tl);
-            sm.th[blk][r][perm(c)] = th;
-            sm.tl[blk][r][perm(c)] = tl;
+        for (int r = 0; r < 16; ++r) sb.tinv[sbk][r][c] = t[r];
+    }
+    __syncthreads();
+    // Z_b = B_b A_b^{-1}, written over the dead upper-left sub-block of d[b]
+    float zv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int idx = tid + kThreads * u, blk = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) acc = fmaf(sb.d[blk][16 + r][s], sb.tinv[2 * blk][s][c], acc);
+        zv[u] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int idx = tid + kThreads * u, blk = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+        sb.d[blk][r][c] = zv[u];
+    }
+    __syncthreads();
+    // T_b assembled: [[A^-1, 0], [-C^-1 Z, C^-1]], split hi/lo, permuted columns
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int idx = tid + kThreads * u, blk = idx >> 10, r = (idx >> 5) & 31, c = idx & 31;
+        float val;
+        if (r < 16) {
+            val = c < 16 ? sb.tinv[2 * blk][r][c] : 0.f;
+        } else if (c >= 16) {
+            val = sb.tinv[2 * blk + 1][r - 16][c - 16];
+        } else {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) acc = fmaf(sb.tinv[2 * blk + 1][r - 16][s], sb.d[blk][s][c], acc);
+            val = -acc;
         }
+        const __bf16 hv = static_cast<__bf16>(val);
+        sb.th[blk][r][perm(c)] = __builtin_bit_cast(uint16_t, hv);
+        sb.tl[blk][r][perm(c)] = bf16_bits(val - static_cast<float>(hv));
     }
 
     // ---- 5. P = Q S0 and R = K S0 for this wave's 32 columns
@@ -277,8 +355,8 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
         split8(s0[kk], sh, sl);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const bf16x8 aq = lds8(&sm.q[32 * t + m][16 * kk + 8 * h]);
-            const bf16x8 ak = lds8(&sm.k[32 * t + m][16 * kk + 8 * h]);
+            const bf16x8 aq = lds8(&sm.a.t.q[32 * t + m][16 * kk + 8 * h]);
+            const bf16x8 ak = lds8(&sm.a.t.k[32 * t + m][16 * kk + 8 * h]);
             P[t] = mfma(aq, sh, P[t]);
             P[t] = mfma(aq, sl, P[t]);
             R[t] = mfma(ak, sh, R[t]);
@@ -292,24 +370,41 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 32 * t + crow(r, h);
-            rhs[t][r] = sm.beta[i] * (vv[t][r] - sm.eg[i] * R[t][r]);
-            P[t][r] *= sm.eg[i];
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int i0 = 32 * t + 8 * q4 + 4 * h;
+            const float4 b4 = *reinterpret_cast<const float4 *>(&sm.beta[i0]);
+            const float4 e4 = *reinterpret_cast<const float4 *>(&sm.eg[i0]);
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ee[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e;
+                const uint32_t pr = vpk[t][r >> 1];
+                const float vval = __uint_as_float((r & 1) ? (pr & 0xffff0000u) : (pr << 16));
+                rhs[t][r] = bb[e] * (vval - ee[e] * R[t][r]);
+                P[t][r] *= ee[e];
+            }
         }
     const f32x16 zero = {};
-    const f32x16 u0 = mm3(sm.th[0], sm.tl[0], rhs[0], zero, m, h);
-    const f32x16 z1 = mm3(sm.xh, sm.xl, u0, rhs[1], m, h);
-    const f32x16 u1 = mm3(sm.th[1], sm.tl[1], z1, zero, m, h);
-    f32x16 o0 = mm3(sm.yh[0], sm.yl[0], u0, P[0], m, h);
-    f32x16 o1 = mm3(sm.yh[1], sm.yl[1], u0, P[1], m, h);
-    o1 = mm3(sm.yh[2], sm.yl[2], u1, o1, m, h);
+    const f32x16 u0 = mm3(sb.th[0], sb.tl[0], rhs[0], zero, m, h);
+    const f32x16 z1 = mm3(sb.xh, sb.xl, u0, rhs[1], m, h);
+    const f32x16 u1 = mm3(sb.th[1], sb.tl[1], z1, zero, m, h);
+    f32x16 o0 = mm3(sb.yh[0], sb.yl[0], u0, P[0], m, h);
+    f32x16 o1 = mm3(sb.yh[1], sb.yl[1], u0, P[1], m, h);
+    o1 = mm3(sb.yh[2], sb.yl[2], u1, o1, m, h);
 
+    // ---- 7. stage the output rows in LDS, then store whole rows
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int i0 = crow(r, h), i1 = 32 + i0;
-        if (i0 < n) orow[(size_t)i0 * H * kD] = o0[r];
-        if (i1 < n) orow[(size_t)i1 * H * kD] = o1[r];
+        sm.a.o[crow(r, h)][col] = o0[r];
+        sm.a.o[32 + crow(r, h)][col] = o1[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int e = tid + kThreads * it, row = e >> 5, c4 = (e & 31) * 4;
+        if (row < n)
+            *reinterpret_cast<float4 *>(out + base + row * rstride + c4) =
+                *reinterpret_cast<const float4 *>(&sm.a.o[row][c4]);
     }
 }
 
