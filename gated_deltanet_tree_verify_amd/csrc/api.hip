@@ -3,6 +3,8 @@
 // contract (layouts, ownership, errors) is in include/gdn_tree.h.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "internal.hpp"
 
 namespace {
@@ -22,6 +24,25 @@ gdn_status shape_status(int batch, int n, int H, int dk, int dv) {
 gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
 }  // namespace
+
+namespace gdn {
+
+int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+}  // namespace gdn
 
 extern "C" {
 
@@ -58,7 +79,9 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path, const int32_t *path_le
     if (st != GDN_OK) return st;
     gdn::CommitArgs a{S, path, path_len, max_path, k, v, qkv_dtype, alpha, beta, parent,
                       batch, n, H, d_k, d_v, status};
-    return from_hip(gdn::launch_commit(a, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gdn::commit_mfma_supports(a)) return from_hip(gdn::launch_commit_mfma(a, s));
+    return from_hip(gdn::launch_commit(a, s));
 }
 
 gdn_status gdn_tree_path(const int32_t *parent, const int32_t *accepted, int32_t *path,

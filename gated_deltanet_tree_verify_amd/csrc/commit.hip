@@ -23,18 +23,22 @@ constexpr int kRowsMax = GDN_MAX_DIM / kGroups;          // rows per thread (<= 
 
 // A path is valid when 0 <= m <= max_path, every id is in [0, n), the first
 // node is a root (parent -1) and every later node's parent is the previous
-// node, with ids strictly increasing (topological order).
-__device__ bool path_valid(const int32_t *par, const int32_t *path, int m, int max_path, int n) {
+// node, with ids strictly increasing (topological order).  Checked by one
+// wave, one path slot per lane: two rounds of reads rather than a chain.
+__device__ bool path_valid_wave(const int32_t *par, const int32_t *path, int m, int max_path,
+                                int n, int lane) {
     if (m < 0 || m > max_path) return false;
-    int prev = -1;
-    for (int j = 0; j < m; ++j) {
-        const int id = path[j];
-        if (id < 0 || id >= n) return false;
-        if (par[id] != prev) return false;
-        if (j > 0 && prev >= id) return false;
-        prev = id;
+    bool bad = false;
+    for (int j0 = 0; j0 < m; j0 += 64) {
+        const int j = j0 + lane;
+        if (j < m) {
+            const int id = path[j];
+            const int prev = j == 0 ? -1 : path[j - 1];
+            if (id < 0 || id >= n || (j > 0 && prev >= id)) bad = true;
+            else if (par[id] != prev) bad = true;
+        }
     }
-    return true;
+    return __ballot(bad) == 0ull;
 }
 
 template <typename T>
@@ -59,10 +63,12 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     const int r0 = grp * rows;
     const int32_t *prow = path + (size_t)b * max_path;
 
-    if (tid == 0) {
-        const bool ok = path_valid(parent + (size_t)b * n, prow, path_len[b], max_path, n);
-        s_ok = ok;
-        if (h == 0 && blockIdx.y == 0 && status) status[b] = ok ? 0 : kFaultBadPath;
+    if (tid < 64) {
+        const bool ok = path_valid_wave(parent + (size_t)b * n, prow, path_len[b], max_path, n, tid);
+        if (tid == 0) {
+            s_ok = ok;
+            if (h == 0 && blockIdx.y == 0 && status) status[b] = ok ? 0 : kFaultBadPath;
+        }
     }
     __syncthreads();
     if (!s_ok) return;

@@ -1,0 +1,332 @@
+// MFMA state commit along the accepted branch, bf16 k/v, d_k = d_v = 128.
+//
+// The commitment is deferred until the accepted branch is known (DFlash-TfM
+// page, rollback-free GDN verification section), and the branch is a chain,
+// so the chunked form of the delta rule applies to it directly.  For a chunk
+// of path nodes j = 0..mc-1 (chunk-local log2 decay prefix g_j) entering with
+// state S:
+//     R = K_p S,   (I + X) U = beta (V_p - e^g R),   X_jt = beta_j e^{g_j-g_t} k_j.k_t (t < j)
+//     S <- e^{g_last} S + K_p^T W,   W_j = e^{g_last - g_j} u_j.
+// This is the same state the explicit update would reach along the chunk.
+// Chunks of 32 nodes are applied in order; paths of up to 32 nodes (every
+// path of a depth-<=31 tree) take one chunk.
+//
+// One workgroup per (sequence, head), four waves of 32 d_v columns.  The
+// state slab of a wave (128 rows x 32 columns, fp32) is held in registers in
+// the 32x32 MFMA result layout for the whole commit: it is the B operand of
+// R = K_p S (with the A operand's columns stored in the matching order), and
+// the accumulator of the rank-mc update, so S is read once and written once
+// and never passes through bf16 except inside R (split hi + lo).
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 128;
+constexpr int kC = 32;          // path nodes per chunk
+constexpr int kThreads = 256;
+constexpr int kKP = kD + 8;     // row stride of the path-key / path-value tiles (bf16)
+constexpr int kBL = 40;         // row stride of 32-wide operand blocks (bf16)
+
+struct Smem {
+    uint16_t kp[kC][kKP];       // path keys, d_k index permuted within 16-blocks
+    uint16_t vp[kC][kKP];       // path values
+    uint16_t kt[kD][kBL];       // path keys transposed [d_k][path slot, permuted]
+    float d[kC][kC];            // strictly-lower X of the chunk; later also Z
+    float tinv[2][16][16];      // inverses of the two 16x16 diagonal sub-blocks
+    uint16_t th[kC][kBL], tl[kC][kBL];   // T = (I + X)^{-1}, hi / lo, permuted columns
+    int node[kC];
+    float g[kC], eg[kC], wdec[kC], beta[kC];
+    float glast;
+    int ok;
+};
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+__device__ __forceinline__ int perm(int c) { return (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1); }
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const __bf16 h = static_cast<__bf16>(x[j]);
+        hi[j] = h;
+        lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+    }
+}
+__device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// A path is valid when 0 <= m <= max_path, every id is in [0, n), the first
+// node is a root and each later node's parent is the previous node, with
+// ids strictly increasing.  Checked by one wave, one path slot per lane, so
+// the path and parent reads are two round trips rather than a chain.
+__device__ bool path_valid_wave(const int32_t *par, const int32_t *path, int m, int max_path,
+                                int n, int lane) {
+    if (m < 0 || m > max_path) return false;
+    bool bad = false;
+    for (int j0 = 0; j0 < m; j0 += 64) {
+        const int j = j0 + lane;
+        if (j < m) {
+            const int id = path[j];
+            const int prev = j == 0 ? -1 : path[j - 1];
+            if (id < 0 || id >= n || (j > 0 && prev >= id)) bad = true;
+            else if (par[id] != prev) bad = true;
+        }
+    }
+    return __ballot(bad) == 0ull;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
+    float *__restrict__ S, const int32_t *__restrict__ path, const int32_t *__restrict__ path_len,
+    int max_path, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ beta,
+    const int32_t *__restrict__ parent, int n, int H, int32_t *__restrict__ status) {
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int m = l & 31, h = l >> 5;
+    const int bh = blockIdx.x, b = bh / H, hd = bh % H;
+    const int col = 32 * w + m;
+    const int32_t *prow = path + (size_t)b * max_path;
+
+    if (w == 0) {
+        const bool ok = path_valid_wave(parent + (size_t)b * n, prow, path_len[b], max_path, n, l);
+        if (l == 0) {
+            sm.ok = ok;
+            if (hd == 0 && status) status[b] = ok ? 0 : kFaultBadPath;
+        }
+    }
+    __syncthreads();
+    if (!sm.ok) return;
+    const int mlen = path_len[b];
+    if (mlen == 0) return;
+
+    // state slab in the result layout: tile q (rows 32q..32q+31), register r
+    // holds row 32q + crow(r, h) of this lane's column
+    float *sp = S + (size_t)bh * kD * kD + col;
+    f32x16 st[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[q][r] = sp[(size_t)(32 * q + crow(r, h)) * kD];
+
+    for (int c0 = 0; c0 < mlen; c0 += kC) {
+        const int mc = min(kC, mlen - c0);
+        // ---- stage the chunk: node ids, gates, keys (two layouts), values
+        if (tid < kC) {
+            const int j = tid;
+            const int node = j < mc ? prow[c0 + j] : -1;
+            sm.node[j] = node;
+            float la = 0.f, bt = 0.f;
+            if (node >= 0) {
+                const size_t row = ((size_t)b * n + node) * H + hd;
+                la = log2f(alpha[row]);
+                bt = beta[row];
+            }
+            // inclusive prefix of the log2 decays over the chunk (32 lanes)
+            float gs = la;
+#pragma unroll
+            for (int o = 1; o < kC; o <<= 1) {
+                const float t = __shfl_up(gs, o, kC);
+                if (j >= o) gs += t;
+            }
+            const float gl = __shfl(gs, mc - 1, kC);
+            sm.g[j] = gs;
+            sm.eg[j] = exp2f(gs);
+            sm.wdec[j] = j < mc ? exp2f(gl - gs) : 0.f;
+            sm.beta[j] = bt;
+            if (j == 0) sm.glast = exp2f(gl);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int e = tid + kThreads * it, j = e >> 4, c8 = (e & 15) * 8;
+            const int node = sm.node[j];
+            uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
+            if (node >= 0) {
+                const size_t off = (((size_t)b * n + node) * H + hd) * kD + c8;
+                kr = *reinterpret_cast<const uint4 *>(k + off);
+                vr = *reinterpret_cast<const uint4 *>(v + off);
+            }
+            *reinterpret_cast<uint4 *>(&sm.vp[j][c8]) = vr;
+            const uint16_t *ke = reinterpret_cast<const uint16_t *>(&kr);
+            // permuted d_k order within each 16-block (bits 2 and 3 swap):
+            // positions c8..c8+3 and c8+4..c8+7 go to perm(c8) and perm(c8+4)
+            *reinterpret_cast<uint2 *>(&sm.kp[j][perm(c8)]) = make_uint2(kr.x, kr.y);
+            *reinterpret_cast<uint2 *>(&sm.kp[j][perm(c8 + 4)]) = make_uint2(kr.z, kr.w);
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) sm.kt[c8 + e2][perm(j)] = ke[e2];
+        }
+        __syncthreads();
+
+        // ---- chunk Gram (wave 0, transposed tile): lane (j, h) holds
+        //      k_t.k_j for t = crow(r, h); X_jt for t < j into d[j][t]
+        if (w == 0) {
+            f32x16 ga = {};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const bf16x8 a = lds8(&sm.kp[m][16 * kk + 8 * h]);
+                ga = mfma(a, a, ga);
+            }
+            const int j = m;
+            const float gj = sm.g[j], bj = sm.beta[j];
+            float x[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 g4 = *reinterpret_cast<const float4 *>(&sm.g[8 * q4 + 4 * h]);
+                const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q4 + e, t = crow(r, h);
+                    x[r] = (t < j) ? bj * __builtin_amdgcn_exp2f(gj - gt[e]) * ga[r] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<float4 *>(&sm.d[j][8 * q4 + 4 * h]) =
+                    make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+        }
+        __syncthreads();
+
+        // ---- T = (I + X)^{-1}: 16x16 diagonal inverses (32 lanes), then
+        //      the lower-left block -C^{-1} (B A^{-1})
+        if (w == 0 && l < 32) {
+            const int sbk = l >> 4, c = l & 15, o16 = 16 * sbk;
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+                for (int s4 = 0; s4 < r; s4 += 4) {
+                    const float4 xr = *reinterpret_cast<const float4 *>(&sm.d[o16 + r][o16 + s4]);
+                    acc = fmaf(-xr.x, t[s4], acc);
+                    if (s4 + 1 < r) acc = fmaf(-xr.y, t[s4 + 1], acc);
+                    if (s4 + 2 < r) acc = fmaf(-xr.z, t[s4 + 2], acc);
+                    if (s4 + 3 < r) acc = fmaf(-xr.w, t[s4 + 3], acc);
+                }
+                t[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.tinv[sbk][r][c] = t[r];
+        }
+        __syncthreads();
+        {   // Z = B A^{-1} (one entry per thread), over the dead upper-left block
+            const int r = tid >> 4, c = tid & 15;
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) acc = fmaf(sm.d[16 + r][s], sm.tinv[0][s][c], acc);
+            __syncthreads();
+            sm.d[r][c] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + kThreads * u, r = idx >> 5, c = idx & 31;
+            float val;
+            if (r < 16) {
+                val = c < 16 ? sm.tinv[0][r][c] : 0.f;
+            } else if (c >= 16) {
+                val = sm.tinv[1][r - 16][c - 16];
+            } else {
+                float acc = 0.f;
+#pragma unroll
+                for (int s = 0; s < 16; ++s) acc = fmaf(sm.tinv[1][r - 16][s], sm.d[s][c], acc);
+                val = -acc;
+            }
+            const __bf16 hv = static_cast<__bf16>(val);
+            sm.th[r][perm(c)] = __builtin_bit_cast(uint16_t, hv);
+            sm.tl[r][perm(c)] = bf16_bits(val - static_cast<float>(hv));
+        }
+        __syncthreads();
+
+        // ---- R = K_p S: B operands straight from the state tiles
+        f32x16 R = {};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                float sv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sv[j] = st[q][8 * kk + j];
+                bf16x8 sh, sl;
+                split8(sv, sh, sl);
+                const bf16x8 a = lds8(&sm.kp[m][32 * q + 16 * kk + 8 * h]);
+                R = mfma(a, sh, R);
+                R = mfma(a, sl, R);
+            }
+
+        // ---- right-hand side and U = T RHS, scaled by the decay to the chunk end
+        f32x16 rhs;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = crow(r, h);
+            const float vv = to_f32(sm.vp[j][col]);
+            rhs[r] = sm.beta[j] * (vv - sm.eg[j] * R[r]);
+        }
+        f32x16 U = {};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            float bv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bv[j] = rhs[8 * kk + j];
+            bf16x8 bhh, bll;
+            split8(bv, bhh, bll);
+            const bf16x8 ah = lds8(&sm.th[m][16 * kk + 8 * h]);
+            const bf16x8 al = lds8(&sm.tl[m][16 * kk + 8 * h]);
+            U = mfma(ah, bhh, U);
+            U = mfma(ah, bll, U);
+            U = mfma(al, bhh, U);
+        }
+        bf16x8 wh[2], wl[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            float wv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wv[j] = sm.wdec[crow(8 * kk + j, h)] * U[8 * kk + j];
+            split8(wv, wh[kk], wl[kk]);
+        }
+
+        // ---- S <- e^{g_last} S + K_p^T W  (K_p exact in bf16; W split)
+        const float gl = sm.glast;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x16 acc = st[q] * gl;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 a = lds8(&sm.kt[32 * q + m][16 * kk + 8 * h]);
+                acc = mfma(a, wh[kk], acc);
+                acc = mfma(a, wl[kk], acc);
+            }
+            st[q] = acc;
+        }
+        __syncthreads();   // the chunk tiles are restaged next
+    }
+
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sp[(size_t)(32 * q + crow(r, h)) * kD] = st[q][r];
+}
+
+}  // namespace
+
+bool commit_mfma_supports(const CommitArgs &a) {
+    return a.dtype == GDN_DTYPE_BF16 && a.dk == kD && a.dv == kD;
+}
+
+hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(commit_mfma_kernel, dim3((unsigned)(a.batch * a.H)), dim3(kThreads), 0, s,
+                       a.S, a.path, a.path_len, a.max_path, (const uint16_t *)a.k,
+                       (const uint16_t *)a.v, a.alpha, a.beta, a.parent, a.n, a.H, a.status);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -32,11 +32,17 @@ struct CommitArgs {
     int32_t *status;
 };
 
+// number of compute units of the current device (cached per device); only
+// used to shape work placement, never for correctness
+int device_cu_count();
+
 // every launcher returns the launch's hipError_t (hipGetLastError after it)
 hipError_t launch_verify_generic(const VerifyArgs &a, hipStream_t s);
 bool verify_mfma_supports(const VerifyArgs &a);
 hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
+bool commit_mfma_supports(const CommitArgs &a);
+hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s);
 hipError_t launch_path(const int32_t *parent, const int32_t *accepted,
                        int32_t *path, int32_t *path_len, int batch, int n,
                        int max_path, int32_t *status, hipStream_t s);

@@ -103,22 +103,34 @@ __device__ __forceinline__ void st8(uint16_t *p, const bf16x8 &x) {
     *reinterpret_cast<bf16x8 *>(p) = x;
 }
 
-// C += A * B for fp32 A (hi/lo blocks in LDS, permuted columns) and an fp32
-// B held as a 32x32 result tile (three bf16 products)
-__device__ __forceinline__ f32x16 mm3(const uint16_t (*ah)[kBL], const uint16_t (*al)[kBL],
-                                      const f32x16 &b, f32x16 c, int m, int h) {
+// a 32x32 fp32 result tile as B operands: two k-steps, bf16 hi and lo
+struct SplitTile {
+    bf16x8 hi[2], lo[2];
+};
+
+__device__ __forceinline__ SplitTile split_tile(const f32x16 &b) {
+    SplitTile t;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         float bv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) bv[j] = b[8 * kk + j];
-        bf16x8 bh, bl;
-        split8(bv, bh, bl);
+        split8(bv, t.hi[kk], t.lo[kk]);
+    }
+    return t;
+}
+
+// C += A * B for fp32 A (hi/lo blocks in LDS, permuted columns) and an fp32
+// B given as a split result tile (three bf16 products per k-step)
+__device__ __forceinline__ f32x16 mm3(const uint16_t (*ah)[kBL], const uint16_t (*al)[kBL],
+                                      const SplitTile &b, f32x16 c, int m, int h) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
         const bf16x8 a_h = lds8(&ah[m][16 * kk + 8 * h]);
         const bf16x8 a_l = lds8(&al[m][16 * kk + 8 * h]);
-        c = mfma(a_h, bh, c);
-        c = mfma(a_h, bl, c);
-        c = mfma(a_l, bh, c);
+        c = mfma(a_h, b.hi[kk], c);
+        c = mfma(a_h, b.lo[kk], c);
+        c = mfma(a_l, b.hi[kk], c);
     }
     return c;
 }
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta,
     const int32_t *__restrict__ parent, const float *__restrict__ S0, float *__restrict__ out,
-    int n, int H, int32_t *__restrict__ status) {
+    int n, int H, int ncu, int32_t *__restrict__ status) {
     __shared__ Smem sm;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int m = l & 31, h = l >> 5;        // row / column within a 32x32 tile, lane half
@@ -136,8 +148,8 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     const size_t rstride = (size_t)H * kD;   // elements between consecutive nodes
     const size_t base = ((size_t)b * n * H + hd) * kD;   // node 0 of this (sequence, head)
 
-    // ---- 1. loads: Q, K, V tiles (16-byte rows chunks, to LDS), gates and
-    //         parents (wave 3, one lane per node), this wave's S0 slab
+    // ---- 1. loads: Q, K, V tiles (16-byte row chunks, to LDS), gates and
+    //         parents (wave 3, one lane per node); then this wave's S0 slab
     uint4 st[12];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -157,13 +169,6 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
         la = log2f(alpha[row]);
         bt = beta[row];
     }
-    const float *s0p = S0 + (size_t)bh * kD * kD + col;
-    float s0[8][8];     // [k-step][j]: S0 row 16 kk + 8 h + j, this lane's column
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s0[kk][j] = s0p[(size_t)(16 * kk + 8 * h + j) * kD];
-
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int e = tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
@@ -172,6 +177,22 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
         *reinterpret_cast<uint4 *>(&sm.b.v[row][c8]) = st[8 + it];
     }
     __syncthreads();
+
+    // The S0 slab is requested only after the Q/K/V tiles have landed, and
+    // a wave that issues it stalls until the memory system has accepted the
+    // whole slab.  The two workgroups resident on a CU (dispatch rounds r
+    // and r + 1) therefore take opposite orders: one streams its state
+    // first and builds the tree matrices afterwards, the other builds them
+    // while its neighbour streams, then streams its own.
+    const bool state_first = ((blockIdx.x / ncu) & 1) == 0;
+    const float *s0p = S0 + (size_t)bh * kD * kD + col;
+    float s0[8][8];     // [k-step][j]: S0 row 16 kk + 8 h + j, this lane's column
+    if (state_first) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s0[kk][j] = s0p[(size_t)(16 * kk + 8 * h + j) * kD];
+    }
 
     // ---- 2. transposed Gram tiles (waves 0-2), topology (wave 3), V -> registers
     // Wave w owns block (mt, nt) = (0,0), (1,0), (1,1) of the node x node
@@ -255,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * q4 + e, s = 32 * nt + crow(r, h);
                 const bool star = (anc >> s) & 1ull;
-                const float wt = star ? exp2f(gi - gs4[e]) : 0.f;
+                const float wt = star ? __builtin_amdgcn_exp2f(gi - gs4[e]) : 0.f;
                 y[r] = wt * gc[r];
                 x[r] = (star && s != i) ? bi * wt * ga[r] : 0.f;
             }
@@ -327,27 +348,40 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
         sb.d[blk][r][c] = zv[u];
     }
     __syncthreads();
-    // T_b assembled: [[A^-1, 0], [-C^-1 Z, C^-1]], split hi/lo, permuted columns
+    // T_b assembled: [[A^-1, 0], [-C^-1 Z, C^-1]], split hi/lo, permuted
+    // columns.  The lower-left products first (two per thread, uniform),
+    // then the copied and zero quadrants.
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int idx = tid + kThreads * u, blk = idx >> 10, r = (idx >> 5) & 31, c = idx & 31;
-        float val;
-        if (r < 16) {
-            val = c < 16 ? sb.tinv[2 * blk][r][c] : 0.f;
-        } else if (c >= 16) {
-            val = sb.tinv[2 * blk + 1][r - 16][c - 16];
-        } else {
-            float acc = 0.f;
+    for (int u = 0; u < 2; ++u) {
+        const int idx = tid + kThreads * u, blk = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+        float acc = 0.f;
 #pragma unroll
-            for (int s = 0; s < 16; ++s) acc = fmaf(sb.tinv[2 * blk + 1][r - 16][s], sb.d[blk][s][c], acc);
-            val = -acc;
-        }
+        for (int s = 0; s < 16; ++s) acc = fmaf(sb.tinv[2 * blk + 1][r][s], sb.d[blk][s][c], acc);
+        const float val = -acc;
+        const __bf16 hv = static_cast<__bf16>(val);
+        sb.th[blk][16 + r][perm(c)] = __builtin_bit_cast(uint16_t, hv);
+        sb.tl[blk][16 + r][perm(c)] = bf16_bits(val - static_cast<float>(hv));
+    }
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+        // 1536 entries: per block, quadrants upper-left, upper-right, lower-right
+        const int idx = tid + kThreads * u, blk = idx / 768, rem = idx % 768;
+        const int quad = rem >> 8, r16 = (rem >> 4) & 15, c16 = rem & 15;
+        const int r = quad == 2 ? 16 + r16 : r16, c = quad == 0 ? c16 : 16 + c16;
+        const float val = quad == 0 ? sb.tinv[2 * blk][r16][c16]
+                                    : (quad == 2 ? sb.tinv[2 * blk + 1][r16][c16] : 0.f);
         const __bf16 hv = static_cast<__bf16>(val);
         sb.th[blk][r][perm(c)] = __builtin_bit_cast(uint16_t, hv);
         sb.tl[blk][r][perm(c)] = bf16_bits(val - static_cast<float>(hv));
     }
 
     // ---- 5. P = Q S0 and R = K S0 for this wave's 32 columns
+    if (!state_first) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s0[kk][j] = s0p[(size_t)(16 * kk + 8 * h + j) * kD];
+    }
     f32x16 P[2] = {}, R[2] = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -385,12 +419,13 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
             }
         }
     const f32x16 zero = {};
-    const f32x16 u0 = mm3(sb.th[0], sb.tl[0], rhs[0], zero, m, h);
-    const f32x16 z1 = mm3(sb.xh, sb.xl, u0, rhs[1], m, h);
-    const f32x16 u1 = mm3(sb.th[1], sb.tl[1], z1, zero, m, h);
-    f32x16 o0 = mm3(sb.yh[0], sb.yl[0], u0, P[0], m, h);
-    f32x16 o1 = mm3(sb.yh[1], sb.yl[1], u0, P[1], m, h);
-    o1 = mm3(sb.yh[2], sb.yl[2], u1, o1, m, h);
+    const f32x16 u0 = mm3(sb.th[0], sb.tl[0], split_tile(rhs[0]), zero, m, h);
+    const SplitTile u0s = split_tile(u0);
+    const f32x16 z1 = mm3(sb.xh, sb.xl, u0s, rhs[1], m, h);
+    const f32x16 u1 = mm3(sb.th[1], sb.tl[1], split_tile(z1), zero, m, h);
+    f32x16 o0 = mm3(sb.yh[0], sb.yl[0], u0s, P[0], m, h);
+    f32x16 o1 = mm3(sb.yh[1], sb.yl[1], u0s, P[1], m, h);
+    o1 = mm3(sb.yh[2], sb.yl[2], split_tile(u1), o1, m, h);
 
     // ---- 7. stage the output rows in LDS, then store whole rows
 #pragma unroll
@@ -417,7 +452,8 @@ bool verify_mfma_supports(const VerifyArgs &a) {
 hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(verify_mfma_n64_kernel, dim3((unsigned)(a.batch * a.H)), dim3(kThreads), 0,
                        s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, a.status);
+                       a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, device_cu_count(),
+                       a.status);
     return hipGetLastError();
 }
 
