@@ -11,9 +11,14 @@ before timing and are used round-robin, so the 256 MiB Infinity Cache cannot
 serve repeated reads; each commit advances its own set's state in place, the
 way a decoding loop would.
 
+Timed regions (HIP events on the launch stream, start and end only, so no
+event fence sits between kernels): K whole steps (the headline value), then
+K back-to-back verify launches and K back-to-back commit launches over the
+same rotating sets (per-kernel means; they include the dispatch gap between
+consecutive kernels).
+
 Prints one JSON line.  `roofline` is for the verify kernel: algorithmic
-bytes per launch / mean launch time from HIP events recorded on the launch
-stream around every verify in the timed loop.  `traffic` is read from the
+bytes per launch / its mean launch time.  `traffic` is read from the
 committed rocprofv3 counter summary when it was taken on the current kernel
 source, else null.  `cpu_baseline` times the fp64 oracle (test
 infrastructure) on the host cores on the same workload.
@@ -35,7 +40,7 @@ HBM_PEAK_GBPS = 8000.0
 WORKLOAD_INDEX = 2
 # arithmetic of the verify path: bf16 operands feed the MFMA contractions with
 # fp32 accumulation; everything else is fp32
-KERNEL_DTYPE = "f32"
+KERNEL_DTYPE = "bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_b16_n64_h32_d128_traffic.txt")
 
 
@@ -81,22 +86,33 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(ts, path, plen):
-    """the fp64 oracle (literal definition, memoised walk) on the host cores"""
+def cpu_baseline(ts, path, plen, budget_s=10.0):
+    """the fp64 oracle (memoised walk of the explicit recurrence) on the host
+    cores: whole steps (verify + commit) of the same workload, repeated until
+    about `budget_s` seconds of CPU time have been spent"""
     import oracle
     threads = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    _, _, used = oracle.verify(ts.q, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, ts.S0,
-                               memo=True, nthreads=threads, return_threads=True)
-    t1 = time.perf_counter()
-    oracle.commit(ts.S0, path, plen, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, nthreads=threads)
-    t2 = time.perf_counter()
+    tv = tc = 0.0
+    steps = 0
+    used = threads
+    while tv + tc < budget_s and steps < 1000:
+        t0 = time.perf_counter()
+        _, _, used = oracle.verify(ts.q, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, ts.S0,
+                                   memo=True, nthreads=threads, return_threads=True)
+        t1 = time.perf_counter()
+        oracle.commit(ts.S0, path, plen, ts.k, ts.v, ts.alpha, ts.beta, ts.parent,
+                      nthreads=threads)
+        t2 = time.perf_counter()
+        tv += t1 - t0
+        tc += t2 - t1
+        steps += 1
     nodes = ts.parent.shape[0] * ts.parent.shape[1]
-    return {"value": nodes / (t2 - t0), "unit": "nodes/s", "cores": int(used), "kind": "oracle",
-            "sample": f"one full step of the same workload ({ts.parent.shape[0]} sequences x "
-                      f"{ts.q.shape[2]} heads x {ts.parent.shape[1]} nodes): fp64 verify "
-                      f"{t1 - t0:.2f} s + commit {t2 - t1:.2f} s",
-            "verify_s": t1 - t0, "commit_s": t2 - t1}
+    return {"value": steps * nodes / (tv + tc), "unit": "nodes/s", "cores": int(used),
+            "kind": "oracle",
+            "sample": f"{steps} full steps of the same workload ({ts.parent.shape[0]} sequences "
+                      f"x {ts.q.shape[2]} heads x {ts.parent.shape[1]} nodes, fp64 verify + "
+                      f"commit), {tv + tc:.1f} s",
+            "verify_s_per_step": tv / steps, "commit_s_per_step": tc / steps}
 
 
 def main():
@@ -163,33 +179,34 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        d = sets[i % len(sets)]
-        e0, e1, e2 = ev[i]
-        e0.record(stream)
+
+    def timed(body):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            body(sets[i % len(sets)])
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K
+
+    def verify_only(d):
         g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"], out=d["out"],
                  stream=stream)
-        e1.record(stream)
+
+    def commit_only(d):
         g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
                  stream=stream)
-        e2.record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ver_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    com_ms = [b.elapsed_time(c) for _, b, c in ev]
-    ms_step = total_ms / K
+
+    ms_step = timed(step)
+    ver_ms = timed(verify_only)
+    com_ms = timed(commit_only)
     nodes = batch * n
     vbytes = verify_bytes(batch, n, H, dk, dv)
     mean_plen = float(np.mean([float(np.sum(d["plen_host"])) for d in sets]))
     cbytes = commit_bytes(batch, H, dk, dv, [mean_plen])
-    v_mean_s = float(np.mean(ver_ms)) * 1e-3
-    c_mean_s = float(np.mean(com_ms)) * 1e-3
+    v_mean_s = ver_ms * 1e-3
+    c_mean_s = com_ms * 1e-3
     achieved = vbytes / v_mean_s / 1e9
     traffic = read_traffic()
 
