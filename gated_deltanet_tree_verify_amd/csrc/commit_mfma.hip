@@ -54,12 +54,30 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+    // hi = bf16(x) (round to nearest even); the residual x - hi is exact in
+    // fp32 and comes out of one dot2 per element: (-1, 0).(hi0, hi1) + x0.
+    // The (-1, 0) and (0, -1) pairs are kept in scalar registers: written as
+    // constants, the compiler encodes one of them as the inline float
+    // constant -1.0, which the dot2 instruction reads as a different bf16
+    // pair (checked on gfx950: every lane wrong).
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t n0b, n1b;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(n0b));
+    asm("s_mov_b32 %0, 0xbf800000" : "=s"(n1b));
+    const bf16x2 n0 = __builtin_bit_cast(bf16x2, n0b);
+    const bf16x2 n1 = __builtin_bit_cast(bf16x2, n1b);
+    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const __bf16 h = static_cast<__bf16>(x[j]);
-        hi[j] = h;
-        lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+    for (int j = 0; j < 4; ++j) {
+        const bf16x2 h2 = {static_cast<__bf16>(x[2 * j]), static_cast<__bf16>(x[2 * j + 1])};
+        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h2, n0, x[2 * j], false);
+        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h2, n1, x[2 * j + 1], false);
+        const bf16x2 l2 = {static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
+        hw[j] = __builtin_bit_cast(uint32_t, h2);
+        lw[j] = __builtin_bit_cast(uint32_t, l2);
     }
+    hi = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
 }
 __device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
@@ -91,7 +109,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     const float *__restrict__ alpha, const float *__restrict__ beta,
     const int32_t *__restrict__ parent, int n, int H, int32_t *__restrict__ status) {
     __shared__ Smem sm;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    // the wave index is uniform: keep it scalar so role branches stay scalar
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int m = l & 31, h = l >> 5;
     const int bh = blockIdx.x, b = bh / H, hd = bh % H;
     const int col = 32 * w + m;

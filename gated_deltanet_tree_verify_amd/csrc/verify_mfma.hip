@@ -87,12 +87,30 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 
 // x = hi + lo + O(2^-17 |x|), hi and lo bf16 (round to nearest even)
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+    // hi = bf16(x) (round to nearest even); the residual x - hi is exact in
+    // fp32 and comes out of one dot2 per element: (-1, 0).(hi0, hi1) + x0.
+    // The (-1, 0) and (0, -1) pairs are kept in scalar registers: written as
+    // constants, the compiler encodes one of them as the inline float
+    // constant -1.0, which the dot2 instruction reads as a different bf16
+    // pair (checked on gfx950: every lane wrong).
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t n0b, n1b;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(n0b));
+    asm("s_mov_b32 %0, 0xbf800000" : "=s"(n1b));
+    const bf16x2 n0 = __builtin_bit_cast(bf16x2, n0b);
+    const bf16x2 n1 = __builtin_bit_cast(bf16x2, n1b);
+    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const __bf16 h = static_cast<__bf16>(x[j]);
-        hi[j] = h;
-        lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+    for (int j = 0; j < 4; ++j) {
+        const bf16x2 h2 = {static_cast<__bf16>(x[2 * j]), static_cast<__bf16>(x[2 * j + 1])};
+        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h2, n0, x[2 * j], false);
+        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h2, n1, x[2 * j + 1], false);
+        const bf16x2 l2 = {static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
+        hw[j] = __builtin_bit_cast(uint32_t, h2);
+        lw[j] = __builtin_bit_cast(uint32_t, l2);
     }
+    hi = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
 }
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {
@@ -141,7 +159,8 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     const int32_t *__restrict__ parent, const float *__restrict__ S0, float *__restrict__ out,
     int n, int H, int ncu, int32_t *__restrict__ status) {
     __shared__ Smem sm;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    // the wave index is uniform: keep it scalar so role branches stay scalar
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int m = l & 31, h = l >> 5;        // row / column within a 32x32 tile, lane half
     const int bh = blockIdx.x, b = bh / H, hd = bh % H;
     const int col = 32 * w + m;              // this lane's d_v column
@@ -150,6 +169,15 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
 
     // ---- 1. loads: Q, K, V tiles (16-byte row chunks, to LDS), gates and
     //         parents (wave 3, one lane per node); then this wave's S0 slab
+    int p = -1;
+    float la = 0.f, bt = 0.f;
+    const bool node_ok = (w == 3) && (l < n);
+    if (node_ok) {
+        const size_t row = ((size_t)b * n + l) * H + hd;
+        p = parent[(size_t)b * n + l];
+        la = alpha[row];
+        bt = beta[row];
+    }
     uint4 st[12];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -160,14 +188,35 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
         st[4 + it] = in ? *reinterpret_cast<const uint4 *>(k + off) : make_uint4(0, 0, 0, 0);
         st[8 + it] = in ? *reinterpret_cast<const uint4 *>(v + off) : make_uint4(0, 0, 0, 0);
     }
-    int p = -1;
-    float la = 0.f, bt = 0.f;
-    const bool node_ok = (w == 3) && (l < n);
-    if (node_ok) {
-        const size_t row = ((size_t)b * n + l) * H + hd;
-        p = parent[(size_t)b * n + l];
-        la = log2f(alpha[row]);
-        bt = beta[row];
+    if (w == 3) {
+        // tree topology while the tiles are in flight (the gates were
+        // requested first): pointer jumping, one lane per node; after round
+        // r every node has folded in its nearest 2^(r+1) path nodes
+        const bool badi = node_ok && !parent_ok(p, l);
+        const unsigned long long badm = __ballot(badi);
+        unsigned long long anc = node_ok ? (1ull << l) : 0ull;
+        int jmp = (node_ok && !badi) ? p : -1;
+        float gs = node_ok ? log2f(la) : 0.f;
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            const int src = jmp >= 0 ? jmp : l;
+            const unsigned lo = __shfl((unsigned)anc, src), hi = __shfl((unsigned)(anc >> 32), src);
+            const float g2 = __shfl(gs, src);
+            const int j2 = __shfl(jmp, src);
+            if (jmp >= 0) {
+                anc |= ((unsigned long long)hi << 32) | lo;
+                gs += g2;
+                jmp = j2;
+            }
+        }
+        sm.anc[l] = anc;
+        sm.g[l] = gs;
+        sm.eg[l] = node_ok ? exp2f(gs) : 0.f;
+        sm.beta[l] = bt;
+        if (l == 0) {
+            sm.bad = badm != 0ull;
+            if (hd == 0 && status) status[b] = badm ? kFaultBadParent : 0;
+        }
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -189,12 +238,14 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     float s0[8][8];     // [k-step][j]: S0 row 16 kk + 8 h + j, this lane's column
     if (state_first) {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
+        for (int kk = 0; kk < 8; ++kk) {
+            const float *rowp = s0p + (size_t)(16 * kk + 8 * h) * kD;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s0[kk][j] = s0p[(size_t)(16 * kk + 8 * h + j) * kD];
+            for (int j = 0; j < 8; ++j) s0[kk][j] = rowp[j * kD];
+        }
     }
 
-    // ---- 2. transposed Gram tiles (waves 0-2), topology (wave 3), V -> registers
+    // ---- 2. transposed Gram tiles (waves 0-2), V -> registers
     // Wave w owns block (mt, nt) = (0,0), (1,0), (1,1) of the node x node
     // matrices and computes it transposed: lane (node i = 32 mt + m, half h)
     // holds k_s.q_i and k_s.k_i for s = 32 nt + crow(r, h), exactly the
@@ -210,34 +261,6 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
             const bf16x8 ki = lds8(&sm.a.t.k[32 * mt + m][16 * kk + 8 * h]);
             gc = mfma(ks, qi, gc);
             ga = mfma(ks, ki, ga);
-        }
-    } else {
-        // pointer jumping, one lane per node: after round r every node has
-        // folded in its nearest 2^(r+1) path nodes (mask bits, log2 decays)
-        const bool badi = node_ok && !parent_ok(p, l);
-        const unsigned long long badm = __ballot(badi);
-        unsigned long long anc = node_ok ? (1ull << l) : 0ull;
-        int jmp = (node_ok && !badi) ? p : -1;
-        float gs = la;
-#pragma unroll
-        for (int r = 0; r < 6; ++r) {
-            const int src = jmp >= 0 ? jmp : l;
-            const unsigned lo = __shfl((unsigned)anc, src), hi = __shfl((unsigned)(anc >> 32), src);
-            const float g2 = __shfl(gs, src);
-            const int j2 = __shfl(jmp, src);
-            if (jmp >= 0) {
-                anc |= ((unsigned long long)hi << 32) | lo;
-                gs += g2;
-                jmp = j2;
-            }
-        }
-        sm.anc[l] = anc;
-        sm.g[l] = gs;
-        sm.eg[l] = node_ok ? exp2f(gs) : 0.f;
-        sm.beta[l] = bt;
-        if (l == 0) {
-            sm.bad = badm != 0ull;
-            if (hd == 0 && status) status[b] = badm ? kFaultBadParent : 0;
         }
     }
     uint32_t vpk[2][8];   // V in this lane's result-tile layout, bf16 pairs
@@ -265,7 +288,10 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     SolveBlocks &sb = sm.b.s;
     if (w < 3) {
         const int il = m, i = 32 * mt + m;
+        // ancestor bits of node i inside key block nt, pre-shifted by this
+        // lane half's row offset so that register r tests a constant bit
         const unsigned long long anc = sm.anc[i];
+        const uint32_t mb = (uint32_t)(anc >> (32 * nt)) >> (4 * h);
         const float gi = sm.g[i], bi = sm.beta[i];
         float y[16], x[16];
 #pragma unroll
@@ -274,11 +300,12 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
             const float gs4[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 4 * q4 + e, s = 32 * nt + crow(r, h);
-                const bool star = (anc >> s) & 1ull;
+                const int r = 4 * q4 + e;
+                const bool star = (mb >> (8 * q4 + e)) & 1u;
                 const float wt = star ? __builtin_amdgcn_exp2f(gi - gs4[e]) : 0.f;
                 y[r] = wt * gc[r];
-                x[r] = (star && s != i) ? bi * wt * ga[r] : 0.f;
+                // the diagonal of X is never read (strictly lower use only)
+                x[r] = (bi * wt) * ga[r];
             }
         }
         const int yb = w;
@@ -331,56 +358,63 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
         for (int r = 0; r < 16; ++r) sb.tinv[sbk][r][c] = t[r];
     }
     __syncthreads();
-    // Z_b = B_b A_b^{-1}, written over the dead upper-left sub-block of d[b]
-    float zv[2];
+    // Z_b = B_b A_b^{-1} into the upper-left sub-block of d[b] (read only by
+    // the forward substitution above), two entries per thread
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int idx = tid + kThreads * u, blk = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
         float acc = 0.f;
 #pragma unroll
         for (int s = 0; s < 16; ++s) acc = fmaf(sb.d[blk][16 + r][s], sb.tinv[2 * blk][s][c], acc);
-        zv[u] = acc;
+        sb.d[blk][r][c] = acc;
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int idx = tid + kThreads * u, blk = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
-        sb.d[blk][r][c] = zv[u];
-    }
-    __syncthreads();
-    // T_b assembled: [[A^-1, 0], [-C^-1 Z, C^-1]], split hi/lo, permuted
-    // columns.  The lower-left products first (two per thread, uniform),
-    // then the copied and zero quadrants.
+    // L_b = -C_b^{-1} Z_b into the lower-left sub-block (B_b is no longer read)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int idx = tid + kThreads * u, blk = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
         float acc = 0.f;
 #pragma unroll
         for (int s = 0; s < 16; ++s) acc = fmaf(sb.tinv[2 * blk + 1][r][s], sb.d[blk][s][c], acc);
-        const float val = -acc;
-        const __bf16 hv = static_cast<__bf16>(val);
-        sb.th[blk][16 + r][perm(c)] = __builtin_bit_cast(uint16_t, hv);
-        sb.tl[blk][16 + r][perm(c)] = bf16_bits(val - static_cast<float>(hv));
+        sb.d[blk][16 + r][c] = -acc;
     }
-#pragma unroll
-    for (int u = 0; u < 6; ++u) {
-        // 1536 entries: per block, quadrants upper-left, upper-right, lower-right
-        const int idx = tid + kThreads * u, blk = idx / 768, rem = idx % 768;
-        const int quad = rem >> 8, r16 = (rem >> 4) & 15, c16 = rem & 15;
-        const int r = quad == 2 ? 16 + r16 : r16, c = quad == 0 ? c16 : 16 + c16;
-        const float val = quad == 0 ? sb.tinv[2 * blk][r16][c16]
-                                    : (quad == 2 ? sb.tinv[2 * blk + 1][r16][c16] : 0.f);
-        const __bf16 hv = static_cast<__bf16>(val);
-        sb.th[blk][r][perm(c)] = __builtin_bit_cast(uint16_t, hv);
-        sb.tl[blk][r][perm(c)] = bf16_bits(val - static_cast<float>(hv));
+    __syncthreads();
+    // T_b = [[A^-1, 0], [L, C^-1]] as bf16 hi/lo operand rows: each thread
+    // fills one 8-entry chunk (permuted positions 8 seg .. 8 seg + 7, i.e.
+    // columns 16 kb + 4 hb + {0..3} and 16 kb + 8 + 4 hb + {0..3})
+    {
+        const int blk = tid >> 7, r = (tid >> 2) & 31, seg = tid & 3, kb = seg >> 1, hb = seg & 1;
+        const int c0 = 16 * kb + 4 * hb;
+        float4 lo4, hi4;
+        if (r < 16) {
+            if (kb == 0) {
+                lo4 = *reinterpret_cast<const float4 *>(&sb.tinv[2 * blk][r][c0]);
+                hi4 = *reinterpret_cast<const float4 *>(&sb.tinv[2 * blk][r][c0 + 8]);
+            } else {
+                lo4 = hi4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        } else if (kb == 1) {
+            lo4 = *reinterpret_cast<const float4 *>(&sb.tinv[2 * blk + 1][r - 16][c0 - 16]);
+            hi4 = *reinterpret_cast<const float4 *>(&sb.tinv[2 * blk + 1][r - 16][c0 - 8]);
+        } else {
+            lo4 = *reinterpret_cast<const float4 *>(&sb.d[blk][r][c0]);
+            hi4 = *reinterpret_cast<const float4 *>(&sb.d[blk][r][c0 + 8]);
+        }
+        const float vals[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+        bf16x8 th8, tl8;
+        split8(vals, th8, tl8);
+        st8(&sb.th[blk][r][8 * seg], th8);
+        st8(&sb.tl[blk][r][8 * seg], tl8);
     }
 
     // ---- 5. P = Q S0 and R = K S0 for this wave's 32 columns
     if (!state_first) {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
+        for (int kk = 0; kk < 8; ++kk) {
+            const float *rowp = s0p + (size_t)(16 * kk + 8 * h) * kD;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s0[kk][j] = s0p[(size_t)(16 * kk + 8 * h + j) * kD];
+            for (int j = 0; j < 8; ++j) s0[kk][j] = rowp[j * kD];
+        }
     }
     f32x16 P[2] = {}, R[2] = {};
 #pragma unroll
