@@ -31,15 +31,15 @@ constexpr int kC = 32;          // path nodes per chunk
 constexpr int kThreads = 256;
 constexpr int kKP = kD + 8;     // row stride of the path-key / path-value tiles (bf16)
 constexpr int kBL = 40;         // row stride of 32-wide operand blocks (bf16)
+constexpr int kMaxPath = GDN_MAX_NODES;   // a valid path has at most n <= 128 nodes
 
 struct Smem {
     uint16_t kp[kC][kKP];       // path keys, d_k index permuted within 16-blocks
     uint16_t vp[kC][kKP];       // path values
-    uint16_t kt[kD][kBL];       // path keys transposed [d_k][path slot, permuted]
-    float d[kC][kC];            // strictly-lower X of the chunk; later also Z
+    float d[kC][kC];            // X of the chunk (strictly lower part used); then Z, L
     float tinv[2][16][16];      // inverses of the two 16x16 diagonal sub-blocks
     uint16_t th[kC][kBL], tl[kC][kBL];   // T = (I + X)^{-1}, hi / lo, permuted columns
-    int node[kC];
+    int pid[kMaxPath];          // path node ids, kept from the validation pass
     float g[kC], eg[kC], wdec[kC], beta[kC];
     float glast;
     int ok;
@@ -103,6 +103,152 @@ __device__ bool path_valid_wave(const int32_t *par, const int32_t *path, int m, 
     return __ballot(bad) == 0ull;
 }
 
+// Gates, rows, Gram, T = (I + X)^{-1} for the chunk starting at path slot c0.
+// Every thread of the workgroup calls this (it contains barriers).
+__device__ __forceinline__ void prepare_chunk(Smem &sm, int c0, int mlen, int b, int hd, int n,
+                                              int H, const uint16_t *__restrict__ k,
+                                              const uint16_t *__restrict__ v,
+                                              const float *__restrict__ alpha,
+                                              const float *__restrict__ beta, int tid, int w,
+                                              int l) {
+    const int m = l & 31, h = l >> 5;
+    const int mc = min(kC, mlen - c0);
+    // gates (threads < 32) and key / value rows (all threads): one round of loads
+    float la = 0.f, bt = 0.f;
+    if (tid < kC && tid < mc) {
+        const size_t row = ((size_t)b * n + sm.pid[c0 + tid]) * H + hd;
+        la = log2f(alpha[row]);
+        bt = beta[row];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int e = tid + kThreads * it, j = e >> 4, c8 = (e & 15) * 8;
+        uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
+        if (j < mc) {
+            const size_t off = (((size_t)b * n + sm.pid[c0 + j]) * H + hd) * kD + c8;
+            kr = *reinterpret_cast<const uint4 *>(k + off);
+            vr = *reinterpret_cast<const uint4 *>(v + off);
+        }
+        *reinterpret_cast<uint4 *>(&sm.vp[j][c8]) = vr;
+        // d_k order permuted within each 16-block (bits 2 and 3 swap):
+        // entries c8..c8+3 land at perm(c8), c8+4..c8+7 at perm(c8 + 4)
+        *reinterpret_cast<uint2 *>(&sm.kp[j][perm(c8)]) = make_uint2(kr.x, kr.y);
+        *reinterpret_cast<uint2 *>(&sm.kp[j][perm(c8 + 4)]) = make_uint2(kr.z, kr.w);
+    }
+    if (tid < kC) {
+        // inclusive prefix of the log2 decays over the chunk (32 lanes)
+        const int j = tid;
+        float gs = la;
+#pragma unroll
+        for (int o = 1; o < kC; o <<= 1) {
+            const float t = __shfl_up(gs, o, kC);
+            if (j >= o) gs += t;
+        }
+        const float gl = __shfl(gs, mc - 1, kC);
+        sm.g[j] = gs;
+        sm.eg[j] = exp2f(gs);
+        sm.wdec[j] = j < mc ? exp2f(gl - gs) : 0.f;
+        sm.beta[j] = bt;
+        if (j == 0) sm.glast = exp2f(gl);
+    }
+    __syncthreads();
+
+    // chunk Gram (wave 0, transposed tile): lane (j, h) holds k_t.k_j for
+    // t = crow(r, h); X_jt = beta_j e^{g_j - g_t} k_j.k_t for t < j into d[j][t]
+    if (w == 0) {
+        f32x16 ga = {};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const bf16x8 a = lds8(&sm.kp[m][16 * kk + 8 * h]);
+            ga = mfma(a, a, ga);
+        }
+        const int j = m;
+        const float gj = sm.g[j], bj = sm.beta[j];
+        float x[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 g4 = *reinterpret_cast<const float4 *>(&sm.g[8 * q4 + 4 * h]);
+            const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e, t = crow(r, h);
+                x[r] = (t < j) ? bj * __builtin_amdgcn_exp2f(gj - gt[e]) * ga[r] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<float4 *>(&sm.d[j][8 * q4 + 4 * h]) =
+                make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+    }
+    __syncthreads();
+
+    // T = (I + X)^{-1}: 16x16 diagonal inverses by forward substitution
+    // (32 lanes: sub-block, column), then Z = B A^{-1} and L = -C^{-1} Z
+    if (w == 0 && l < 32) {
+        const int sbk = l >> 4, c = l & 15, o16 = 16 * sbk;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int s4 = 0; s4 < r; s4 += 4) {
+                const float4 xr = *reinterpret_cast<const float4 *>(&sm.d[o16 + r][o16 + s4]);
+                acc = fmaf(-xr.x, t[s4], acc);
+                if (s4 + 1 < r) acc = fmaf(-xr.y, t[s4 + 1], acc);
+                if (s4 + 2 < r) acc = fmaf(-xr.z, t[s4 + 2], acc);
+                if (s4 + 3 < r) acc = fmaf(-xr.w, t[s4 + 3], acc);
+            }
+            t[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.tinv[sbk][r][c] = t[r];
+    }
+    __syncthreads();
+    {   // Z = B A^{-1} over the upper-left sub-block (read only by the substitution)
+        const int r = tid >> 4, c = tid & 15;
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) acc = fmaf(sm.d[16 + r][s], sm.tinv[0][s][c], acc);
+        sm.d[r][c] = acc;
+    }
+    __syncthreads();
+    {   // L = -C^{-1} Z over the lower-left sub-block (B is no longer read)
+        const int r = tid >> 4, c = tid & 15;
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) acc = fmaf(sm.tinv[1][r][s], sm.d[s][c], acc);
+        sm.d[16 + r][c] = -acc;
+    }
+    __syncthreads();
+    if (tid < 4 * kC) {
+        // T = [[A^-1, 0], [L, C^-1]] as bf16 hi/lo operand rows, one 8-entry
+        // chunk per thread (permuted positions 8 seg .. 8 seg + 7)
+        const int r = tid >> 2, seg = tid & 3, kb = seg >> 1, hb = seg & 1;
+        const int c0c = 16 * kb + 4 * hb;
+        float4 lo4, hi4;
+        if (r < 16) {
+            if (kb == 0) {
+                lo4 = *reinterpret_cast<const float4 *>(&sm.tinv[0][r][c0c]);
+                hi4 = *reinterpret_cast<const float4 *>(&sm.tinv[0][r][c0c + 8]);
+            } else {
+                lo4 = hi4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        } else if (kb == 1) {
+            lo4 = *reinterpret_cast<const float4 *>(&sm.tinv[1][r - 16][c0c - 16]);
+            hi4 = *reinterpret_cast<const float4 *>(&sm.tinv[1][r - 16][c0c - 8]);
+        } else {
+            lo4 = *reinterpret_cast<const float4 *>(&sm.d[r][c0c]);
+            hi4 = *reinterpret_cast<const float4 *>(&sm.d[r][c0c + 8]);
+        }
+        const float vals[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+        bf16x8 th8, tl8;
+        split8(vals, th8, tl8);
+        *reinterpret_cast<bf16x8 *>(&sm.th[r][8 * seg]) = th8;
+        *reinterpret_cast<bf16x8 *>(&sm.tl[r][8 * seg]) = tl8;
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     float *__restrict__ S, const int32_t *__restrict__ path, const int32_t *__restrict__ path_len,
     int max_path, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -117,7 +263,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     const int32_t *prow = path + (size_t)b * max_path;
 
     if (w == 0) {
-        const bool ok = path_valid_wave(parent + (size_t)b * n, prow, path_len[b], max_path, n, l);
+        const int mv = path_len[b];
+        const bool ok = path_valid_wave(parent + (size_t)b * n, prow, mv, max_path, n, l);
+        if (ok)
+            for (int j = l; j < mv; j += 64) sm.pid[j] = prow[j];
         if (l == 0) {
             sm.ok = ok;
             if (hd == 0 && status) status[b] = ok ? 0 : kFaultBadPath;
@@ -128,143 +277,29 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     const int mlen = path_len[b];
     if (mlen == 0) return;
 
-    // state slab in the result layout: tile q (rows 32q..32q+31), register r
-    // holds row 32q + crow(r, h) of this lane's column
+    // State slab in the result layout: tile q (rows 32q..32q+31), register r
+    // holds row 32q + crow(r, h) of this lane's column.
     float *sp = S + (size_t)bh * kD * kD + col;
     f32x16 st[4];
+
+    // identity operands that move a path-key tile into the result layout:
+    // k-step kb, lane (n = m, h), element e is 1 where n is the d_k index
+    // that the permuted key storage puts in that slot
+    bf16x8 ident[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            ident[kb][e] = static_cast<__bf16>(
+                (m == 16 * kb + 8 * (e >> 2) + 4 * h + (e & 3)) ? 1.f : 0.f);
+
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[q][r] = sp[(size_t)(32 * q + crow(r, h)) * kD];
 
     for (int c0 = 0; c0 < mlen; c0 += kC) {
-        const int mc = min(kC, mlen - c0);
-        // ---- stage the chunk: node ids, gates, keys (two layouts), values
-        if (tid < kC) {
-            const int j = tid;
-            const int node = j < mc ? prow[c0 + j] : -1;
-            sm.node[j] = node;
-            float la = 0.f, bt = 0.f;
-            if (node >= 0) {
-                const size_t row = ((size_t)b * n + node) * H + hd;
-                la = log2f(alpha[row]);
-                bt = beta[row];
-            }
-            // inclusive prefix of the log2 decays over the chunk (32 lanes)
-            float gs = la;
-#pragma unroll
-            for (int o = 1; o < kC; o <<= 1) {
-                const float t = __shfl_up(gs, o, kC);
-                if (j >= o) gs += t;
-            }
-            const float gl = __shfl(gs, mc - 1, kC);
-            sm.g[j] = gs;
-            sm.eg[j] = exp2f(gs);
-            sm.wdec[j] = j < mc ? exp2f(gl - gs) : 0.f;
-            sm.beta[j] = bt;
-            if (j == 0) sm.glast = exp2f(gl);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int e = tid + kThreads * it, j = e >> 4, c8 = (e & 15) * 8;
-            const int node = sm.node[j];
-            uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-            if (node >= 0) {
-                const size_t off = (((size_t)b * n + node) * H + hd) * kD + c8;
-                kr = *reinterpret_cast<const uint4 *>(k + off);
-                vr = *reinterpret_cast<const uint4 *>(v + off);
-            }
-            *reinterpret_cast<uint4 *>(&sm.vp[j][c8]) = vr;
-            const uint16_t *ke = reinterpret_cast<const uint16_t *>(&kr);
-            // permuted d_k order within each 16-block (bits 2 and 3 swap):
-            // positions c8..c8+3 and c8+4..c8+7 go to perm(c8) and perm(c8+4)
-            *reinterpret_cast<uint2 *>(&sm.kp[j][perm(c8)]) = make_uint2(kr.x, kr.y);
-            *reinterpret_cast<uint2 *>(&sm.kp[j][perm(c8 + 4)]) = make_uint2(kr.z, kr.w);
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) sm.kt[c8 + e2][perm(j)] = ke[e2];
-        }
-        __syncthreads();
-
-        // ---- chunk Gram (wave 0, transposed tile): lane (j, h) holds
-        //      k_t.k_j for t = crow(r, h); X_jt for t < j into d[j][t]
-        if (w == 0) {
-            f32x16 ga = {};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const bf16x8 a = lds8(&sm.kp[m][16 * kk + 8 * h]);
-                ga = mfma(a, a, ga);
-            }
-            const int j = m;
-            const float gj = sm.g[j], bj = sm.beta[j];
-            float x[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 g4 = *reinterpret_cast<const float4 *>(&sm.g[8 * q4 + 4 * h]);
-                const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * q4 + e, t = crow(r, h);
-                    x[r] = (t < j) ? bj * __builtin_amdgcn_exp2f(gj - gt[e]) * ga[r] : 0.f;
-                }
-            }
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<float4 *>(&sm.d[j][8 * q4 + 4 * h]) =
-                    make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
-        }
-        __syncthreads();
-
-        // ---- T = (I + X)^{-1}: 16x16 diagonal inverses (32 lanes), then
-        //      the lower-left block -C^{-1} (B A^{-1})
-        if (w == 0 && l < 32) {
-            const int sbk = l >> 4, c = l & 15, o16 = 16 * sbk;
-            float t[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == c) ? 1.f : 0.f;
-#pragma unroll
-                for (int s4 = 0; s4 < r; s4 += 4) {
-                    const float4 xr = *reinterpret_cast<const float4 *>(&sm.d[o16 + r][o16 + s4]);
-                    acc = fmaf(-xr.x, t[s4], acc);
-                    if (s4 + 1 < r) acc = fmaf(-xr.y, t[s4 + 1], acc);
-                    if (s4 + 2 < r) acc = fmaf(-xr.z, t[s4 + 2], acc);
-                    if (s4 + 3 < r) acc = fmaf(-xr.w, t[s4 + 3], acc);
-                }
-                t[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.tinv[sbk][r][c] = t[r];
-        }
-        __syncthreads();
-        {   // Z = B A^{-1} (one entry per thread), over the dead upper-left block
-            const int r = tid >> 4, c = tid & 15;
-            float acc = 0.f;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) acc = fmaf(sm.d[16 + r][s], sm.tinv[0][s][c], acc);
-            __syncthreads();
-            sm.d[r][c] = acc;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = tid + kThreads * u, r = idx >> 5, c = idx & 31;
-            float val;
-            if (r < 16) {
-                val = c < 16 ? sm.tinv[0][r][c] : 0.f;
-            } else if (c >= 16) {
-                val = sm.tinv[1][r - 16][c - 16];
-            } else {
-                float acc = 0.f;
-#pragma unroll
-                for (int s = 0; s < 16; ++s) acc = fmaf(sm.tinv[1][r - 16][s], sm.d[s][c], acc);
-                val = -acc;
-            }
-            const __bf16 hv = static_cast<__bf16>(val);
-            sm.th[r][perm(c)] = __builtin_bit_cast(uint16_t, hv);
-            sm.tl[r][perm(c)] = bf16_bits(val - static_cast<float>(hv));
-        }
-        __syncthreads();
+        prepare_chunk(sm, c0, mlen, b, hd, n, H, k, v, alpha, beta, tid, w, l);
 
         // ---- R = K_p S: B operands straight from the state tiles
         f32x16 R = {};
@@ -287,8 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int j = crow(r, h);
-            const float vv = to_f32(sm.vp[j][col]);
-            rhs[r] = sm.beta[j] * (vv - sm.eg[j] * R[r]);
+            rhs[r] = sm.beta[j] * (to_f32(sm.vp[j][col]) - sm.eg[j] * R[r]);
         }
         f32x16 U = {};
 #pragma unroll
@@ -313,14 +347,22 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
             split8(wv, wh[kk], wl[kk]);
         }
 
-        // ---- S <- e^{g_last} S + K_p^T W  (K_p exact in bf16; W split)
+        // ---- S <- e^{g_last} S + K_p^T W.  The key tile of rows 32q.. is put
+        // in the result layout by an exact identity product; that layout is
+        // the A operand of K_p^T with the path slots in the order W holds them.
         const float gl = sm.glast;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            f32x16 kt = {};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                kt = mfma(lds8(&sm.kp[m][32 * q + 16 * kb + 8 * h]), ident[kb], kt);
             f32x16 acc = st[q] * gl;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 a = lds8(&sm.kt[32 * q + m][16 * kk + 8 * h]);
+                bf16x8 a;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = static_cast<__bf16>(kt[8 * kk + e]);
                 acc = mfma(a, wh[kk], acc);
                 acc = mfma(a, wl[kk], acc);
             }
