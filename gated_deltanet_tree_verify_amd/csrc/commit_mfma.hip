@@ -1,253 +1,19 @@
 // MFMA state commit along the accepted branch, bf16 k/v, d_k = d_v = 128.
-//
-// The commitment is deferred until the accepted branch is known (DFlash-TfM
-// page, rollback-free GDN verification section), and the branch is a chain,
-// so the chunked form of the delta rule applies to it directly.  For a chunk
-// of path nodes j = 0..mc-1 (chunk-local log2 decay prefix g_j) entering with
-// state S:
-//     R = K_p S,   (I + X) U = beta (V_p - e^g R),   X_jt = beta_j e^{g_j-g_t} k_j.k_t (t < j)
-//     S <- e^{g_last} S + K_p^T W,   W_j = e^{g_last - g_j} u_j.
-// This is the same state the explicit update would reach along the chunk.
-// Chunks of 32 nodes are applied in order; paths of up to 32 nodes (every
-// path of a depth-<=31 tree) take one chunk.
-//
-// One workgroup per (sequence, head), four waves of 32 d_v columns.  The
-// state slab of a wave (128 rows x 32 columns, fp32) is held in registers in
-// the 32x32 MFMA result layout for the whole commit: it is the B operand of
-// R = K_p S (with the A operand's columns stored in the matching order), and
-// the accumulator of the rank-mc update, so S is read once and written once
-// and never passes through bf16 except inside R (split hi + lo).
-#include "device_common.hpp"
+// One workgroup per (sequence, head); the chunked commit stages are in
+// path_commit.hpp, where the method is described.  The state is read once
+// and written once.
 #include "internal.hpp"
+#include "path_commit.hpp"
 
 namespace gdn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kD = 128;
-constexpr int kC = 32;          // path nodes per chunk
-constexpr int kThreads = 256;
-constexpr int kKP = kD + 8;     // row stride of the path-key / path-value tiles (bf16)
-constexpr int kBL = 40;         // row stride of 32-wide operand blocks (bf16)
-constexpr int kMaxPath = GDN_MAX_NODES;   // a valid path has at most n <= 128 nodes
+using namespace pc;
 
 struct Smem {
-    uint16_t kp[kC][kKP];       // path keys, d_k index permuted within 16-blocks
-    uint16_t vp[kC][kKP];       // path values
-    float d[kC][kC];            // X of the chunk (strictly lower part used); then Z, L
-    float tinv[2][16][16];      // inverses of the two 16x16 diagonal sub-blocks
-    uint16_t th[kC][kBL], tl[kC][kBL];   // T = (I + X)^{-1}, hi / lo, permuted columns
-    int pid[kMaxPath];          // path node ids, kept from the validation pass
-    float g[kC], eg[kC], wdec[kC], beta[kC];
-    float glast;
-    int ok;
+    ChunkTiles ct;
+    PathIds pi;
 };
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-__device__ __forceinline__ int perm(int c) { return (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1); }
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-__device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
-    // hi = bf16(x) (round to nearest even); the residual x - hi is exact in
-    // fp32 and comes out of one dot2 per element: (-1, 0).(hi0, hi1) + x0.
-    // The (-1, 0) and (0, -1) pairs are kept in scalar registers: written as
-    // constants, the compiler encodes one of them as the inline float
-    // constant -1.0, which the dot2 instruction reads as a different bf16
-    // pair (checked on gfx950: every lane wrong).
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    uint32_t n0b, n1b;
-    asm("s_mov_b32 %0, 0xbf80" : "=s"(n0b));
-    asm("s_mov_b32 %0, 0xbf800000" : "=s"(n1b));
-    const bf16x2 n0 = __builtin_bit_cast(bf16x2, n0b);
-    const bf16x2 n1 = __builtin_bit_cast(bf16x2, n1b);
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const bf16x2 h2 = {static_cast<__bf16>(x[2 * j]), static_cast<__bf16>(x[2 * j + 1])};
-        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h2, n0, x[2 * j], false);
-        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h2, n1, x[2 * j + 1], false);
-        const bf16x2 l2 = {static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
-        hw[j] = __builtin_bit_cast(uint32_t, h2);
-        lw[j] = __builtin_bit_cast(uint32_t, l2);
-    }
-    hi = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    lo = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-}
-__device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {
-    return *reinterpret_cast<const bf16x8 *>(p);
-}
-
-// A path is valid when 0 <= m <= max_path, every id is in [0, n), the first
-// node is a root and each later node's parent is the previous node, with
-// ids strictly increasing.  Checked by one wave, one path slot per lane, so
-// the path and parent reads are two round trips rather than a chain.
-__device__ bool path_valid_wave(const int32_t *par, const int32_t *path, int m, int max_path,
-                                int n, int lane) {
-    if (m < 0 || m > max_path) return false;
-    bool bad = false;
-    for (int j0 = 0; j0 < m; j0 += 64) {
-        const int j = j0 + lane;
-        if (j < m) {
-            const int id = path[j];
-            const int prev = j == 0 ? -1 : path[j - 1];
-            if (id < 0 || id >= n || (j > 0 && prev >= id)) bad = true;
-            else if (par[id] != prev) bad = true;
-        }
-    }
-    return __ballot(bad) == 0ull;
-}
-
-// Gates, rows, Gram, T = (I + X)^{-1} for the chunk starting at path slot c0.
-// Every thread of the workgroup calls this (it contains barriers).
-__device__ __forceinline__ void prepare_chunk(Smem &sm, int c0, int mlen, int b, int hd, int n,
-                                              int H, const uint16_t *__restrict__ k,
-                                              const uint16_t *__restrict__ v,
-                                              const float *__restrict__ alpha,
-                                              const float *__restrict__ beta, int tid, int w,
-                                              int l) {
-    const int m = l & 31, h = l >> 5;
-    const int mc = min(kC, mlen - c0);
-    // gates (threads < 32) and key / value rows (all threads): one round of loads
-    float la = 0.f, bt = 0.f;
-    if (tid < kC && tid < mc) {
-        const size_t row = ((size_t)b * n + sm.pid[c0 + tid]) * H + hd;
-        la = log2f(alpha[row]);
-        bt = beta[row];
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int e = tid + kThreads * it, j = e >> 4, c8 = (e & 15) * 8;
-        uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-        if (j < mc) {
-            const size_t off = (((size_t)b * n + sm.pid[c0 + j]) * H + hd) * kD + c8;
-            kr = *reinterpret_cast<const uint4 *>(k + off);
-            vr = *reinterpret_cast<const uint4 *>(v + off);
-        }
-        *reinterpret_cast<uint4 *>(&sm.vp[j][c8]) = vr;
-        // d_k order permuted within each 16-block (bits 2 and 3 swap):
-        // entries c8..c8+3 land at perm(c8), c8+4..c8+7 at perm(c8 + 4)
-        *reinterpret_cast<uint2 *>(&sm.kp[j][perm(c8)]) = make_uint2(kr.x, kr.y);
-        *reinterpret_cast<uint2 *>(&sm.kp[j][perm(c8 + 4)]) = make_uint2(kr.z, kr.w);
-    }
-    if (tid < kC) {
-        // inclusive prefix of the log2 decays over the chunk (32 lanes)
-        const int j = tid;
-        float gs = la;
-#pragma unroll
-        for (int o = 1; o < kC; o <<= 1) {
-            const float t = __shfl_up(gs, o, kC);
-            if (j >= o) gs += t;
-        }
-        const float gl = __shfl(gs, mc - 1, kC);
-        sm.g[j] = gs;
-        sm.eg[j] = exp2f(gs);
-        sm.wdec[j] = j < mc ? exp2f(gl - gs) : 0.f;
-        sm.beta[j] = bt;
-        if (j == 0) sm.glast = exp2f(gl);
-    }
-    __syncthreads();
-
-    // chunk Gram (wave 0, transposed tile): lane (j, h) holds k_t.k_j for
-    // t = crow(r, h); X_jt = beta_j e^{g_j - g_t} k_j.k_t for t < j into d[j][t]
-    if (w == 0) {
-        f32x16 ga = {};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const bf16x8 a = lds8(&sm.kp[m][16 * kk + 8 * h]);
-            ga = mfma(a, a, ga);
-        }
-        const int j = m;
-        const float gj = sm.g[j], bj = sm.beta[j];
-        float x[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 g4 = *reinterpret_cast<const float4 *>(&sm.g[8 * q4 + 4 * h]);
-            const float gt[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * q4 + e, t = crow(r, h);
-                x[r] = (t < j) ? bj * __builtin_amdgcn_exp2f(gj - gt[e]) * ga[r] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<float4 *>(&sm.d[j][8 * q4 + 4 * h]) =
-                make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
-    }
-    __syncthreads();
-
-    // T = (I + X)^{-1}: 16x16 diagonal inverses by forward substitution
-    // (32 lanes: sub-block, column), then Z = B A^{-1} and L = -C^{-1} Z
-    if (w == 0 && l < 32) {
-        const int sbk = l >> 4, c = l & 15, o16 = 16 * sbk;
-        float t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int s4 = 0; s4 < r; s4 += 4) {
-                const float4 xr = *reinterpret_cast<const float4 *>(&sm.d[o16 + r][o16 + s4]);
-                acc = fmaf(-xr.x, t[s4], acc);
-                if (s4 + 1 < r) acc = fmaf(-xr.y, t[s4 + 1], acc);
-                if (s4 + 2 < r) acc = fmaf(-xr.z, t[s4 + 2], acc);
-                if (s4 + 3 < r) acc = fmaf(-xr.w, t[s4 + 3], acc);
-            }
-            t[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.tinv[sbk][r][c] = t[r];
-    }
-    __syncthreads();
-    {   // Z = B A^{-1} over the upper-left sub-block (read only by the substitution)
-        const int r = tid >> 4, c = tid & 15;
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) acc = fmaf(sm.d[16 + r][s], sm.tinv[0][s][c], acc);
-        sm.d[r][c] = acc;
-    }
-    __syncthreads();
-    {   // L = -C^{-1} Z over the lower-left sub-block (B is no longer read)
-        const int r = tid >> 4, c = tid & 15;
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) acc = fmaf(sm.tinv[1][r][s], sm.d[s][c], acc);
-        sm.d[16 + r][c] = -acc;
-    }
-    __syncthreads();
-    if (tid < 4 * kC) {
-        // T = [[A^-1, 0], [L, C^-1]] as bf16 hi/lo operand rows, one 8-entry
-        // chunk per thread (permuted positions 8 seg .. 8 seg + 7)
-        const int r = tid >> 2, seg = tid & 3, kb = seg >> 1, hb = seg & 1;
-        const int c0c = 16 * kb + 4 * hb;
-        float4 lo4, hi4;
-        if (r < 16) {
-            if (kb == 0) {
-                lo4 = *reinterpret_cast<const float4 *>(&sm.tinv[0][r][c0c]);
-                hi4 = *reinterpret_cast<const float4 *>(&sm.tinv[0][r][c0c + 8]);
-            } else {
-                lo4 = hi4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        } else if (kb == 1) {
-            lo4 = *reinterpret_cast<const float4 *>(&sm.tinv[1][r - 16][c0c - 16]);
-            hi4 = *reinterpret_cast<const float4 *>(&sm.tinv[1][r - 16][c0c - 8]);
-        } else {
-            lo4 = *reinterpret_cast<const float4 *>(&sm.d[r][c0c]);
-            hi4 = *reinterpret_cast<const float4 *>(&sm.d[r][c0c + 8]);
-        }
-        const float vals[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-        bf16x8 th8, tl8;
-        split8(vals, th8, tl8);
-        *reinterpret_cast<bf16x8 *>(&sm.th[r][8 * seg]) = th8;
-        *reinterpret_cast<bf16x8 *>(&sm.tl[r][8 * seg]) = tl8;
-    }
-    __syncthreads();
-}
 
 __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     float *__restrict__ S, const int32_t *__restrict__ path, const int32_t *__restrict__ path_len,
@@ -261,120 +27,30 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     const int bh = blockIdx.x, b = bh / H, hd = bh % H;
     const int col = 32 * w + m;
     const int32_t *prow = path + (size_t)b * max_path;
+    const int mlen = path_len[b];
 
     if (w == 0) {
-        const int mv = path_len[b];
-        const bool ok = path_valid_wave(parent + (size_t)b * n, prow, mv, max_path, n, l);
-        if (ok)
-            for (int j = l; j < mv; j += 64) sm.pid[j] = prow[j];
+        const bool ok = validate_and_keep(sm.pi, parent + (size_t)b * n, prow, mlen, max_path, n, l);
         if (l == 0) {
-            sm.ok = ok;
+            sm.pi.ok = ok;
             if (hd == 0 && status) status[b] = ok ? 0 : kFaultBadPath;
         }
     }
     __syncthreads();
-    if (!sm.ok) return;
-    const int mlen = path_len[b];
-    if (mlen == 0) return;
+    if (!sm.pi.ok || mlen == 0) return;
 
-    // State slab in the result layout: tile q (rows 32q..32q+31), register r
-    // holds row 32q + crow(r, h) of this lane's column.
+    // state slab: four result tiles of this lane's column
     float *sp = S + (size_t)bh * kD * kD + col;
     f32x16 st[4];
-
-    // identity operands that move a path-key tile into the result layout:
-    // k-step kb, lane (n = m, h), element e is 1 where n is the d_k index
-    // that the permuted key storage puts in that slot
+    load_state(st, sp, kD, h);
     bf16x8 ident[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            ident[kb][e] = static_cast<__bf16>(
-                (m == 16 * kb + 8 * (e >> 2) + 4 * h + (e & 3)) ? 1.f : 0.f);
-
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[q][r] = sp[(size_t)(32 * q + crow(r, h)) * kD];
-
+    key_identity(ident, m, h);
     for (int c0 = 0; c0 < mlen; c0 += kC) {
-        prepare_chunk(sm, c0, mlen, b, hd, n, H, k, v, alpha, beta, tid, w, l);
-
-        // ---- R = K_p S: B operands straight from the state tiles
-        f32x16 R = {};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                float sv[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sv[j] = st[q][8 * kk + j];
-                bf16x8 sh, sl;
-                split8(sv, sh, sl);
-                const bf16x8 a = lds8(&sm.kp[m][32 * q + 16 * kk + 8 * h]);
-                R = mfma(a, sh, R);
-                R = mfma(a, sl, R);
-            }
-
-        // ---- right-hand side and U = T RHS, scaled by the decay to the chunk end
-        f32x16 rhs;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int j = crow(r, h);
-            rhs[r] = sm.beta[j] * (to_f32(sm.vp[j][col]) - sm.eg[j] * R[r]);
-        }
-        f32x16 U = {};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float bv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bv[j] = rhs[8 * kk + j];
-            bf16x8 bhh, bll;
-            split8(bv, bhh, bll);
-            const bf16x8 ah = lds8(&sm.th[m][16 * kk + 8 * h]);
-            const bf16x8 al = lds8(&sm.tl[m][16 * kk + 8 * h]);
-            U = mfma(ah, bhh, U);
-            U = mfma(ah, bll, U);
-            U = mfma(al, bhh, U);
-        }
-        bf16x8 wh[2], wl[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float wv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) wv[j] = sm.wdec[crow(8 * kk + j, h)] * U[8 * kk + j];
-            split8(wv, wh[kk], wl[kk]);
-        }
-
-        // ---- S <- e^{g_last} S + K_p^T W.  The key tile of rows 32q.. is put
-        // in the result layout by an exact identity product; that layout is
-        // the A operand of K_p^T with the path slots in the order W holds them.
-        const float gl = sm.glast;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            f32x16 kt = {};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                kt = mfma(lds8(&sm.kp[m][32 * q + 16 * kb + 8 * h]), ident[kb], kt);
-            f32x16 acc = st[q] * gl;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 a;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] = static_cast<__bf16>(kt[8 * kk + e]);
-                acc = mfma(a, wh[kk], acc);
-                acc = mfma(a, wl[kk], acc);
-            }
-            st[q] = acc;
-        }
+        prepare_chunk(sm.ct, sm.pi.pid, c0, mlen, b, hd, n, H, k, v, alpha, beta, tid, w, l);
+        apply_chunk(sm.ct, st, ident, m, h, col);
         __syncthreads();   // the chunk tiles are restaged next
     }
-
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sp[(size_t)(32 * q + crow(r, h)) * kD] = st[q][r];
+    store_state(st, sp, kD, h);
 }
 
 }  // namespace

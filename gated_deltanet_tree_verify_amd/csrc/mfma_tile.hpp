@@ -1,0 +1,141 @@
+// 32x32x16 bf16 MFMA tile helpers shared by the verify, commit and fused
+// commit-verify kernels (gfx950).
+//
+// Conventions used throughout:
+//   * A 32x32 fp32 result tile ("result layout") is held by a wave as 16
+//     registers per lane: lane (col = l & 31, half h = l >> 5), register r
+//     holds row crow(r, h) = 8 (r >> 2) + 4 h + (r & 3).
+//   * An A operand lane (row = l & 31, h) supplies 8 bf16 for k-step kk at
+//     slots 16 kk + 8 h + e; a B operand lane (col, h) supplies the same 8
+//     slots.  Both sides use the same (h, e) -> slot pairing, so any
+//     consistent relabelling of the contraction index is exact.
+//   * A result tile fed back as a B operand supplies, for k-step kk, its
+//     registers 8 kk .. 8 kk + 7, i.e. rows crow(8 kk + e, h).  The matching
+//     A operand therefore stores its contraction index with bits 2 and 3
+//     swapped within each 16-block: position perm(c).
+//   * A result tile of Z also is, register for register, the A operand of
+//     Z^T (rows = columns of Z, contraction over the rows of Z in that same
+//     permuted order).
+//   * fp32 values enter a bf16 product split in two: x = hi + lo + O(2^-17 x).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+namespace tile {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// row of a 32x32 result tile held by lane half h in register r
+__device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// storage position of contraction index c in an A operand whose B operand
+// is a result tile: bits 2 and 3 of c swap places
+__device__ __forceinline__ int perm(int c) { return (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1); }
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ __forceinline__ void st8(uint16_t *p, const bf16x8 &x) {
+    *reinterpret_cast<bf16x8 *>(p) = x;
+}
+
+// x = hi + lo: hi = bf16(x) (round to nearest even); the residual x - hi is
+// exact in fp32 and comes out of one dot2 per element, (-1, 0).(hi0, hi1) + x0.
+// The (-1, 0) and (0, -1) pairs are kept in scalar registers: written as
+// constants, the compiler encodes one of them as the inline float constant
+// -1.0, which the dot2 instruction reads as a different bf16 pair (checked on
+// gfx950: every lane wrong).
+__device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+    uint32_t n0b, n1b;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(n0b));
+    asm("s_mov_b32 %0, 0xbf800000" : "=s"(n1b));
+    const bf16x2 n0 = __builtin_bit_cast(bf16x2, n0b);
+    const bf16x2 n1 = __builtin_bit_cast(bf16x2, n1b);
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bf16x2 h2 = {static_cast<__bf16>(x[2 * j]), static_cast<__bf16>(x[2 * j + 1])};
+        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h2, n0, x[2 * j], false);
+        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h2, n1, x[2 * j + 1], false);
+        const bf16x2 l2 = {static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
+        hw[j] = __builtin_bit_cast(uint32_t, h2);
+        lw[j] = __builtin_bit_cast(uint32_t, l2);
+    }
+    hi = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+}
+
+// registers 8 kk .. 8 kk + 7 of a result tile as split B operands
+struct SplitTile {
+    bf16x8 hi[2], lo[2];
+};
+
+__device__ __forceinline__ SplitTile split_tile(const f32x16 &b) {
+    SplitTile t;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        float bv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = b[8 * kk + j];
+        split8(bv, t.hi[kk], t.lo[kk]);
+    }
+    return t;
+}
+
+// C += A B for an fp32 A stored as hi/lo bf16 rows (permuted contraction
+// index, row stride LD) and an fp32 B given as a split result tile:
+// hi*hi + hi*lo + lo*hi
+template <int LD>
+__device__ __forceinline__ f32x16 mm3(const uint16_t (*ah)[LD], const uint16_t (*al)[LD],
+                                      const SplitTile &b, f32x16 c, int m, int h) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a_h = lds8(&ah[m][16 * kk + 8 * h]);
+        const bf16x8 a_l = lds8(&al[m][16 * kk + 8 * h]);
+        c = mfma(a_h, b.hi[kk], c);
+        c = mfma(a_h, b.lo[kk], c);
+        c = mfma(a_l, b.hi[kk], c);
+    }
+    return c;
+}
+
+// Write 8 consecutive bf16 of a global row (c8..c8+7) into an LDS row whose
+// contraction index is stored permuted within 16-blocks: entries c8..c8+3
+// land at perm(c8), c8+4..c8+7 at perm(c8 + 4).
+__device__ __forceinline__ void store_row8_permuted(uint16_t *row, int c8, const uint4 &x) {
+    *reinterpret_cast<uint2 *>(&row[perm(c8)]) = make_uint2(x.x, x.y);
+    *reinterpret_cast<uint2 *>(&row[perm(c8 + 4)]) = make_uint2(x.z, x.w);
+}
+
+// The state slab of a wave: rows 0..127 of its 32 columns as four result
+// tiles, tile q holding rows 32 q + crow(r, h).  p points at row 0 of the
+// lane's column; rs is the row stride in elements.
+__device__ __forceinline__ void load_state(f32x16 (&st)[4], const float *p, int rs, int h) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[q][r] = p[(size_t)(32 * q + crow(r, h)) * rs];
+}
+
+__device__ __forceinline__ void store_state(const f32x16 (&st)[4], float *p, int rs, int h) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[(size_t)(32 * q + crow(r, h)) * rs] = st[q][r];
+}
+
+}  // namespace tile
+}  // namespace gdn
