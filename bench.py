@@ -1,27 +1,32 @@
 """Benchmark: GDN tree verify + commit on one MI355X.
 
-One step = gdn_tree_verify over a batch of draft trees followed by
-gdn_tree_commit of one accepted branch per sequence (the whole hot path).
-Workload: one GDN layer, batch 16, 32 heads, d_k = d_v = 128, 64-node trees
-grown by width-8 best-first expansion (depth <= 12), bf16 q/k/v, fp32 gates
-and state; seeded synthetic inputs (gdn_synth), no model weights.
+One step = the whole hot path for one batch of draft trees: the accepted
+branch of the previous step's trees is committed into the state and the new
+trees are verified from the committed state, in one gdn_tree_commit_verify
+launch (the commit is the one the verify method defers to the next
+iteration).  Workload: one GDN layer, batch 16, 32 heads, d_k = d_v = 128,
+64-node trees grown by width-8 best-first expansion (depth <= 12), bf16
+q/k/v, fp32 gates and state; seeded synthetic inputs (gdn_synth), no model
+weights.
 
 R independent input sets (default 16, ~1.2 GB in total) are resident in HBM
 before timing and are used round-robin, so the 256 MiB Infinity Cache cannot
-serve repeated reads; each commit advances its own set's state in place, the
-way a decoding loop would.
+serve repeated reads.  Step i works on set i mod R: its state is advanced
+along the accepted path of set i - 1's tree (whose k, v, gates and parents
+the commit reads), then set i's tree is verified.
 
 Timed regions (HIP events on the launch stream, start and end only, so no
-event fence sits between kernels): K whole steps (the headline value), then
-K back-to-back verify launches and K back-to-back commit launches over the
-same rotating sets (per-kernel means; they include the dispatch gap between
-consecutive kernels).
+event fence sits between kernels), K launches each: the fused step (the
+headline value), the same step as two launches (gdn_tree_verify then
+gdn_tree_commit), verify alone and commit alone.  Launches are prepared
+once (binding Launch objects), so the host enqueues faster than the GPU
+drains and the events time the GPU.
 
-Prints one JSON line.  `roofline` is for the verify kernel: algorithmic
-bytes per launch / its mean launch time.  `traffic` is read from the
-committed rocprofv3 counter summary when it was taken on the current kernel
-source, else null.  `cpu_baseline` times the fp64 oracle (test
-infrastructure) on the host cores on the same workload.
+Prints one JSON line.  `roofline` is for the fused kernel: algorithmic bytes
+per launch / its mean launch time.  `traffic` is read from the committed
+rocprofv3 counter summary when it was taken on the current kernel source,
+else null.  `cpu_baseline` times the fp64 oracle (test infrastructure) on
+the host cores on the same workload.
 """
 from __future__ import annotations
 
@@ -41,7 +46,9 @@ WORKLOAD_INDEX = 2
 # arithmetic of the verify path: bf16 operands feed the MFMA contractions with
 # fp32 accumulation; everything else is fp32
 KERNEL_DTYPE = "bf16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_b16_n64_h32_d128_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "commit_verify_b16_n64_h32_d128_traffic.txt")
+TRAFFIC_SOURCES = ("commit_verify_mfma.hip", "path_commit.hpp", "tree_verify.hpp",
+                   "mfma_tile.hpp", "device_common.hpp")
 
 
 def verify_bytes(batch, n, H, dk, dv, elem=2):
@@ -59,10 +66,18 @@ def commit_bytes(batch, H, dk, dv, path_lens, elem=2, max_path=None):
             + m * 4 + batch * 4)
 
 
+def fused_bytes(batch, n, H, dk, dv, path_lens):
+    """one commit + verify launch: the state read once and written once, the
+    new tree's q/k/v/gates/parents read once, out written once, the path
+    nodes' k/v/gates and the path read once"""
+    return (verify_bytes(batch, n, H, dk, dv) + commit_bytes(batch, H, dk, dv, path_lens)
+            - batch * H * 4 * dk * dv)
+
+
 def kernel_source_digest():
     p = os.path.join(ROOT, "gated_deltanet_tree_verify_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("verify_mfma.hip", "verify_generic.hip", "device_common.hpp"):
+    for f in TRAFFIC_SOURCES:
         with open(os.path.join(p, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -70,7 +85,7 @@ def kernel_source_digest():
 
 def read_traffic():
     """per-launch HBM bytes from the committed counter summary, or None when
-    the verify kernel source changed since the counters were taken"""
+    the fused kernel's source changed since the counters were taken"""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -168,46 +183,56 @@ def main():
                    if isinstance(t, torch.Tensor))
     log(f"generated {args.sets} sets ({resident / 2**30:.2f} GiB resident) in {time.time() - t0:.1f}s")
 
-    def step(d):
-        g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"], out=d["out"],
-                 stream=stream)
-        g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
-                 stream=stream)
+    R = len(sets)
+    fused, ver, com = [], [], []
+    for i, d in enumerate(sets):
+        p = sets[(i - 1) % R]
+        fused.append(g.commit_verify(d["S"], p["path"], p["plen"],
+                                     (p["k"], p["v"], p["alpha"], p["beta"], p["parent"]),
+                                     d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                                     out=d["out"], stream=stream, prepare=True))
+        ver.append(g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"],
+                            out=d["out"], stream=stream, prepare=True))
+        com.append(g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"],
+                            d["parent"], stream=stream, prepare=True))
 
     for i in range(args.warmup):
-        step(sets[i % len(sets)])
+        fused[i % R]()
     torch.cuda.synchronize()
 
     K = args.steps
+    host_s = {}
 
-    def timed(body):
+    def timed(name, body):
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
+        h0 = time.perf_counter()
         for i in range(K):
-            body(sets[i % len(sets)])
+            body(i % R)
+        host_s[name] = (time.perf_counter() - h0) / K
         end.record(stream)
         torch.cuda.synchronize()
         return start.elapsed_time(end) / K
 
-    def verify_only(d):
-        g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"], out=d["out"],
-                 stream=stream)
+    def separate(i):
+        ver[i]()
+        com[i]()
 
-    def commit_only(d):
-        g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
-                 stream=stream)
-
-    ms_step = timed(step)
-    ver_ms = timed(verify_only)
-    com_ms = timed(commit_only)
+    ms_step = timed("fused", lambda i: fused[i]())
+    sep_ms = timed("separate", separate)
+    ver_ms = timed("verify", lambda i: ver[i]())
+    com_ms = timed("commit", lambda i: com[i]())
+    log(f"fused {ms_step * 1e3:.2f} us, separate {sep_ms * 1e3:.2f} us, verify {ver_ms * 1e3:.2f} "
+        f"us, commit {com_ms * 1e3:.2f} us per launch (host enqueue "
+        f"{host_s['fused'] * 1e6:.1f} us per fused launch)")
     nodes = batch * n
-    vbytes = verify_bytes(batch, n, H, dk, dv)
     mean_plen = float(np.mean([float(np.sum(d["plen_host"])) for d in sets]))
+    vbytes = verify_bytes(batch, n, H, dk, dv)
     cbytes = commit_bytes(batch, H, dk, dv, [mean_plen])
-    v_mean_s = ver_ms * 1e-3
-    c_mean_s = com_ms * 1e-3
-    achieved = vbytes / v_mean_s / 1e9
+    fbytes = fused_bytes(batch, n, H, dk, dv, [mean_plen])
+    step_s = ms_step * 1e-3
+    achieved = fbytes / step_s / 1e9
     traffic = read_traffic()
 
     # achievable-bandwidth line: a plain 1 GiB device copy
@@ -225,7 +250,7 @@ def main():
 
     result = {
         "metric": METRIC,
-        "value": nodes / (ms_step * 1e-3),
+        "value": nodes / step_s,
         "unit": "nodes/s",
         "n_gpus": 1,
         "steps": K,
@@ -237,17 +262,20 @@ def main():
         "dtype": KERNEL_DTYPE,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": batch, "tree_nodes": n, "heads": H, "d_k": dk,
-                   "d_v": dv, "tree": "width-8 best-first, depth<=12", "rotating_sets": args.sets,
-                   "step": "verify + commit"},
+                   "d_v": dv, "tree": "width-8 best-first, depth<=12", "rotating_sets": R,
+                   "step": "commit previous accepted path + verify new trees (one launch)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "gdn_tree_verify", "algorithmic_bytes_per_launch": vbytes,
-                     "mean_launch_us": v_mean_s * 1e6},
-        "verify_us": v_mean_s * 1e6,
-        "commit_us": c_mean_s * 1e6,
-        "verify_nodes_per_s": nodes / v_mean_s,
-        "step_hbm_gbps": (vbytes + cbytes) / (ms_step * 1e-3) / 1e9,
-        "commit_hbm_gbps": cbytes / c_mean_s / 1e9,
+                     "kernel": "gdn_tree_commit_verify", "algorithmic_bytes_per_launch": fbytes,
+                     "mean_launch_us": step_s * 1e6},
+        "separate_step_us": sep_ms * 1e3,
+        "separate_step_nodes_per_s": nodes / (sep_ms * 1e-3),
+        "verify_us": ver_ms * 1e3,
+        "commit_us": com_ms * 1e3,
+        "verify_nodes_per_s": nodes / (ver_ms * 1e-3),
+        "verify_hbm_gbps": vbytes / (ver_ms * 1e-3) / 1e9,
+        "commit_hbm_gbps": cbytes / (com_ms * 1e-3) / 1e9,
+        "host_enqueue_us_per_step": host_s["fused"] * 1e6,
         "copy_gbps": copy_gbps,
     }
     if not args.no_cpu_baseline:

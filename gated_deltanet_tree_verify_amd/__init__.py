@@ -8,6 +8,8 @@ is no CPU or PyTorch fallback, and a missing library raises.
 
     verify(q, k, v, alpha, beta, parent, S0)        -> out   (gdn_tree_verify)
     commit(S, path, path_len, k, v, alpha, beta, parent)     (gdn_tree_commit, in place)
+    commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent)
+                                                    -> out   (gdn_tree_commit_verify)
     path(parent, accepted, max_path)                -> (path, path_len)
     index(parent)                                   -> (depth, anc)
 """
@@ -17,7 +19,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["load", "lib_path", "verify", "commit", "path", "index", "status_string",
+__all__ = ["load", "lib_path", "verify", "commit", "commit_verify", "path", "Launch", "index", "status_string",
            "GdnError", "FAULT_BAD_PARENT", "FAULT_BAD_PATH", "DTYPE_F32", "DTYPE_BF16",
            "MAX_NODES", "MAX_DIM", "build"]
 
@@ -68,6 +70,9 @@ def load() -> ctypes.CDLL:
         lib.gdn_tree_verify.restype = I
         lib.gdn_tree_commit.argtypes = [P, P, P, I, P, P, I, P, P, P, I, I, I, I, I, P, P]
         lib.gdn_tree_commit.restype = I
+        lib.gdn_tree_commit_verify.argtypes = [P, P, P, I, P, P, P, P, P, I, P, P, P, I, P, P, P,
+                                               P, I, I, I, I, I, P, P]
+        lib.gdn_tree_commit_verify.restype = I
         lib.gdn_tree_path.argtypes = [P, P, P, P, I, I, I, P, P]
         lib.gdn_tree_path.restype = I
         lib.gdn_tree_index.argtypes = [P, P, P, I, I, P, P]
@@ -110,6 +115,32 @@ def _check(fn, code):
         raise GdnError(fn, code, status_string(code))
 
 
+class Launch:
+    """One entry-point call with its arguments already checked and marshalled
+    (device pointers, sizes, stream).  Calling it re-issues the same launch
+    with no per-call checks, for launch loops where those checks would cost
+    more host time than the kernel takes on the GPU.  It keeps references to
+    its tensors; `result` is what the eager call returns."""
+
+    __slots__ = ("_fn", "_name", "_args", "_keep", "result")
+
+    def __init__(self, name, fn, args, keep, result):
+        self._name, self._fn, self._args, self._keep, self.result = name, fn, args, keep, result
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _check(self._name, rc)
+        return self.result
+
+
+def _issue(name, fn, args, keep, result, prepare):
+    if prepare:
+        return Launch(name, fn, args, keep, result)
+    _check(name, fn(*args))
+    return result
+
+
 def _need(t, name, dtypes, shape=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
@@ -132,8 +163,9 @@ def _qkv_dtype(q):
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
-def verify(q, k, v, alpha, beta, parent, S0, out=None, status=None, stream=None):
-    """gdn_tree_verify: fp32 out [batch][n][H][d_v]; S0 is never written."""
+def verify(q, k, v, alpha, beta, parent, S0, out=None, status=None, stream=None, prepare=False):
+    """gdn_tree_verify: fp32 out [batch][n][H][d_v]; S0 is never written.
+    prepare=True returns a Launch instead of launching."""
     torch = _torch()
     lib = load()
     qk = (torch.bfloat16, torch.float32)
@@ -153,15 +185,16 @@ def verify(q, k, v, alpha, beta, parent, S0, out=None, status=None, stream=None)
     _need(out, "out", (torch.float32,), (batch, n, H, dv))
     if status is not None:
         _need(status, "status", (torch.int32,), (batch,))
-    rc = lib.gdn_tree_verify(_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(alpha), _ptr(beta),
-                             _ptr(parent), _ptr(S0), _ptr(out), batch, n, H, dk, dv,
-                             _ptr(status), _stream(stream))
-    _check("gdn_tree_verify", rc)
-    return out
+    args = (_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(alpha), _ptr(beta), _ptr(parent),
+            _ptr(S0), _ptr(out), batch, n, H, dk, dv, _ptr(status), _stream(stream))
+    return _issue("gdn_tree_verify", lib.gdn_tree_verify, args,
+                  (q, k, v, alpha, beta, parent, S0, out, status), out, prepare)
 
 
-def commit(S, path, path_len, k, v, alpha, beta, parent, status=None, stream=None):
-    """gdn_tree_commit: advances S [batch][H][d_k][d_v] in place; returns S."""
+def commit(S, path, path_len, k, v, alpha, beta, parent, status=None, stream=None,
+           prepare=False):
+    """gdn_tree_commit: advances S [batch][H][d_k][d_v] in place; returns S.
+    prepare=True returns a Launch instead of launching."""
     torch = _torch()
     lib = load()
     _need(k, "k", (torch.bfloat16, torch.float32))
@@ -178,11 +211,61 @@ def commit(S, path, path_len, k, v, alpha, beta, parent, status=None, stream=Non
     _need(parent, "parent", (torch.int32,), (batch, n))
     if status is not None:
         _need(status, "status", (torch.int32,), (batch,))
-    rc = lib.gdn_tree_commit(_ptr(S), _ptr(path), _ptr(path_len), int(path.shape[1]), _ptr(k),
-                             _ptr(v), _qkv_dtype(k), _ptr(alpha), _ptr(beta), _ptr(parent),
-                             batch, n, H, dk, dv, _ptr(status), _stream(stream))
-    _check("gdn_tree_commit", rc)
-    return S
+    args = (_ptr(S), _ptr(path), _ptr(path_len), int(path.shape[1]), _ptr(k), _ptr(v),
+            _qkv_dtype(k), _ptr(alpha), _ptr(beta), _ptr(parent), batch, n, H, dk, dv,
+            _ptr(status), _stream(stream))
+    return _issue("gdn_tree_commit", lib.gdn_tree_commit, args,
+                  (S, path, path_len, k, v, alpha, beta, parent, status), S, prepare)
+
+
+def commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent, out=None,
+                  status=None, stream=None, prepare=False):
+    """gdn_tree_commit_verify: commit the previous tree's accepted path into S
+    (in place), then verify the new tree from the committed S.
+
+    prev = (k_prev, v_prev, alpha_prev, beta_prev, parent_prev): the tensors
+    of the tree the path was accepted from.  Returns out [batch][n][H][d_v]
+    (prepare=True: a Launch instead of launching).
+    """
+    torch = _torch()
+    lib = load()
+    k_prev, v_prev, alpha_prev, beta_prev, parent_prev = prev
+    qk = (torch.bfloat16, torch.float32)
+    _need(q, "q", qk)
+    batch, n, H, dk = q.shape
+    _need(k, "k", (q.dtype,), q.shape)
+    _need(v, "v", (q.dtype,))
+    if tuple(v.shape[:3]) != (batch, n, H):
+        raise ValueError("v must be [batch][n][H][d_v]")
+    dv = v.shape[3]
+    _need(alpha, "alpha", (torch.float32,), (batch, n, H))
+    _need(beta, "beta", (torch.float32,), (batch, n, H))
+    _need(parent, "parent", (torch.int32,), (batch, n))
+    _need(k_prev, "k_prev", (q.dtype,))
+    if k_prev.dim() != 4 or k_prev.shape[0] != batch or tuple(k_prev.shape[2:]) != (H, dk):
+        raise ValueError("k_prev must be [batch][n_prev][H][d_k]")
+    n_prev = k_prev.shape[1]
+    _need(v_prev, "v_prev", (q.dtype,), (batch, n_prev, H, dv))
+    _need(alpha_prev, "alpha_prev", (torch.float32,), (batch, n_prev, H))
+    _need(beta_prev, "beta_prev", (torch.float32,), (batch, n_prev, H))
+    _need(parent_prev, "parent_prev", (torch.int32,), (batch, n_prev))
+    _need(S, "S", (torch.float32,), (batch, H, dk, dv))
+    _need(path, "path", (torch.int32,))
+    if path.dim() != 2 or path.shape[0] != batch:
+        raise ValueError("path must be [batch][max_path]")
+    _need(path_len, "path_len", (torch.int32,), (batch,))
+    if out is None:
+        out = torch.empty((batch, n, H, dv), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), (batch, n, H, dv))
+    if status is not None:
+        _need(status, "status", (torch.int32,), (batch,))
+    args = (_ptr(S), _ptr(path), _ptr(path_len), int(path.shape[1]), _ptr(k_prev),
+            _ptr(v_prev), _ptr(alpha_prev), _ptr(beta_prev), _ptr(parent_prev), n_prev, _ptr(q),
+            _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(alpha), _ptr(beta), _ptr(parent), _ptr(out),
+            batch, n, H, dk, dv, _ptr(status), _stream(stream))
+    return _issue("gdn_tree_commit_verify", lib.gdn_tree_commit_verify, args,
+                  (S, path, path_len, *prev, q, k, v, alpha, beta, parent, out, status), out,
+                  prepare)
 
 
 def path(parent, accepted, max_path, out=None, path_len=None, status=None, stream=None):

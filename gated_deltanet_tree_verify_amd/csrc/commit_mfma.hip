@@ -40,9 +40,9 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     if (!sm.pi.ok || mlen == 0) return;
 
     // state slab: four result tiles of this lane's column
-    float *sp = S + (size_t)bh * kD * kD + col;
+    float *slab = S + (size_t)bh * kD * kD;
     f32x16 st[4];
-    load_state(st, sp, kD, h);
+    load_state(st, slab, col, h);
     bf16x8 ident[2];
     key_identity(ident, m, h);
     for (int c0 = 0; c0 < mlen; c0 += kC) {
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
         apply_chunk(sm.ct, st, ident, m, h, col);
         __syncthreads();   // the chunk tiles are restaged next
     }
-    store_state(st, sp, kD, h);
+    store_state(st, slab, col, h);
 }
 
 }  // namespace

@@ -18,6 +18,7 @@ struct VerifyArgs {
     float *out;
     int batch, n, H, dk, dv;
     int32_t *status;
+    bool status_or = false;   // OR the flags into status[b] instead of overwriting it
 };
 
 struct CommitArgs {
@@ -32,6 +33,13 @@ struct CommitArgs {
     int32_t *status;
 };
 
+// commit of a previous tree's path, then verify of the next tree from the
+// committed state (c.S is the verify's S0); both halves share batch, H, d
+struct CommitVerifyArgs {
+    CommitArgs c;
+    VerifyArgs v;
+};
+
 // number of compute units of the current device (cached per device); only
 // used to shape work placement, never for correctness
 int device_cu_count();
@@ -43,6 +51,8 @@ hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
 bool commit_mfma_supports(const CommitArgs &a);
 hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s);
+bool commit_verify_mfma_supports(const CommitVerifyArgs &a);
+hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s);
 hipError_t launch_path(const int32_t *parent, const int32_t *accepted,
                        int32_t *path, int32_t *path_len, int batch, int n,
                        int max_path, int32_t *status, hipStream_t s);

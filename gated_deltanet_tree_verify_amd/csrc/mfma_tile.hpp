@@ -121,20 +121,51 @@ __device__ __forceinline__ void store_row8_permuted(uint16_t *row, int c8, const
 }
 
 // The state slab of a wave: rows 0..127 of its 32 columns as four result
-// tiles, tile q holding rows 32 q + crow(r, h).  p points at row 0 of the
-// lane's column; rs is the row stride in elements.
-__device__ __forceinline__ void load_state(f32x16 (&st)[4], const float *p, int rs, int h) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[q][r] = p[(size_t)(32 * q + crow(r, h)) * rs];
+// tiles, tile q holding rows 32 q + crow(r, h).  The 128 x 128 fp32 state of
+// one (sequence, head) is addressed through a buffer resource: the lane's
+// column and half go into one 32-bit lane offset and every row offset is a
+// scalar constant, so the 64 loads or stores of a lane carry no per-element
+// address arithmetic and nothing address-like stays live between the load
+// and the store of the slab.  The resource's size bounds every access to
+// the 64 KiB of that state.  slab must be wave-uniform.  The b32 buffer
+// builtins move 32-bit integers: the floats pass through them as bit
+// patterns.
+constexpr int kStateDim = 128;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float *slab) {
+    // word 3 = 0x00020000: 32-bit data format, the gfx9 raw-buffer setting
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(slab), (short)0,
+                                             kStateDim * kStateDim * 4, 0x00020000);
 }
 
-__device__ __forceinline__ void store_state(const f32x16 (&st)[4], float *p, int rs, int h) {
+__device__ __forceinline__ int state_lane_offset(int col, int h) {
+    return 4 * (col + 4 * h * kStateDim);
+}
+
+__device__ __forceinline__ void load_state(f32x16 (&st)[4], const float *slab, int col, int h) {
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc(slab);
+    const int vo = state_lane_offset(col, h);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[(size_t)(32 * q + crow(r, h)) * rs] = st[q][r];
+        for (int r = 0; r < 16; ++r)
+            st[q][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rs, vo, 4 * kStateDim * (32 * q + crow(r, 0)), 0));
+}
+
+__device__ __forceinline__ void store_state(const f32x16 (&st)[4], float *slab, int col, int h) {
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc(slab);
+    const int vo = state_lane_offset(col, h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // through a scalar temporary: a bit cast applied to the vector
+            // element itself reads element 0 with this compiler
+            const float x = st[q][r];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, vo,
+                                                  4 * kStateDim * (32 * q + crow(r, 0)), 0);
+        }
 }
 
 }  // namespace tile

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void verify_generic_kernel(
     const float *__restrict__ alpha, const float *__restrict__ beta,
     const int32_t *__restrict__ parent, const float *__restrict__ S0,
     float *__restrict__ out, int n, int H, int dk, int dv,
-    int32_t *__restrict__ status) {
+    int32_t *__restrict__ status, bool status_or) {
     __shared__ int s_par[kMaxN], s_depth[kMaxN], s_off[kMaxN + 1];
     __shared__ float s_g[kMaxN], s_eg[kMaxN], s_beta[kMaxN];
     __shared__ float s_X[kMaxEntries], s_Y[kMaxEntries];
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void verify_generic_kernel(
         }
         s_off[n] = off;
         s_bad = bad;
-        if (writer && status) status[b] = bad ? kFaultBadParent : 0;
+        if (writer && status) status[b] = (status_or ? status[b] : 0) | (bad ? kFaultBadParent : 0);
     }
     __syncthreads();
     if (s_bad) {
@@ -152,11 +152,13 @@ hipError_t launch_verify_generic(const VerifyArgs &a, hipStream_t s) {
     if (a.dtype == GDN_DTYPE_BF16) {
         hipLaunchKernelGGL(verify_generic_kernel<uint16_t>, grid, dim3(kThreads), 0, s,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, a.dk, a.dv, a.status);
+                           a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, a.dk, a.dv, a.status,
+                           a.status_or);
     } else {
         hipLaunchKernelGGL(verify_generic_kernel<float>, grid, dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v,
-                           a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, a.dk, a.dv, a.status);
+                           a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, a.dk, a.dv, a.status,
+                           a.status_or);
     }
     return hipGetLastError();
 }

@@ -54,9 +54,9 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     __syncthreads();
 
     const bool state_first = ((blockIdx.x / ncu) & 1) == 0;
-    const float *sp = S0 + (size_t)blockIdx.x * kD * kD + c.col;
+    const float *slab = S0 + (size_t)blockIdx.x * kD * kD;
     f32x16 st[4];
-    if (state_first) load_state(st, sp, kD, c.h);
+    if (state_first) load_state(st, slab, c.col, c.h);
 
     // ---- 2. transposed Gram tiles (waves 0-2), V -> registers
     f32x16 gc, ga;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     inverse(c, sm.b.s);
 
     // ---- 5. P = Q S0, R = K S0
-    if (!state_first) load_state(st, sp, kD, c.h);
+    if (!state_first) load_state(st, slab, c.col, c.h);
     f32x16 P[2], R[2];
     contract(c, sm.a.t, st, P, R);
     __syncthreads();

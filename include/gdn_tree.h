@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 1
+#define GDN_TREE_ABI_VERSION 2
 #define GDN_MAX_NODES 128
 #define GDN_MAX_DIM 128
 
@@ -105,6 +105,40 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path,
                            const float *alpha, const float *beta,
                            const int32_t *parent, int batch, int n, int H,
                            int d_k, int d_v, int32_t *status, void *stream);
+
+/*
+ * Commit of the previous step's accepted branch fused with the verify of
+ * the next tree (the commitment is deferred to the next iteration in the
+ * section above, so the two meet in one call).  Same result as
+ *   gdn_tree_commit(S, path, path_len, max_path, k_prev, v_prev, qkv_dtype,
+ *                   alpha_prev, beta_prev, parent_prev, batch, n_prev, H,
+ *                   d_k, d_v, ...);
+ *   gdn_tree_verify(q, k, v, qkv_dtype, alpha, beta, parent, S, out, batch,
+ *                   n, H, d_k, d_v, ...);
+ * on the same stream: S is advanced in place along path (the previous tree,
+ * n_prev nodes, tensors k_prev, v_prev, alpha_prev, beta_prev, parent_prev
+ * in the layouts above with n_prev rows), then the tree (q, k, v, alpha,
+ * beta, parent, n nodes) is verified from the committed S, which the call
+ * reads from HBM once and writes once.  status[b] receives the OR of both
+ * halves' flags: GDN_FAULT_BAD_PATH leaves S[b] bit-unchanged and the
+ * verify runs from it; GDN_FAULT_BAD_PARENT (of the new tree) sets that
+ * element's out rows to NaN and does not undo its commit.  path_len[b] = 0
+ * commits nothing.  out must not alias any input, S must not alias any
+ * other argument; the previous-tree tensors may be the same tensors as the
+ * new ones.  1 <= n_prev <= GDN_MAX_NODES, 1 <= max_path.
+ */
+gdn_status gdn_tree_commit_verify(float *S, const int32_t *path,
+                                  const int32_t *path_len, int max_path,
+                                  const void *k_prev, const void *v_prev,
+                                  const float *alpha_prev,
+                                  const float *beta_prev,
+                                  const int32_t *parent_prev, int n_prev,
+                                  const void *q, const void *k, const void *v,
+                                  gdn_dtype qkv_dtype, const float *alpha,
+                                  const float *beta, const int32_t *parent,
+                                  float *out, int batch, int n, int H,
+                                  int d_k, int d_v, int32_t *status,
+                                  void *stream);
 
 /*
  * Accepted path: path[b][0..m) = root .. accepted[b] (root first), the rest

@@ -31,8 +31,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_path", "gdn_tree_index",
-            "gdn_status_string", "gdn_tree_abi_version"} <= set(names)
+    assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_commit_verify", "gdn_tree_path",
+            "gdn_tree_index", "gdn_status_string", "gdn_tree_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -81,6 +81,30 @@ def test_commit_rejects(lib):
     assert call(S=MISALIGNED) == -1
     assert call(dtype=3) == -1
     del ok
+
+
+def _commit_verify(lib, null=None, ptr=FAKE, max_path=4, n_prev=8, batch=1, n=8, H=1, dk=16,
+                   dv=16, dtype=1, status=None):
+    p = [ptr] * 15    # S path path_len k_prev v_prev a_prev b_prev par_prev q k v a b par out
+    if null is not None:
+        p[null] = None
+    return lib.gdn_tree_commit_verify(p[0], p[1], p[2], max_path, p[3], p[4], p[5], p[6], p[7],
+                                      n_prev, p[8], p[9], p[10], dtype, p[11], p[12], p[13],
+                                      p[14], batch, n, H, dk, dv, status, None)
+
+
+@pytest.mark.parametrize("null", range(15))
+def test_commit_verify_null_pointer(lib, null):
+    assert _commit_verify(lib, null=null) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(max_path=0), -1), (dict(n_prev=0), -1), (dict(n=0), -1), (dict(batch=0), -1),
+    (dict(n_prev=129), -2), (dict(n=129), -2), (dict(dk=12), -2), (dict(dv=256), -2),
+    (dict(dtype=2), -1), (dict(ptr=MISALIGNED), -1), (dict(status=MISALIGNED), -1),
+])
+def test_commit_verify_rejects(lib, kw, code):
+    assert _commit_verify(lib, **kw) == code
 
 
 def test_path_and_index_reject(lib):

@@ -280,6 +280,100 @@ def test_commit_empty_path_is_noop(gpu_lib):
 
 
 # ---------------------------------------------------------------------------
+# fused commit (previous tree's path) + verify (next tree)
+# ---------------------------------------------------------------------------
+def run_commit_verify(g, prev, cur, path, plen):
+    dp, dc = upload(prev), upload(cur)
+    S = dp["S0"].clone()
+    st = torch.full((cur.parent.shape[0],), -7, dtype=torch.int32, device="cuda")
+    out = g.commit_verify(S, dev(path), dev(plen),
+                          (dp["k"], dp["v"], dp["alpha"], dp["beta"], dp["parent"]),
+                          dc["q"], dc["k"], dc["v"], dc["alpha"], dc["beta"], dc["parent"],
+                          status=st)
+    torch.cuda.synchronize()
+    return host(out), host(S), host(st)
+
+
+def oracle_commit_verify(prev, cur, path, plen):
+    """the definition: commit along the previous tree's path, then verify the
+    next tree from the committed state"""
+    Sref, cst = oracle.commit_set(prev, path_arr=path, path_len=plen)
+    oref, vst = oracle.verify(cur.q, cur.k, cur.v, cur.alpha, cur.beta, cur.parent, Sref)
+    return oref, Sref, cst | vst
+
+
+def test_commit_verify_b16_n64_full(gpu_lib):
+    """the benchmarked step: two consecutive trees of the b16/n64 workload"""
+    say("commit-verify b16 n64")
+    prev, cur = gs.make_config(2, s=0), gs.make_config(2, s=1)
+    path, plen = prev.paths(max_path=13)
+    out, S, st = run_commit_verify(gpu_lib, prev, cur, path, plen)
+    oref, Sref, rst = oracle_commit_verify(prev, cur, path, plen)
+    assert st.tolist() == rst.tolist() == [0] * 16
+    eo, es = oracle.rel_err(out, oref), oracle.rel_err(S, Sref)
+    say("rel err out", eo, "S", es)
+    assert eo <= BF16_GATE and es <= BF16_GATE
+
+
+def test_commit_verify_matches_separate_calls(gpu_lib):
+    """same tensors for both trees; the fused call agrees with commit then
+    verify (the same stages, so to within rounding order) and with the oracle"""
+    ts = gs.make_config(1)
+    d = upload(ts)
+    path, plen = ts.paths(max_path=32)
+    out, S, st = run_commit_verify(gpu_lib, ts, ts, path, plen)
+    S2 = d["S0"].clone()
+    gpu_lib.commit(S2, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"])
+    o2 = gpu_lib.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], S2)
+    torch.cuda.synchronize()
+    assert st.tolist() == [0]
+    say("fused == separate:", np.array_equal(S, host(S2)), np.array_equal(out, host(o2)))
+    assert oracle.rel_err(S, host(S2)) <= 1e-6
+    assert oracle.rel_err(out, host(o2)) <= 1e-5
+    oref, Sref, _ = oracle_commit_verify(ts, ts, path, plen)
+    assert oracle.rel_err(out, oref) <= BF16_GATE
+
+
+@pytest.mark.parametrize("n_prev,n,dk,dv,dtype", [
+    (128, 64, 128, 128, "bf16"),    # fused kernel, four commit chunks
+    (20, 1, 128, 128, "bf16"),      # fused kernel, one-node tree
+    (64, 100, 128, 128, "bf16"),    # MFMA commit + generic verify
+    (8, 65, 128, 128, "bf16"),
+    (37, 37, 64, 64, "fp32"),       # generic commit + generic verify
+    (50, 30, 32, 48, "bf16"),
+])
+def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype):
+    """sequence 0 clean, 1 bad previous path, 2 bad new tree, 3 both, 4 empty path"""
+    say("commit-verify", n_prev, n, dk, dv, dtype)
+    rng = np.random.default_rng(n_prev * 7 + n)
+    pp = np.stack([gs.chain_tree(n_prev) if n_prev == 128 else
+                   gs.random_recursive_tree(rng, n_prev, max_depth=12) for _ in range(5)])
+    pc = np.stack([gs.random_recursive_tree(rng, n, max_depth=10) for _ in range(5)])
+    acc = np.array([gs.pick_leaf(rng, pp[i]) for i in range(5)], np.int32)
+    if n_prev == 128:
+        acc[:] = 127
+    prev = gs.make_set(pp, 2, dk, dv, dtype, seed=n_prev, accepted=acc)
+    cur = gs.make_set(pc, 2, dk, dv, dtype, seed=n_prev + 1)
+    path, plen = prev.paths(max_path=n_prev)
+    path[1, plen[1] - 1] = n_prev       # id out of range
+    path[3, 0] = n_prev + 3
+    plen[4] = 0
+    cur.parent[2, n - 1] = n - 1        # parent not before the node
+    cur.parent[3, 0] = -5
+    out, S, st = run_commit_verify(gpu_lib, prev, cur, path, plen)
+    oref, Sref, rst = oracle_commit_verify(prev, cur, path, plen)
+    assert st.tolist() == rst.tolist() == [0, 2, 1, 3, 0]
+    for b in (1, 3, 4):
+        assert np.array_equal(S[b], prev.S0[b]), b
+    assert np.isnan(out[2:4]).all()
+    g = gate(prev)
+    for b in (0, 2):
+        assert oracle.rel_err(S[b], Sref[b]) <= g, b
+    for b in (0, 1, 4):
+        assert oracle.rel_err(out[b], oref[b]) <= g, b
+
+
+# ---------------------------------------------------------------------------
 # integer work: bit-exact
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
