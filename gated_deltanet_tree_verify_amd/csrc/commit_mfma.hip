@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
             if (hd == 0 && status) status[b] = ok ? 0 : kFaultBadPath;
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (!sm.pi.ok || mlen == 0) return;
 
     // state slab: four result tiles of this lane's column
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     for (int c0 = 0; c0 < mlen; c0 += kC) {
         prepare_chunk(sm.ct, sm.pi.pid, c0, mlen, b, hd, n, H, k, v, alpha, beta, tid, w, l);
         apply_chunk(sm.ct, st, ident, m, h, col);
-        __syncthreads();   // the chunk tiles are restaged next
+        lds_barrier();   // the chunk tiles are restaged next
     }
     store_state(st, slab, col, h);
 }
@@ -56,7 +56,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
 }  // namespace
 
 bool commit_mfma_supports(const CommitArgs &a) {
-    return a.dtype == GDN_DTYPE_BF16 && a.dk == kD && a.dv == kD;
+    // byte extents of a head's rows must fit the 32-bit buffer ranges
+    return a.dtype == GDN_DTYPE_BF16 && a.dk == kD && a.dv == kD && a.H <= 4096;
 }
 
 hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s) {

@@ -11,9 +11,11 @@
 // state is issued before the verify's tree matrices are built, so it drains
 // while the workgroup computes.
 //
-// LDS (79 KB, two workgroups per CU): the Q/K tiles of the new tree are
-// staged during the commit; the commit's chunk tiles, the new V tile and
-// the solve blocks take turns in one region.
+// Load order: the state slab first (the commit needs it), then the path
+// rows, then the new tree's Q/K while the first path chunk is prepared, then
+// V while the committed state is written back.  LDS (79 KB, two workgroups
+// per CU): the Q/K tiles are staged during the commit; the commit's chunk
+// tiles, the new V tile and the solve blocks take turns in one region.
 #include "internal.hpp"
 #include "path_commit.hpp"
 #include "tree_verify.hpp"
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     const int mlen = path_len[s.b];
     float *slab = S + (size_t)blockIdx.x * kD * kD;
 
-    // ---- 1. previous path (wave 1), state slab, new tree gates and Q/K
+    // ---- 1. previous path (wave 1), state slab, new tree gates
     f32x16 st[4];
     if (c.w == 1) {
         const bool ok = pc::validate_and_keep(sm.b.cp.pi, parent_prev + (size_t)s.b * n_prev,
@@ -67,28 +69,43 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     }
     load_state(st, slab, c.col, c.h);
     const Gates gt = load_gates(c, s, parent, alpha, beta);
-    uint4 rq[4], rk[4];
-    load_rows(c, s, q, rq);
-    load_rows(c, s, k, rk);
     if (c.w == 3) topology(c, s, gt, sm.tp, status, false);
-    store_rows_permuted(c, rq, sm.a.t.q);
-    store_rows_permuted(c, rk, sm.a.t.k);
-    __syncthreads();
+    lds_barrier();
     const bool commit_ok = sm.commit_ok;
     if (c.tid == 0 && s.hd == 0 && status)
         status[s.b] = (commit_ok ? 0 : kFaultBadPath) | (sm.tp.bad ? kFaultBadParent : 0);
 
-    // ---- 2. commit along the previous path, chunk by chunk, in registers
+    // ---- 2. commit along the previous path, chunk by chunk, in registers.
+    //         The new tree's Q/K rows are requested right after the first
+    //         chunk's rows, so they arrive while the chunk is prepared.
     const bool commit = commit_ok && mlen > 0;
     if (commit) {
         bf16x8 ident[2];
         pc::key_identity(ident, c.m, c.h);
-        for (int c0 = 0; c0 < mlen; c0 += pc::kC) {
+        {
+            const pc::ChunkRows cr = pc::load_chunk(sm.b.cp.pi.pid, 0, mlen, s.b, s.hd, n_prev, H,
+                                                    k_prev, v_prev, alpha_prev, beta_prev, c.tid);
+            uint4 rq[4], rk[4];
+            load_rows(c, s, q, rq);
+            load_rows(c, s, k, rk);
+            pc::build_chunk(sm.b.cp.ct, cr, 0, mlen, c.tid, c.w, c.l);
+            store_rows_permuted(c, rq, sm.a.t.q);
+            store_rows_permuted(c, rk, sm.a.t.k);
+            pc::apply_chunk(sm.b.cp.ct, st, ident, c.m, c.h, c.col);
+            lds_barrier();   // the chunk tiles are restaged (or become the V tile)
+        }
+        for (int c0 = pc::kC; c0 < mlen; c0 += pc::kC) {
             pc::prepare_chunk(sm.b.cp.ct, sm.b.cp.pi.pid, c0, mlen, s.b, s.hd, n_prev, H, k_prev,
                               v_prev, alpha_prev, beta_prev, c.tid, c.w, c.l);
             pc::apply_chunk(sm.b.cp.ct, st, ident, c.m, c.h, c.col);
-            __syncthreads();   // the chunk tiles are restaged (or become the V tile)
+            lds_barrier();
         }
+    } else {
+        uint4 rq[4], rk[4];
+        load_rows(c, s, q, rq);
+        load_rows(c, s, k, rk);
+        store_rows_permuted(c, rq, sm.a.t.q);
+        store_rows_permuted(c, rk, sm.a.t.k);
     }
 
     // ---- 3. new V rows in flight while the committed state is written back
@@ -96,24 +113,24 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     load_rows(c, s, v, rv);
     if (commit) store_state(st, slab, c.col, c.h);
     store_rows(c, rv, sm.b.v);
-    __syncthreads();
+    lds_barrier();
 
     // ---- 4. verify the new tree from the committed state (held in st)
     f32x16 gc, ga;
     if (c.w < 3) gram(c, sm.a.t, gc, ga);
     uint32_t vpk[2][8];
     v_to_regs(c, sm.b.v, vpk);
-    __syncthreads();
+    lds_barrier();
     if (sm.tp.bad) {
         store_nan(c, s, out);
         return;
     }
     if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
-    __syncthreads();
+    lds_barrier();
     inverse(c, sm.b.s);
     f32x16 P[2], R[2];
     contract(c, sm.a.t, st, P, R);
-    __syncthreads();
+    lds_barrier();
     f32x16 o0, o1;
     solve_output(c, sm.tp, sm.b.s, P, R, vpk, o0, o1);
     store_output(c, s, sm.a.o, o0, o1, out);
@@ -122,7 +139,9 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
 }  // namespace
 
 bool commit_verify_mfma_supports(const CommitVerifyArgs &a) {
-    return a.c.dtype == GDN_DTYPE_BF16 && a.c.dk == kD && a.c.dv == kD && a.v.n <= kN;
+    // byte extents of a head's rows must fit the 32-bit buffer ranges
+    return a.c.dtype == GDN_DTYPE_BF16 && a.c.dk == kD && a.c.dv == kD && a.v.n <= kN &&
+           a.v.H <= 4096;
 }
 
 hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s) {

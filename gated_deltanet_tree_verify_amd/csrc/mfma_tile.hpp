@@ -33,6 +33,17 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier that orders LDS only.  Every exchange between threads in
+// these kernels goes through LDS, so the barrier need not wait for the
+// wave's outstanding global loads (a full __syncthreads() waits for all of
+// them, which would stall each barrier behind whatever prefetch is in
+// flight).  A global load is still waited for where its value is used.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // row of a 32x32 result tile held by lane half h in register r
 __device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -120,6 +131,20 @@ __device__ __forceinline__ void store_row8_permuted(uint16_t *row, int c8, const
     *reinterpret_cast<uint2 *>(&row[perm(c8 + 4)]) = make_uint2(x.z, x.w);
 }
 
+// Raw buffer resource over `bytes` bytes from base (wave-uniform).  A load
+// whose offset lies past the end returns zero: rows beyond a tree's n, or
+// path slots beyond a path's end, read as zero with no branch around the
+// load, which keeps the memory-counter waits in front of each use exact.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    // word 3 = 0x00020000: 32-bit data format, the gfx9 raw-buffer setting
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // The state slab of a wave: rows 0..127 of its 32 columns as four result
 // tiles, tile q holding rows 32 q + crow(r, h).  The 128 x 128 fp32 state of
 // one (sequence, head) is addressed through a buffer resource: the lane's
@@ -133,9 +158,7 @@ __device__ __forceinline__ void store_row8_permuted(uint16_t *row, int c8, const
 constexpr int kStateDim = 128;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float *slab) {
-    // word 3 = 0x00020000: 32-bit data format, the gfx9 raw-buffer setting
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(slab), (short)0,
-                                             kStateDim * kStateDim * 4, 0x00020000);
+    return make_rsrc(slab, kStateDim * kStateDim * 4);
 }
 
 __device__ __forceinline__ int state_lane_offset(int col, int h) {

@@ -79,34 +79,56 @@ __device__ __forceinline__ bool validate_and_keep(PathIds &pi, const int32_t *pa
     return ok;
 }
 
-// Gates, rows, Gram, T = (I + X)^{-1} for the chunk starting at path slot c0.
-// Every thread of the workgroup calls this (it contains barriers).
-__device__ __forceinline__ void prepare_chunk(ChunkTiles &sm, const int *pid, int c0, int mlen,
-                                              int b, int hd, int n, int H, const uint16_t *__restrict__ k,
-                                              const uint16_t *__restrict__ v,
-                                              const float *__restrict__ alpha,
-                                              const float *__restrict__ beta, int tid, int w,
-                                              int l) {
-    const int m = l & 31, h = l >> 5;
+// Gates and key / value rows of the chunk starting at path slot c0, in
+// registers (one round of loads; threads < 32 also take a gate pair).
+struct ChunkRows {
+    uint4 kr[2], vr[2];
+    float la, bt;
+};
+
+__device__ __forceinline__ ChunkRows load_chunk(const int *pid, int c0, int mlen, int b, int hd,
+                                                int n, int H, const uint16_t *__restrict__ k,
+                                                const uint16_t *__restrict__ v,
+                                                const float *__restrict__ alpha,
+                                                const float *__restrict__ beta, int tid) {
     const int mc = min(kC, mlen - c0);
-    // gates (threads < 32) and key / value rows (all threads): one round of loads
-    float la = 0.f, bt = 0.f;
-    if (tid < kC && tid < mc) {
-        const size_t row = ((size_t)b * n + pid[c0 + tid]) * H + hd;
-        la = log2f(alpha[row]);
-        bt = beta[row];
-    }
+    ChunkRows r;
+    // every thread reads the gates of a valid path node (slots past the
+    // chunk repeat its last node and are zeroed), so no load sits in a branch
+    const int jg = min(tid & (kC - 1), mc - 1);
+    const size_t grow = ((size_t)b * n + pid[c0 + jg]) * H + hd;
+    const float a = alpha[grow], be = beta[grow];
+    const bool live = tid < mc;
+    r.la = live ? log2f(a) : 0.f;
+    r.bt = live ? be : 0.f;
+    // key / value rows through buffer resources over this head's n rows;
+    // slots past the chunk get an offset past the end and read as zero
+    const size_t base = ((size_t)b * n * H + hd) * kD;
+    const uint32_t bytes = (uint32_t)(n * H * kD * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + base, bytes), vr = make_rsrc(v + base, bytes);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int e = tid + kThreads * it, j = e >> 4, c8 = (e & 15) * 8;
-        uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-        if (j < mc) {
-            const size_t off = (((size_t)b * n + pid[c0 + j]) * H + hd) * kD + c8;
-            kr = *reinterpret_cast<const uint4 *>(k + off);
-            vr = *reinterpret_cast<const uint4 *>(v + off);
-        }
-        *reinterpret_cast<uint4 *>(&sm.vp[j][c8]) = vr;
-        store_row8_permuted(sm.kp[j], c8, kr);
+        const uint32_t off =
+            j < mc ? (uint32_t)(((size_t)pid[c0 + j] * H * kD + c8) * 2) : bytes;
+        r.kr[it] = load16(kr, off);
+        r.vr[it] = load16(vr, off);
+    }
+    return r;
+}
+
+// Rows into LDS, decay prefix, Gram, T = (I + X)^{-1} for the chunk.  Every
+// thread of the workgroup calls this (it contains barriers).
+__device__ __forceinline__ void build_chunk(ChunkTiles &sm, const ChunkRows &cr, int c0, int mlen,
+                                            int tid, int w, int l) {
+    const int m = l & 31, h = l >> 5;
+    const int mc = min(kC, mlen - c0);
+    const float la = cr.la, bt = cr.bt;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int e = tid + kThreads * it, j = e >> 4, c8 = (e & 15) * 8;
+        *reinterpret_cast<uint4 *>(&sm.vp[j][c8]) = cr.vr[it];
+        store_row8_permuted(sm.kp[j], c8, cr.kr[it]);
     }
     if (tid < kC) {
         // inclusive prefix of the log2 decays over the chunk (32 lanes)
@@ -124,7 +146,7 @@ __device__ __forceinline__ void prepare_chunk(ChunkTiles &sm, const int *pid, in
         sm.beta[j] = bt;
         if (j == 0) sm.glast = exp2f(gl);
     }
-    __syncthreads();
+    lds_barrier();
 
     // chunk Gram (wave 0, transposed tile): lane (j, h) holds k_t.k_j for
     // t = crow(r, h); X_jt = beta_j e^{g_j - g_t} k_j.k_t for t < j into d[j][t]
@@ -153,7 +175,7 @@ __device__ __forceinline__ void prepare_chunk(ChunkTiles &sm, const int *pid, in
             *reinterpret_cast<float4 *>(&sm.d[j][8 * q4 + 4 * h]) =
                 make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // T = (I + X)^{-1}: 16x16 diagonal inverses by forward substitution
     // (32 lanes: sub-block, column), then Z = B A^{-1} and L = -C^{-1} Z
@@ -176,23 +198,28 @@ __device__ __forceinline__ void prepare_chunk(ChunkTiles &sm, const int *pid, in
 #pragma unroll
         for (int r = 0; r < 16; ++r) sm.tinv[sbk][r][c] = t[r];
     }
-    __syncthreads();
-    {   // Z = B A^{-1} over the upper-left sub-block (read only by the substitution)
-        const int r = tid >> 4, c = tid & 15;
-        float acc = 0.f;
+    lds_barrier();
+    // rows past the chunk length are zero, so for mc <= 16 the lower block
+    // of T is [0, I]: its coupling L is zero and the two passes are skipped
+    const bool two_blocks = mc > 16;
+    if (two_blocks) {
+        {   // Z = B A^{-1} over the upper-left sub-block (read only by the substitution)
+            const int r = tid >> 4, c = tid & 15;
+            float acc = 0.f;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) acc = fmaf(sm.d[16 + r][s], sm.tinv[0][s][c], acc);
-        sm.d[r][c] = acc;
-    }
-    __syncthreads();
-    {   // L = -C^{-1} Z over the lower-left sub-block (B is no longer read)
-        const int r = tid >> 4, c = tid & 15;
-        float acc = 0.f;
+            for (int s2 = 0; s2 < 16; ++s2) acc = fmaf(sm.d[16 + r][s2], sm.tinv[0][s2][c], acc);
+            sm.d[r][c] = acc;
+        }
+        lds_barrier();
+        {   // L = -C^{-1} Z over the lower-left sub-block (B is no longer read)
+            const int r = tid >> 4, c = tid & 15;
+            float acc = 0.f;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) acc = fmaf(sm.tinv[1][r][s], sm.d[s][c], acc);
-        sm.d[16 + r][c] = -acc;
+            for (int s2 = 0; s2 < 16; ++s2) acc = fmaf(sm.tinv[1][r][s2], sm.d[s2][c], acc);
+            sm.d[16 + r][c] = -acc;
+        }
+        lds_barrier();
     }
-    __syncthreads();
     if (tid < 4 * kC) {
         // T = [[A^-1, 0], [L, C^-1]] as bf16 hi/lo operand rows, one 8-entry
         // chunk per thread (permuted positions 8 seg .. 8 seg + 7)
@@ -209,9 +236,11 @@ __device__ __forceinline__ void prepare_chunk(ChunkTiles &sm, const int *pid, in
         } else if (kb == 1) {
             lo4 = *reinterpret_cast<const float4 *>(&sm.tinv[1][r - 16][c0c - 16]);
             hi4 = *reinterpret_cast<const float4 *>(&sm.tinv[1][r - 16][c0c - 8]);
-        } else {
+        } else if (two_blocks) {
             lo4 = *reinterpret_cast<const float4 *>(&sm.d[r][c0c]);
             hi4 = *reinterpret_cast<const float4 *>(&sm.d[r][c0c + 8]);
+        } else {
+            lo4 = hi4 = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         const float vals[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
         bf16x8 th8, tl8;
@@ -219,7 +248,19 @@ __device__ __forceinline__ void prepare_chunk(ChunkTiles &sm, const int *pid, in
         *reinterpret_cast<bf16x8 *>(&sm.th[r][8 * seg]) = th8;
         *reinterpret_cast<bf16x8 *>(&sm.tl[r][8 * seg]) = tl8;
     }
-    __syncthreads();
+    lds_barrier();
+}
+
+// load_chunk then build_chunk
+__device__ __forceinline__ void prepare_chunk(ChunkTiles &sm, const int *pid, int c0, int mlen,
+                                              int b, int hd, int n, int H,
+                                              const uint16_t *__restrict__ k,
+                                              const uint16_t *__restrict__ v,
+                                              const float *__restrict__ alpha,
+                                              const float *__restrict__ beta, int tid, int w,
+                                              int l) {
+    build_chunk(sm, load_chunk(pid, c0, mlen, b, hd, n, H, k, v, alpha, beta, tid), c0, mlen, tid,
+                w, l);
 }
 
 // identity operands that move a path-key tile into the result layout:

@@ -141,14 +141,15 @@ __device__ __forceinline__ void topology(const Lane &c, const Seq &s, const Gate
 }
 
 // 64 node rows of one (sequence, head) of a bf16 [batch][n][H][128] tensor:
-// four 16-byte chunks per thread (rows past n read as zero)
+// four 16-byte chunks per thread; rows past n lie past the end of the buffer
+// resource and read as zero
 __device__ __forceinline__ void load_rows(const Lane &c, const Seq &s, const uint16_t *src,
                                           uint4 (&x)[4]) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + s.base, (uint32_t)(s.n * s.rstride * 2));
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
-        x[it] = row < s.n ? *reinterpret_cast<const uint4 *>(src + s.base + row * s.rstride + c8)
-                          : make_uint4(0, 0, 0, 0);
+        x[it] = load16(rs, (uint32_t)((row * s.rstride + c8) * 2));
     }
 }
 
@@ -277,7 +278,7 @@ __device__ __forceinline__ void inverse(const Lane &c, SolveBlocks &sb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sb.tinv[sbk][r][col] = t[r];
     }
-    __syncthreads();
+    lds_barrier();
     // Z_b into the upper-left sub-block of d[b] (read only by the substitution)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -287,7 +288,7 @@ __device__ __forceinline__ void inverse(const Lane &c, SolveBlocks &sb) {
         for (int s = 0; s < 16; ++s) acc = fmaf(sb.d[blk][16 + r][s], sb.tinv[2 * blk][s][col], acc);
         sb.d[blk][r][col] = acc;
     }
-    __syncthreads();
+    lds_barrier();
     // L_b into the lower-left sub-block (B_b is no longer read)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -297,7 +298,7 @@ __device__ __forceinline__ void inverse(const Lane &c, SolveBlocks &sb) {
         for (int s = 0; s < 16; ++s) acc = fmaf(sb.tinv[2 * blk + 1][r][s], sb.d[blk][s][col], acc);
         sb.d[blk][16 + r][col] = -acc;
     }
-    __syncthreads();
+    lds_barrier();
     {
         // one 8-entry chunk per thread: permuted positions 8 seg .. 8 seg + 7,
         // i.e. columns 16 kb + 4 hb + {0..3} and 16 kb + 8 + 4 hb + {0..3}
@@ -396,7 +397,7 @@ __device__ __forceinline__ void store_output(const Lane &c, const Seq &s, float 
         ostage[crow(r, c.h)][c.col] = o0[r];
         ostage[32 + crow(r, c.h)][c.col] = o1[r];
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int e = c.tid + kThreads * it, row = e >> 5, c4 = (e & 31) * 4;

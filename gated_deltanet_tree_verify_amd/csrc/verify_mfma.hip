@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     store_rows_permuted(c, rq, sm.a.t.q);
     store_rows_permuted(c, rk, sm.a.t.k);
     store_rows(c, rv, sm.b.v);
-    __syncthreads();
+    lds_barrier();
 
     const bool state_first = ((blockIdx.x / ncu) & 1) == 0;
     const float *slab = S0 + (size_t)blockIdx.x * kD * kD;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     if (c.w < 3) gram(c, sm.a.t, gc, ga);
     uint32_t vpk[2][8];
     v_to_regs(c, sm.b.v, vpk);
-    __syncthreads();
+    lds_barrier();
     if (sm.tp.bad) {
         store_nan(c, s, out);
         return;
@@ -71,14 +71,14 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
 
     // ---- 3. X and Y blocks, 4. block inverses
     if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
-    __syncthreads();
+    lds_barrier();
     inverse(c, sm.b.s);
 
     // ---- 5. P = Q S0, R = K S0
     if (!state_first) load_state(st, slab, c.col, c.h);
     f32x16 P[2], R[2];
     contract(c, sm.a.t, st, P, R);
-    __syncthreads();
+    lds_barrier();
 
     // ---- 6. solve and output, 7. whole-row stores
     f32x16 o0, o1;
@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
 }  // namespace
 
 bool verify_mfma_supports(const VerifyArgs &a) {
-    return a.dtype == GDN_DTYPE_BF16 && a.dk == kD && a.dv == kD && a.n <= kN;
+    // byte extents of a head's rows must fit the 32-bit buffer ranges
+    return a.dtype == GDN_DTYPE_BF16 && a.dk == kD && a.dv == kD && a.n <= kN && a.H <= 4096;
 }
 
 hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s) {
