@@ -7,15 +7,24 @@
 // state slab of each wave (128 x 32 fp32, four result tiles) is read from
 // HBM once, committed in registers (path_commit.hpp), written back once, and
 // is then the B operand of Q S and K S for the verify (tree_verify.hpp)
-// without another trip through memory.  The write-back of the committed
-// state is issued before the verify's tree matrices are built, so it drains
-// while the workgroup computes.
+// without another trip through memory.
 //
-// Load order: the state slab first (the commit needs it), then the path
-// rows, then the new tree's Q/K while the first path chunk is prepared, then
-// V while the committed state is written back.  LDS (79 KB, two workgroups
-// per CU): the Q/K tiles are staged during the commit; the commit's chunk
-// tiles, the new V tile and the solve blocks take turns in one region.
+// Schedule.  The only verify work that needs the state is Q S, K S and what
+// follows; the Gram matrices, masks and block inverses of the new tree need
+// only q/k/v and the parents.  So every wave requests its q/k/v rows first
+// and its state slab right behind them; the tree matrices are built while
+// the state streams in.  Wave 3 also reads the previous path (ids, then the
+// parents that validate it and the first 16 path nodes' rows and gates) and
+// keeps the path rows in registers until the inverse's scratch is free; it
+// then prepares the commit chunk on its own (16-slot chunk tiles overlay
+// that scratch), every wave applies it to its slab, and the verify finishes
+// from the committed slab.  Longer paths continue chunk by chunk.
+//
+// LDS (80 KB, two workgroups per CU): Q/K tiles (later the output staging),
+// one region for the V tile, then the solve blocks, whose inverse scratch
+// later holds the commit chunk, and the topology / chunk gate arrays.
+#include <stddef.h>
+
 #include "internal.hpp"
 #include "path_commit.hpp"
 #include "tree_verify.hpp"
@@ -25,10 +34,7 @@ namespace {
 
 using namespace tv;
 
-struct CommitPart {
-    pc::ChunkTiles ct;
-    pc::PathIds pi;
-};
+constexpr int kMaxPathIds = 128;   // a valid path has at most n_prev <= 128 nodes
 
 struct Smem {
     union {
@@ -36,13 +42,51 @@ struct Smem {
         float o[kN][kD + 4];
     } a;
     union {
-        CommitPart cp;
         uint16_t v[kN][kQK];
         SolveBlocks s;
+        pc::Chunk16 ch;   // over d / tinv, dead once the inverse has finished
     } b;
     Topo tp;
+    pc::Chunk16Aux cx;
     int commit_ok;
 };
+
+static_assert(sizeof(pc::Chunk16) <= offsetof(SolveBlocks, th),
+              "the commit chunk must fit in the inverse scratch of the solve blocks");
+static_assert(sizeof(Smem) <= 81920, "two workgroups per CU");
+
+// Previous path as seen by wave 3: lane l holds the ids of slots l and
+// 64 + l (-1 past the path) and, after the second round of loads, the
+// parents that validate them.
+struct PathLanes {
+    int id0, id1;
+    int par0, par1;
+};
+
+// node id of path slot j (j < 128)
+__device__ __forceinline__ int slot_id(const PathLanes &p, int j) {
+    const int a = __shfl(p.id0, j & 63), b = __shfl(p.id1, j & 63);
+    return j < 64 ? a : b;
+}
+
+// a path is valid when 0 <= m <= max_path, its ids lie in [0, n_prev) and
+// increase, the first is a root and each later id's parent is the previous id
+__device__ __forceinline__ bool path_valid(const PathLanes &p, int m, int max_path, int n_prev,
+                                           int l) {
+    if (m < 0 || m > max_path || m > kMaxPathIds) return false;
+    const int last0 = __shfl(p.id0, 63);
+    bool bad = false;
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd) {
+        const int j = 64 * rnd + l;
+        const int id = rnd == 0 ? p.id0 : p.id1;
+        const int par = rnd == 0 ? p.par0 : p.par1;
+        int prev = __shfl(id, (l + 63) & 63);
+        if (l == 0) prev = rnd == 0 ? -1 : last0;
+        if (j < m && (id < 0 || id >= n_prev || (j > 0 && prev >= id) || par != prev)) bad = true;
+    }
+    return __ballot(bad) == 0ull;
+}
 
 __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     float *__restrict__ S, const int32_t *__restrict__ path, const int32_t *__restrict__ path_len,
@@ -51,85 +95,123 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     const int32_t *__restrict__ parent_prev, int n_prev, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta,
-    const int32_t *__restrict__ parent, float *__restrict__ out, int n, int H,
+    const int32_t *__restrict__ parent, float *__restrict__ out, int n, int H, int ncu,
     int32_t *__restrict__ status) {
     __shared__ Smem sm;
     const Lane c = lane_coords();
     const Seq s = seq_coords(blockIdx.x, n, H);
     const int mlen = path_len[s.b];
     float *slab = S + (size_t)blockIdx.x * kD * kD;
+    // previous tree, this (sequence, head): node 0's row and gate entry
+    const size_t prow0 = ((size_t)s.b * n_prev * H + s.hd) * kD;
+    const size_t pgate0 = (size_t)s.b * n_prev * H + s.hd;
+    const uint32_t pbytes = (uint32_t)((size_t)n_prev * H * kD * 2);
+    const int32_t *ppar = parent_prev + (size_t)s.b * n_prev;
 
-    // ---- 1. previous path (wave 1), state slab, new tree gates
-    f32x16 st[4];
-    if (c.w == 1) {
-        const bool ok = pc::validate_and_keep(sm.b.cp.pi, parent_prev + (size_t)s.b * n_prev,
-                                              path + (size_t)s.b * max_path, mlen, max_path,
-                                              n_prev, c.l);
-        if (c.l == 0) sm.commit_ok = ok;
+    // ---- 1. loads: wave 3 first takes the new tree's gates and the path
+    //         ids, every wave its q/k/v rows, then its state slab; wave 3
+    //         requests the path parents and first chunk rows in between
+    Gates gt{-1, 1.f, 0.f, false};
+    PathLanes pl{-1, -1, -2, -2};
+    if (c.w == 3) {
+        gt = load_gates(c, s, parent, alpha, beta);
+        const int32_t *prow = path + (size_t)s.b * max_path;
+        const int lim = min(min(mlen, max_path), kMaxPathIds);
+        if (c.l < lim) pl.id0 = prow[c.l];
+        if (64 + c.l < lim) pl.id1 = prow[64 + c.l];
     }
-    load_state(st, slab, c.col, c.h);
-    const Gates gt = load_gates(c, s, parent, alpha, beta);
-    if (c.w == 3) topology(c, s, gt, sm.tp, status, false);
-    lds_barrier();
-    const bool commit_ok = sm.commit_ok;
-    if (c.tid == 0 && s.hd == 0 && status)
-        status[s.b] = (commit_ok ? 0 : kFaultBadPath) | (sm.tp.bad ? kFaultBadParent : 0);
-
-    // ---- 2. commit along the previous path, chunk by chunk, in registers.
-    //         The new tree's Q/K rows are requested right after the first
-    //         chunk's rows, so they arrive while the chunk is prepared.
-    const bool commit = commit_ok && mlen > 0;
-    if (commit) {
-        bf16x8 ident[2];
-        pc::key_identity(ident, c.m, c.h);
-        {
-            const pc::ChunkRows cr = pc::load_chunk(sm.b.cp.pi.pid, 0, mlen, s.b, s.hd, n_prev, H,
-                                                    k_prev, v_prev, alpha_prev, beta_prev, c.tid);
-            uint4 rq[4], rk[4];
-            load_rows(c, s, q, rq);
-            load_rows(c, s, k, rk);
-            pc::build_chunk(sm.b.cp.ct, cr, 0, mlen, c.tid, c.w, c.l);
-            store_rows_permuted(c, rq, sm.a.t.q);
-            store_rows_permuted(c, rk, sm.a.t.k);
-            pc::apply_chunk(sm.b.cp.ct, st, ident, c.m, c.h, c.col);
-            lds_barrier();   // the chunk tiles are restaged (or become the V tile)
-        }
-        for (int c0 = pc::kC; c0 < mlen; c0 += pc::kC) {
-            pc::prepare_chunk(sm.b.cp.ct, sm.b.cp.pi.pid, c0, mlen, s.b, s.hd, n_prev, H, k_prev,
-                              v_prev, alpha_prev, beta_prev, c.tid, c.w, c.l);
-            pc::apply_chunk(sm.b.cp.ct, st, ident, c.m, c.h, c.col);
-            lds_barrier();
-        }
-    } else {
-        uint4 rq[4], rk[4];
-        load_rows(c, s, q, rq);
-        load_rows(c, s, k, rk);
-        store_rows_permuted(c, rq, sm.a.t.q);
-        store_rows_permuted(c, rk, sm.a.t.k);
-    }
-
-    // ---- 3. new V rows in flight while the committed state is written back
-    uint4 rv[4];
+    uint4 rq[4], rk[4], rv[4];
+    load_rows(c, s, q, rq);
+    load_rows(c, s, k, rk);
     load_rows(c, s, v, rv);
-    if (commit) store_state(st, slab, c.col, c.h);
+    // the state slab is requested one 32-row tile at a time, between the
+    // tree-matrix phases: a wave that issues a whole 64 KiB slab stalls
+    // until the memory system has accepted all of it
+    f32x16 st[4];
+    pc::Rows16 r16;
+    if (c.w == 3) {
+        // parents of the path ids (ids out of range fail validation by
+        // themselves) and the first chunk's rows and gates
+        if (pl.id0 >= 0 && pl.id0 < n_prev) pl.par0 = ppar[pl.id0];
+        if (pl.id1 >= 0 && pl.id1 < n_prev) pl.par1 = ppar[pl.id1];
+        const int mc0 = min(pc::kC16, mlen);
+        const int rj = c.l >> 2;
+        const int rid = slot_id(pl, rj);
+        r16 = pc::load_rows16(rid, rj < mc0 && rid >= 0 && rid < n_prev, pl.id0,
+                              c.l < mc0 && pl.id0 >= 0 && pl.id0 < n_prev, k_prev + prow0,
+                              v_prev + prow0, alpha_prev + pgate0, beta_prev + pgate0, H * kD, H,
+                              pbytes, c.l);
+        topology(c, s, gt, sm.tp, status, false);
+        // zero rows for the padded slots of the commit chunk operands
+        for (int i = c.l; i < pc::kKP; i += 64) sm.cx.zk[i] = 0;
+        if (c.l < pc::kBL) sm.cx.zt[c.l] = 0;
+    }
+    store_rows_permuted(c, rq, sm.a.t.q);
+    store_rows_permuted(c, rk, sm.a.t.k);
     store_rows(c, rv, sm.b.v);
+    load_state_tile(st[0], 0, slab, c.col, c.h);
     lds_barrier();
 
-    // ---- 4. verify the new tree from the committed state (held in st)
+    // ---- 2. the new tree's Gram, masks and block inverses (no state needed)
     f32x16 gc, ga;
     if (c.w < 3) gram(c, sm.a.t, gc, ga);
     uint32_t vpk[2][8];
     v_to_regs(c, sm.b.v, vpk);
+    load_state_tile(st[1], 1, slab, c.col, c.h);
     lds_barrier();
-    if (sm.tp.bad) {
+    const bool tree_ok = !sm.tp.bad;
+    if (tree_ok) {
+        if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
+        load_state_tile(st[2], 2, slab, c.col, c.h);
+        lds_barrier();
+        inverse(c, sm.b.s);
+    } else {
+        load_state_tile(st[2], 2, slab, c.col, c.h);
+    }
+    load_state_tile(st[3], 3, slab, c.col, c.h);
+    lds_barrier();   // the inverse scratch is free from here on
+
+    // ---- 3. commit: wave 3 validates the path and prepares the first chunk
+    if (c.w == 3) {
+        const bool ok = path_valid(pl, mlen, max_path, n_prev, c.l);
+        if (c.l == 0) {
+            sm.commit_ok = ok;
+            if (s.hd == 0 && status)
+                status[s.b] = (ok ? 0 : kFaultBadPath) | (tree_ok ? 0 : kFaultBadParent);
+        }
+        if (ok && mlen > 0) pc::build16(sm.b.ch, sm.cx, r16, min(pc::kC16, mlen), c.l);
+    }
+    lds_barrier();
+    const bool commit = sm.commit_ok && mlen > 0;
+    if (commit) {
+        bf16x8 ident[2];
+        pc::key_identity(ident, c.m, c.h);
+        pc::apply16(sm.b.ch, sm.cx, st, ident, c.m, c.h, c.col);
+        for (int c0 = pc::kC16; c0 < mlen; c0 += pc::kC16) {
+            lds_barrier();   // every wave is done with the previous chunk
+            if (c.w == 3) {
+                const int mc = min(pc::kC16, mlen - c0);
+                const int rj = c.l >> 2;
+                const pc::Rows16 rr = pc::load_rows16(
+                    slot_id(pl, c0 + rj), rj < mc, slot_id(pl, c0 + (c.l & 15)), c.l < mc,
+                    k_prev + prow0, v_prev + prow0, alpha_prev + pgate0, beta_prev + pgate0,
+                    H * kD, H, pbytes, c.l);
+                pc::build16(sm.b.ch, sm.cx, rr, mc, c.l);
+            }
+            lds_barrier();
+            pc::apply16(sm.b.ch, sm.cx, st, ident, c.m, c.h, c.col);
+        }
+    }
+
+    // ---- 4. verify from the committed slab, writing the slab back as the
+    //         contraction consumes it
+    if (!tree_ok) {
+        if (commit) store_state(st, slab, c.col, c.h);
         store_nan(c, s, out);
         return;
     }
-    if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
-    lds_barrier();
-    inverse(c, sm.b.s);
     f32x16 P[2], R[2];
-    contract(c, sm.a.t, st, P, R);
+    contract(c, sm.a.t, st, P, R, commit ? slab : nullptr);
     lds_barrier();
     f32x16 o0, o1;
     solve_output(c, sm.tp, sm.b.s, P, R, vpk, o0, o1);
@@ -150,7 +232,7 @@ hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s) {
                        (const uint16_t *)a.c.k, (const uint16_t *)a.c.v, a.c.alpha, a.c.beta,
                        a.c.parent, a.c.n, (const uint16_t *)a.v.q, (const uint16_t *)a.v.k,
                        (const uint16_t *)a.v.v, a.v.alpha, a.v.beta, a.v.parent, a.v.out, a.v.n,
-                       a.v.H, a.v.status);
+                       a.v.H, device_cu_count(), a.v.status);
     return hipGetLastError();
 }
 

@@ -176,6 +176,29 @@ __device__ __forceinline__ void load_state(f32x16 (&st)[4], const float *slab, i
                 rs, vo, 4 * kStateDim * (32 * q + crow(r, 0)), 0));
 }
 
+// one tile (rows 32 q .. 32 q + 31) of the slab
+__device__ __forceinline__ void load_state_tile(f32x16 &t, int q, const float *slab, int col,
+                                                int h) {
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc(slab);
+    const int vo = state_lane_offset(col, h);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        t[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rs, vo, 4 * kStateDim * (32 * q + crow(r, 0)), 0));
+}
+
+__device__ __forceinline__ void store_state_tile(const f32x16 &t, int q, float *slab, int col,
+                                                 int h) {
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc(slab);
+    const int vo = state_lane_offset(col, h);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float x = t[r];   // scalar temporary: see store_state
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, vo,
+                                              4 * kStateDim * (32 * q + crow(r, 0)), 0);
+    }
+}
+
 __device__ __forceinline__ void store_state(const f32x16 (&st)[4], float *slab, int col, int h) {
     const __amdgpu_buffer_rsrc_t rs = state_rsrc(slab);
     const int vo = state_lane_offset(col, h);

@@ -275,9 +275,23 @@ __device__ __forceinline__ void key_identity(bf16x8 (&ident)[2], int m, int h) {
                 (m == 16 * kb + 8 * (e >> 2) + 4 * h + (e & 3)) ? 1.f : 0.f);
 }
 
-// Apply the prepared chunk to this wave's state slab (no barrier inside).
-__device__ __forceinline__ void apply_chunk(const ChunkTiles &sm, f32x16 (&st)[4],
-                                            const bf16x8 (&ident)[2], int m, int h, int col) {
+// What the application of a chunk reads, from the point of view of one lane
+// (row m of the path-slot operands).  Rows past the chunk are zero rows.
+struct ChunkView {
+    const uint16_t *kp_row;           // path keys of slot m (d_k permuted)
+    const uint16_t *th_row, *tl_row;  // row m of T, hi / lo (permuted columns)
+    const uint16_t *vp;               // path values, [NR][vp_stride]
+    int vp_stride;
+    const float *eg, *wdec, *beta;    // per path slot, 32 entries, zero past the chunk
+    float glast;
+};
+
+// Apply a prepared chunk of NR (16 or 32) path slots to this wave's state
+// slab (no barrier inside).
+template <int NR>
+__device__ __forceinline__ void apply_rows(const ChunkView &cv, f32x16 (&st)[4],
+                                           const bf16x8 (&ident)[2], int h, int col) {
+    constexpr int KS = NR / 16;   // k-steps over path slots that can be nonzero
     // ---- R = K_p S: B operands straight from the state tiles
     f32x16 R = {};
 #pragma unroll
@@ -289,7 +303,7 @@ __device__ __forceinline__ void apply_chunk(const ChunkTiles &sm, f32x16 (&st)[4
             for (int j = 0; j < 8; ++j) sv[j] = st[q][8 * kk + j];
             bf16x8 sh, sl;
             split8(sv, sh, sl);
-            const bf16x8 a = lds8(&sm.kp[m][32 * q + 16 * kk + 8 * h]);
+            const bf16x8 a = lds8(cv.kp_row + 32 * q + 16 * kk + 8 * h);
             R = mfma(a, sh, R);
             R = mfma(a, sl, R);
         }
@@ -299,44 +313,44 @@ __device__ __forceinline__ void apply_chunk(const ChunkTiles &sm, f32x16 (&st)[4
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int j = crow(r, h);
-        rhs[r] = sm.beta[j] * (to_f32(sm.vp[j][col]) - sm.eg[j] * R[r]);
+        rhs[r] = j < NR ? cv.beta[j] * (to_f32(cv.vp[j * cv.vp_stride + col]) - cv.eg[j] * R[r])
+                        : 0.f;
     }
     f32x16 U = {};
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
         float bv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) bv[j] = rhs[8 * kk + j];
         bf16x8 bhh, bll;
         split8(bv, bhh, bll);
-        const bf16x8 ah = lds8(&sm.th[m][16 * kk + 8 * h]);
-        const bf16x8 al = lds8(&sm.tl[m][16 * kk + 8 * h]);
+        const bf16x8 ah = lds8(cv.th_row + 16 * kk + 8 * h);
+        const bf16x8 al = lds8(cv.tl_row + 16 * kk + 8 * h);
         U = mfma(ah, bhh, U);
         U = mfma(ah, bll, U);
         U = mfma(al, bhh, U);
     }
     bf16x8 wh[2], wl[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
         float wv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) wv[j] = sm.wdec[crow(8 * kk + j, h)] * U[8 * kk + j];
+        for (int j = 0; j < 8; ++j) wv[j] = cv.wdec[crow(8 * kk + j, h)] * U[8 * kk + j];
         split8(wv, wh[kk], wl[kk]);
     }
 
     // ---- S <- e^{g_last} S + K_p^T W.  The key tile of rows 32q.. is put
     // in the result layout by an exact identity product; that layout is
     // the A operand of K_p^T with the path slots in the order W holds them.
-    const float gl = sm.glast;
+    const float gl = cv.glast;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         f32x16 kt = {};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            kt = mfma(lds8(&sm.kp[m][32 * q + 16 * kb + 8 * h]), ident[kb], kt);
+        for (int kb = 0; kb < 2; ++kb) kt = mfma(lds8(cv.kp_row + 32 * q + 16 * kb + 8 * h), ident[kb], kt);
         f32x16 acc = st[q] * gl;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < KS; ++kk) {
             bf16x8 a;
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] = static_cast<__bf16>(kt[8 * kk + e]);
@@ -345,6 +359,167 @@ __device__ __forceinline__ void apply_chunk(const ChunkTiles &sm, f32x16 (&st)[4
         }
         st[q] = acc;
     }
+}
+
+__device__ __forceinline__ void apply_chunk(const ChunkTiles &sm, f32x16 (&st)[4],
+                                            const bf16x8 (&ident)[2], int m, int h, int col) {
+    const ChunkView cv{sm.kp[m], sm.th[m], sm.tl[m], &sm.vp[0][0], kKP,
+                       sm.eg,    sm.wdec,  sm.beta,  sm.glast};
+    apply_rows<kC>(cv, st, ident, h, col);
+}
+
+// ---- 16-slot chunks, for the fused commit-verify kernel, where the chunk
+// tiles overlay scratch of the verify's block inverse and must be small.
+// One wave loads and prepares a chunk on its own (no barrier inside); every
+// wave then applies it.
+constexpr int kC16 = 16;
+
+struct Chunk16 {
+    uint16_t kp[kC16][kKP];               // path keys, d_k permuted within 16-blocks
+    uint16_t vp[kC16][kD];                // path values
+    float x[kC16][kC16];                  // X of the chunk (strictly lower)
+    uint16_t th[kC16][kBL], tl[kC16][kBL];   // T hi / lo; permuted columns, 16..31 zero
+};
+
+struct Chunk16Aux {
+    float g[32], eg[32], wdec[32], beta[32];   // per path slot, zero past the chunk
+    float glast;
+    uint16_t zk[kKP];                           // zero key row (slots 16..31)
+    uint16_t zt[kBL];                           // zero T row (rows 16..31)
+};
+
+// A chunk's rows in the registers of the wave that prepares it: lane l holds
+// bytes [64 (l & 3), 64 (l & 3) + 64) of slot l >> 2's key and value rows,
+// and lanes < 16 hold slot l's gates.
+struct Rows16 {
+    uint4 k[4], v[4];
+    float la, bt;
+};
+
+// slot_id(j) is the node id of chunk slot j (valid for j < mc).  k, v, alpha,
+// beta point at node 0 of this (sequence, head); rs = elements between nodes
+// (H * 128), gs = gate entries between nodes (H); bytes = n * rs * 2.
+__device__ __forceinline__ Rows16 load_rows16(int row_id, bool row_live, int gate_id,
+                                              bool gate_live, const uint16_t *k,
+                                              const uint16_t *v, const float *alpha,
+                                              const float *beta, int rs, int gs, uint32_t bytes,
+                                              int l) {
+    Rows16 r;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k, bytes), vr = make_rsrc(v, bytes);
+    const uint32_t base = row_live ? (uint32_t)(row_id * rs + 32 * (l & 3)) * 2 : bytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.k[i] = load16(kr, row_live ? base + 16 * i : bytes);
+        r.v[i] = load16(vr, row_live ? base + 16 * i : bytes);
+    }
+    const int gi = gate_live ? gate_id : 0;
+    const float a = alpha[(size_t)gi * gs], be = beta[(size_t)gi * gs];
+    r.la = gate_live ? log2f(a) : 0.f;
+    r.bt = gate_live ? be : 0.f;
+    return r;
+}
+
+// One wave: rows into the chunk tiles, decay prefix, Gram, X, and
+// T = (I + X)^{-1} by forward substitution (lane = column of T).  LDS
+// accesses of one wave complete in order, so no barrier is needed inside.
+__device__ __forceinline__ void build16(Chunk16 &ch, Chunk16Aux &ax, const Rows16 &r, int mc,
+                                        int l) {
+    const int m = l & 31, h = l >> 5;
+    {
+        const int j = l >> 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c8 = 32 * (l & 3) + 8 * i;
+            store_row8_permuted(ch.kp[j], c8, r.k[i]);
+            *reinterpret_cast<uint4 *>(&ch.vp[j][c8]) = r.v[i];
+        }
+    }
+    // inclusive prefix of the log2 decays over the chunk (slots past mc: 0)
+    {
+        float gs = (l < mc) ? r.la : 0.f;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            const float t = __shfl_up(gs, o, 32);
+            if ((l & 31) >= o) gs += t;
+        }
+        const float gl = __shfl(gs, mc - 1, 32);
+        if (l < 32) {
+            ax.g[l] = gs;
+            ax.eg[l] = l < mc ? exp2f(gs) : 0.f;
+            ax.wdec[l] = l < mc ? exp2f(gl - gs) : 0.f;
+            ax.beta[l] = l < mc ? r.bt : 0.f;
+        }
+        if (l == 0) ax.glast = exp2f(gl);
+    }
+    // Gram of the chunk keys (transposed tile: lane (j, h) holds k_t.k_j for
+    // t = crow(r, h)); rows past 16 read the zero row
+    const uint16_t *kp_row = m < kC16 ? ch.kp[m] : ax.zk;
+    f32x16 ga = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 a = lds8(kp_row + 16 * kk + 8 * h);
+        ga = mfma(a, a, ga);
+    }
+    // X_jt = beta_j e^{g_j - g_t} k_j.k_t for t < j (registers r < 8 hold t < 16)
+    if (m < kC16) {
+        const int j = m;
+        const float gj = ax.g[j], bj = ax.beta[j];
+#pragma unroll
+        for (int q4 = 0; q4 < 2; ++q4) {
+            float x4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * q4 + e, t = crow(rr, h);
+                x4[e] = (t < j) ? bj * __builtin_amdgcn_exp2f(gj - ax.g[t]) * ga[rr] : 0.f;
+            }
+            *reinterpret_cast<float4 *>(&ch.x[j][8 * q4 + 4 * h]) =
+                make_float4(x4[0], x4[1], x4[2], x4[3]);
+        }
+    }
+    // T column l (lanes 0..15) by forward substitution; lanes 16..31 write
+    // the zero columns 16..31
+    if (l < 16) {
+        const int col = l;
+        float t[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float acc = (rr == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int s4 = 0; s4 < rr; s4 += 4) {
+                const float4 xr = *reinterpret_cast<const float4 *>(&ch.x[rr][s4]);
+                acc = fmaf(-xr.x, t[s4], acc);
+                if (s4 + 1 < rr) acc = fmaf(-xr.y, t[s4 + 1], acc);
+                if (s4 + 2 < rr) acc = fmaf(-xr.z, t[s4 + 2], acc);
+                if (s4 + 3 < rr) acc = fmaf(-xr.w, t[s4 + 3], acc);
+            }
+            t[rr] = acc;
+        }
+        const int pc = perm(col);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const __bf16 hi = static_cast<__bf16>(t[rr]);
+            const __bf16 lo = static_cast<__bf16>(t[rr] - static_cast<float>(hi));
+            ch.th[rr][pc] = __builtin_bit_cast(uint16_t, hi);
+            ch.tl[rr][pc] = __builtin_bit_cast(uint16_t, lo);
+        }
+    } else if (l < 32) {
+        const int pc = perm(l);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            ch.th[rr][pc] = 0;
+            ch.tl[rr][pc] = 0;
+        }
+    }
+}
+
+__device__ __forceinline__ void apply16(const Chunk16 &ch, const Chunk16Aux &ax, f32x16 (&st)[4],
+                                        const bf16x8 (&ident)[2], int m, int h, int col) {
+    const bool live = m < kC16;
+    const ChunkView cv{live ? ch.kp[m] : ax.zk, live ? ch.th[m] : ax.zt, live ? ch.tl[m] : ax.zt,
+                       &ch.vp[0][0],           kD,
+                       ax.eg,                  ax.wdec,
+                       ax.beta,                ax.glast};
+    apply_rows<kC16>(cv, st, ident, h, col);
 }
 
 }  // namespace pc

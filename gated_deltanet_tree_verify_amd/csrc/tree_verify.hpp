@@ -331,10 +331,11 @@ __device__ __forceinline__ void inverse(const Lane &c, SolveBlocks &sb) {
 // P = Q S0 and R = K S0 for this wave's 32 columns; the state slab (four
 // result tiles of S0 rows) is the B operand, split hi/lo
 __device__ __forceinline__ void contract(const Lane &c, const QKTiles &t, const f32x16 (&st)[4],
-                                         f32x16 (&P)[2], f32x16 (&R)[2]) {
+                                         f32x16 (&P)[2], f32x16 (&R)[2],
+                                         float *store_slab = nullptr) {
     P[0] = P[1] = R[0] = R[1] = f32x16{};
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             float sv[8];
@@ -352,6 +353,10 @@ __device__ __forceinline__ void contract(const Lane &c, const QKTiles &t, const 
                 R[tt] = mfma(ak, sl, R[tt]);
             }
         }
+        // optionally write the state tile back as soon as it has been read,
+        // spreading the slab's stores over the contraction
+        if (store_slab) store_state_tile(st[q], q, store_slab, c.col, c.h);
+    }
 }
 
 // right-hand side, tiled forward substitution and output tiles o0 (rows
