@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=16, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the tree-size-126 tree vs single-branch comparison")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -235,6 +237,54 @@ def main():
     achieved = fbytes / step_s / 1e9
     traffic = read_traffic()
 
+    # tree-size-126 comparison: the tree verify against single-branch
+    # recurrent verification (one chain per root-to-leaf branch) on the same
+    # inputs, 8 rotating sets of width-8 best-first trees of 126 nodes
+    cmp126 = None
+    if not args.no_compare:
+        sets = fused = ver = com = None
+        torch.cuda.empty_cache()
+        c_sets = []
+        for s_ in range(8):
+            ts = gs.make_tree126(s_)
+            c_sets.append(dict(q=dev(ts.q_bits.view(np.int16)).view(torch.bfloat16),
+                               k=dev(ts.k_bits.view(np.int16)).view(torch.bfloat16),
+                               v=dev(ts.v_bits.view(np.int16)).view(torch.bfloat16),
+                               alpha=dev(ts.alpha), beta=dev(ts.beta), parent=dev(ts.parent),
+                               S=dev(ts.S0), leaves=sum(len(gs.leaves(p)) for p in ts.parent)))
+        for d in c_sets:
+            d["out"] = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+        tv126 = [g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"],
+                          out=d["out"], stream=stream, prepare=True) for d in c_sets]
+        bv126 = [g.branch_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                                 d["S"], out=d["out"], stream=stream, prepare=True)
+                 for d in c_sets]
+
+        def timed_list(calls, reps):
+            for i in range(3):
+                calls[i % len(calls)]()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                calls[i % len(calls)]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        t_tree = timed_list(tv126, 40)
+        t_branch = timed_list(bv126, 10)
+        w126 = gs.TREE126
+        cmp126 = {"workload": w126.name, "tree_verify_us": t_tree, "branch_verify_us": t_branch,
+                  "speedup": t_branch / t_tree,
+                  "mean_leaves_per_tree": float(np.mean([d["leaves"] / w126.batch
+                                                         for d in c_sets])),
+                  "tree_verify_nodes_per_s": w126.batch * w126.n / (t_tree * 1e-6),
+                  "pages_speedup_b200": 7.1}
+        log(f"n=126: tree verify {t_tree:.1f} us, branch verify {t_branch:.1f} us, "
+            f"speedup {t_branch / t_tree:.2f}")
+        c_sets = tv126 = bv126 = None
+
     # achievable-bandwidth line: a plain 1 GiB device copy
     src = torch.empty(2**28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -277,6 +327,7 @@ def main():
         "commit_hbm_gbps": cbytes / (com_ms * 1e-3) / 1e9,
         "host_enqueue_us_per_step": host_s["fused"] * 1e6,
         "copy_gbps": copy_gbps,
+        "tree126_vs_branch": cmp126,
     }
     if not args.no_cpu_baseline:
         ts, path, plen = host0

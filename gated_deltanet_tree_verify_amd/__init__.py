@@ -7,6 +7,7 @@ of the same name.  All computation runs in the library's HIP kernels; there
 is no CPU or PyTorch fallback, and a missing library raises.
 
     verify(q, k, v, alpha, beta, parent, S0)        -> out   (gdn_tree_verify)
+    branch_verify(q, k, v, alpha, beta, parent, S0) -> out   (gdn_branch_verify, baseline)
     commit(S, path, path_len, k, v, alpha, beta, parent)     (gdn_tree_commit, in place)
     commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent)
                                                     -> out   (gdn_tree_commit_verify)
@@ -19,7 +20,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["load", "lib_path", "verify", "commit", "commit_verify", "path", "Launch", "index", "status_string",
+__all__ = ["load", "lib_path", "verify", "branch_verify", "commit", "commit_verify", "path", "Launch", "index", "status_string",
            "GdnError", "FAULT_BAD_PARENT", "FAULT_BAD_PATH", "DTYPE_F32", "DTYPE_BF16",
            "MAX_NODES", "MAX_DIM", "build"]
 
@@ -68,6 +69,8 @@ def load() -> ctypes.CDLL:
         P, I = ctypes.c_void_p, ctypes.c_int
         lib.gdn_tree_verify.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, P, P]
         lib.gdn_tree_verify.restype = I
+        lib.gdn_branch_verify.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, P, P]
+        lib.gdn_branch_verify.restype = I
         lib.gdn_tree_commit.argtypes = [P, P, P, I, P, P, I, P, P, P, I, I, I, I, I, P, P]
         lib.gdn_tree_commit.restype = I
         lib.gdn_tree_commit_verify.argtypes = [P, P, P, I, P, P, P, P, P, I, P, P, P, I, P, P, P,
@@ -163,9 +166,7 @@ def _qkv_dtype(q):
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
-def verify(q, k, v, alpha, beta, parent, S0, out=None, status=None, stream=None, prepare=False):
-    """gdn_tree_verify: fp32 out [batch][n][H][d_v]; S0 is never written.
-    prepare=True returns a Launch instead of launching."""
+def _verify_like(name, q, k, v, alpha, beta, parent, S0, out, status, stream, prepare):
     torch = _torch()
     lib = load()
     qk = (torch.bfloat16, torch.float32)
@@ -187,8 +188,23 @@ def verify(q, k, v, alpha, beta, parent, S0, out=None, status=None, stream=None,
         _need(status, "status", (torch.int32,), (batch,))
     args = (_ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(alpha), _ptr(beta), _ptr(parent),
             _ptr(S0), _ptr(out), batch, n, H, dk, dv, _ptr(status), _stream(stream))
-    return _issue("gdn_tree_verify", lib.gdn_tree_verify, args,
+    return _issue(name, getattr(lib, name), args,
                   (q, k, v, alpha, beta, parent, S0, out, status), out, prepare)
+
+
+def verify(q, k, v, alpha, beta, parent, S0, out=None, status=None, stream=None, prepare=False):
+    """gdn_tree_verify: fp32 out [batch][n][H][d_v]; S0 is never written.
+    prepare=True returns a Launch instead of launching."""
+    return _verify_like("gdn_tree_verify", q, k, v, alpha, beta, parent, S0, out, status, stream,
+                        prepare)
+
+
+def branch_verify(q, k, v, alpha, beta, parent, S0, out=None, status=None, stream=None,
+                  prepare=False):
+    """gdn_branch_verify: the single-branch recurrent baseline, same result
+    as verify()."""
+    return _verify_like("gdn_branch_verify", q, k, v, alpha, beta, parent, S0, out, status,
+                        stream, prepare)
 
 
 def commit(S, path, path_len, k, v, alpha, beta, parent, status=None, stream=None,

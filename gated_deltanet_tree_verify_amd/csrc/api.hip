@@ -61,7 +61,24 @@ gdn_status gdn_tree_verify(const void *q, const void *k, const void *v, gdn_dtyp
                       batch, n, H, d_k, d_v, status};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::verify_mfma_supports(a)) return from_hip(gdn::launch_verify_mfma(a, s));
+    if (gdn::verify_mfma128_supports(a)) return from_hip(gdn::launch_verify_mfma128(a, s));
     return from_hip(gdn::launch_verify_generic(a, s));
+}
+
+gdn_status gdn_branch_verify(const void *q, const void *k, const void *v, gdn_dtype qkv_dtype,
+                             const float *alpha, const float *beta, const int32_t *parent,
+                             const float *S0, float *out, int batch, int n, int H, int d_k,
+                             int d_v, int32_t *status, void *stream) {
+    if (!q || !k || !v || !alpha || !beta || !parent || !S0 || !out) return GDN_ERR_INVALID_ARG;
+    if (qkv_dtype != GDN_DTYPE_F32 && qkv_dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, alpha, beta, parent, S0, out, status};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+    const gdn_status st = shape_status(batch, n, H, d_k, d_v);
+    if (st != GDN_OK) return st;
+    gdn::VerifyArgs a{q, k, v, qkv_dtype, alpha, beta, parent, S0, out,
+                      batch, n, H, d_k, d_v, status};
+    return from_hip(gdn::launch_branch_verify(a, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_tree_commit(float *S, const int32_t *path, const int32_t *path_len, int max_path,

@@ -1,0 +1,346 @@
+// Stages of the MFMA tree verify for trees of 65..128 nodes, bf16 q/k/v,
+// d_k = d_v = 128 (gfx950).  Same method as tree_verify.hpp (the whole tree
+// is one chunk of the delta rule: (I + X) U = beta (V - e^g (K S0)),
+// O = e^g (Q S0) + Y U, DFlash-TfM page, section on rollback-free tree
+// verification for GDN); the node range is four 32-row blocks, solved as
+// two halves of 64 nodes:
+//     half 0:  U_01 = (I + X_{01,01})^{-1} RHS_01,
+//              O_01 = e^g P_01 + Y_{01,01} U_01
+//     half 1:  U_23 = (I + X_{23,23})^{-1} (RHS_23 - X_{23,01} U_01),
+//              O_23 = e^g P_23 + Y_{23,01} U_01 + Y_{23,23} U_23
+// Each half reuses the 64-node solve blocks (tv::SolveBlocks, tv::inverse);
+// the four cross blocks X_{23,01}, Y_{23,01} have their own LDS.
+#pragma once
+
+#include "tree_verify.hpp"
+
+namespace gdn {
+namespace tv128 {
+
+using namespace tile;
+using tv::kBL;
+using tv::kD;
+using tv::kQK;
+using tv::kThreads;
+using tv::Lane;
+using tv::Seq;
+using tv::SolveBlocks;
+
+constexpr int kN = 128;
+
+struct QKTiles {
+    uint16_t q[kN][kQK];   // d_k index permuted within 16-blocks
+    uint16_t k[kN][kQK];
+};
+
+// cross blocks (row block 2 + a, key block b), a, b in {0, 1}
+struct Cross {
+    uint16_t xh[2][2][32][kBL], xl[2][2][32][kBL];   // -X, hi / lo
+    uint16_t yh[2][2][32][kBL], yl[2][2][32][kBL];   // Y, hi / lo
+};
+
+struct Topo {
+    unsigned long long anc[kN][2];   // ancestor-or-self bitmask per node (bits 0..127)
+    float g[kN];                     // log2 of the path decay product
+    float eg[kN];                    // path decay product e^{g}
+    float beta[kN];
+    int bad;
+};
+
+// wave 3, two nodes per lane (l and 64 + l): parent validation, ancestor
+// bitmasks and log2 decay prefix by pointer jumping (7 rounds cover 128)
+__device__ __forceinline__ void topology(const Lane &c, const Seq &s, const int32_t *parent,
+                                         const float *alpha, const float *beta, Topo &tp,
+                                         int32_t *status, bool write_status) {
+    int par[2], jmp[2];
+    float gs[2], bt[2];
+    bool live[2], badi[2];
+    unsigned long long a0[2], a1[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = 64 * u + c.l;
+        live[u] = i < s.n;
+        par[u] = -1;
+        float a = 1.f;
+        bt[u] = 0.f;
+        if (live[u]) {
+            const size_t row = ((size_t)s.b * s.n + i) * s.H + s.hd;
+            par[u] = parent[(size_t)s.b * s.n + i];
+            a = alpha[row];
+            bt[u] = beta[row];
+        }
+        badi[u] = live[u] && !parent_ok(par[u], i);
+        jmp[u] = (live[u] && !badi[u]) ? par[u] : -1;
+        gs[u] = live[u] ? log2f(a) : 0.f;
+        a0[u] = (live[u] && u == 0) ? (1ull << c.l) : 0ull;
+        a1[u] = (live[u] && u == 1) ? (1ull << c.l) : 0ull;
+    }
+    const bool bad = (__ballot(badi[0]) | __ballot(badi[1])) != 0ull;
+#pragma unroll
+    for (int r = 0; r < 7; ++r) {
+        // every lane publishes both of its nodes; a node fetches its jump
+        // target from the lane and half that hold it
+        const unsigned lo0[2] = {(unsigned)a0[0], (unsigned)a0[1]};
+        const unsigned hi0[2] = {(unsigned)(a0[0] >> 32), (unsigned)(a0[1] >> 32)};
+        const unsigned lo1[2] = {(unsigned)a1[0], (unsigned)a1[1]};
+        const unsigned hi1[2] = {(unsigned)(a1[0] >> 32), (unsigned)(a1[1] >> 32)};
+        int nj[2];
+        float ng[2];
+        unsigned long long na0[2], na1[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int src = jmp[u] >= 0 ? jmp[u] : 64 * u + c.l;
+            const int sl = src & 63;
+            const bool up = src >= 64;
+            const unsigned l0a = __shfl(lo0[0], sl), l0b = __shfl(lo0[1], sl);
+            const unsigned h0a = __shfl(hi0[0], sl), h0b = __shfl(hi0[1], sl);
+            const unsigned l1a = __shfl(lo1[0], sl), l1b = __shfl(lo1[1], sl);
+            const unsigned h1a = __shfl(hi1[0], sl), h1b = __shfl(hi1[1], sl);
+            const float ga = __shfl(gs[0], sl), gb = __shfl(gs[1], sl);
+            const int ja = __shfl(jmp[0], sl), jb = __shfl(jmp[1], sl);
+            na0[u] = ((unsigned long long)(up ? h0b : h0a) << 32) | (up ? l0b : l0a);
+            na1[u] = ((unsigned long long)(up ? h1b : h1a) << 32) | (up ? l1b : l1a);
+            ng[u] = up ? gb : ga;
+            nj[u] = up ? jb : ja;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (jmp[u] >= 0) {
+                a0[u] |= na0[u];
+                a1[u] |= na1[u];
+                gs[u] += ng[u];
+                jmp[u] = nj[u];
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = 64 * u + c.l;
+        tp.anc[i][0] = a0[u];
+        tp.anc[i][1] = a1[u];
+        tp.g[i] = gs[u];
+        tp.eg[i] = live[u] ? exp2f(gs[u]) : 0.f;
+        tp.beta[i] = bt[u];
+    }
+    if (c.l == 0) {
+        tp.bad = bad;
+        if (write_status && status) status[s.b] = bad ? kFaultBadParent : 0;
+    }
+}
+
+// 128 node rows of a bf16 [batch][n][H][128] tensor: eight 16-byte chunks
+// per thread; rows past n read as zero (past the end of the resource)
+__device__ __forceinline__ void load_rows(const Lane &c, const Seq &s, const uint16_t *src,
+                                          uint4 (&x)[8]) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + s.base, (uint32_t)(s.n * s.rstride * 2));
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
+        x[it] = load16(rs, (uint32_t)((row * s.rstride + c8) * 2));
+    }
+}
+
+__device__ __forceinline__ void store_rows_permuted(const Lane &c, const uint4 (&x)[8],
+                                                    uint16_t (*dst)[kQK]) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
+        store_row8_permuted(dst[row], c8, x[it]);
+    }
+}
+
+__device__ __forceinline__ void store_rows(const Lane &c, const uint4 (&x)[8],
+                                           uint16_t (*dst)[kQK]) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
+        *reinterpret_cast<uint4 *>(&dst[row][c8]) = x[it];
+    }
+}
+
+// V values of this lane's four result tiles, as bf16 pairs
+__device__ __forceinline__ void v_to_regs(const Lane &c, const uint16_t (*v)[kQK],
+                                          uint32_t (&vpk)[4][8]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+            vpk[t][r / 2] = (uint32_t)v[32 * t + crow(r, c.h)][c.col] |
+                            ((uint32_t)v[32 * t + crow(r + 1, c.h)][c.col] << 16);
+}
+
+// Gram block (row block a, key block b), transposed: lane (node 32 a + m, h)
+// holds k_s.q_i and k_s.k_i for s = 32 b + crow(r, h)
+__device__ __forceinline__ void gram(const Lane &c, const QKTiles &t, int a, int b, f32x16 &gc,
+                                     f32x16 &ga) {
+    gc = f32x16{};
+    ga = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 ks = lds8(&t.k[32 * b + c.m][16 * kk + 8 * c.h]);
+        const bf16x8 qi = lds8(&t.q[32 * a + c.m][16 * kk + 8 * c.h]);
+        const bf16x8 ki = lds8(&t.k[32 * a + c.m][16 * kk + 8 * c.h]);
+        gc = mfma(ks, qi, gc);
+        ga = mfma(ks, ki, ga);
+    }
+}
+
+// ancestor mask and decay weights on a Gram block: y = Y entries, x = X
+// entries (not yet negated; the diagonal of X is never read)
+__device__ __forceinline__ void mask(const Lane &c, const Topo &tp, int a, int b, const f32x16 &gc,
+                                     const f32x16 &ga, float (&y)[16], float (&x)[16]) {
+    const int i = 32 * a + c.m, h = c.h;
+    const uint32_t mb = (uint32_t)(tp.anc[i][b >> 1] >> (32 * (b & 1))) >> (4 * h);
+    const float gi = tp.g[i], bi = tp.beta[i];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 g4 = *reinterpret_cast<const float4 *>(&tp.g[32 * b + 8 * q4 + 4 * h]);
+        const float gs4[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            const bool star = (mb >> (8 * q4 + e)) & 1u;
+            const float wt = star ? __builtin_amdgcn_exp2f(gi - gs4[e]) : 0.f;
+            y[r] = wt * gc[r];
+            x[r] = (bi * wt) * ga[r];
+        }
+    }
+}
+
+__device__ __forceinline__ void store_split(const Lane &c, const float (&v)[16],
+                                            uint16_t (*hi)[kBL], uint16_t (*lo)[kBL]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 h8, l8;
+        split8(&v[8 * kk], h8, l8);
+        st8(&hi[c.m][16 * kk + 8 * c.h], h8);
+        st8(&lo[c.m][16 * kk + 8 * c.h], l8);
+    }
+}
+
+// the three blocks of half hf (row / key blocks 2 hf, 2 hf + 1) into the
+// 64-node solve blocks, wave w < 3 taking block (0,0), (1,0), (1,1)
+__device__ __forceinline__ void half_blocks(const Lane &c, const QKTiles &t, const Topo &tp,
+                                            int hf, SolveBlocks &sb) {
+    const int la = c.w == 0 ? 0 : 1, lb = c.w == 2 ? 1 : 0;
+    f32x16 gc, ga;
+    gram(c, t, 2 * hf + la, 2 * hf + lb, gc, ga);
+    float y[16], x[16];
+    mask(c, tp, 2 * hf + la, 2 * hf + lb, gc, ga, y, x);
+    store_split(c, y, sb.yh[c.w], sb.yl[c.w]);
+    if (c.w == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = -x[r];
+        store_split(c, x, sb.xh, sb.xl);
+    } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<float4 *>(&sb.d[la][c.m][8 * q4 + 4 * c.h]) =
+                make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+    }
+}
+
+// cross block (2 + a, b) for wave w = 2 a + b
+__device__ __forceinline__ void cross_block(const Lane &c, const QKTiles &t, const Topo &tp,
+                                            Cross &cr) {
+    const int a = c.w >> 1, b = c.w & 1;
+    f32x16 gc, ga;
+    gram(c, t, 2 + a, b, gc, ga);
+    float y[16], x[16];
+    mask(c, tp, 2 + a, b, gc, ga, y, x);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = -x[r];
+    store_split(c, y, cr.yh[a][b], cr.yl[a][b]);
+    store_split(c, x, cr.xh[a][b], cr.xl[a][b]);
+}
+
+// P = Q S0, R = K S0 over rows 64 hf .. 64 hf + 63 for this wave's columns
+__device__ __forceinline__ void contract(const Lane &c, const QKTiles &t, int hf,
+                                         const f32x16 (&st)[4], f32x16 (&P)[2], f32x16 (&R)[2]) {
+    P[0] = P[1] = R[0] = R[1] = f32x16{};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            float sv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sv[j] = st[q][8 * kk + j];
+            bf16x8 sh, sl;
+            split8(sv, sh, sl);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int row = 64 * hf + 32 * tt + c.m;
+                const bf16x8 aq = lds8(&t.q[row][32 * q + 16 * kk + 8 * c.h]);
+                const bf16x8 ak = lds8(&t.k[row][32 * q + 16 * kk + 8 * c.h]);
+                P[tt] = mfma(aq, sh, P[tt]);
+                P[tt] = mfma(aq, sl, P[tt]);
+                R[tt] = mfma(ak, sh, R[tt]);
+                R[tt] = mfma(ak, sl, R[tt]);
+            }
+        }
+}
+
+// right-hand side beta (v - e^g R) and e^g P for rows 64 hf + 32 t + crow
+__device__ __forceinline__ void rhs_and_decay(const Lane &c, const Topo &tp, int hf,
+                                              f32x16 (&P)[2], const f32x16 (&R)[2],
+                                              const uint32_t (&vpk)[4][8], f32x16 (&rhs)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int i0 = 64 * hf + 32 * t + 8 * q4 + 4 * c.h;
+            const float4 b4 = *reinterpret_cast<const float4 *>(&tp.beta[i0]);
+            const float4 e4 = *reinterpret_cast<const float4 *>(&tp.eg[i0]);
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ee[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e;
+                const uint32_t pr = vpk[2 * hf + t][r >> 1];
+                const float vval = __uint_as_float((r & 1) ? (pr & 0xffff0000u) : (pr << 16));
+                rhs[t][r] = bb[e] * (vval - ee[e] * R[t][r]);
+                P[t][r] *= ee[e];
+            }
+        }
+}
+
+// the 64-node solve on prepared right-hand sides and decayed P:
+// u0 = T_0 rhs0, u1 = T_1 (rhs1 - X_10 u0), o = P + Y u
+__device__ __forceinline__ void solve_half(const Lane &c, const SolveBlocks &sb,
+                                           const f32x16 (&rhs)[2], const f32x16 (&P)[2],
+                                           f32x16 (&u)[2], f32x16 (&o)[2]) {
+    const f32x16 zero = {};
+    u[0] = mm3<kBL>(sb.th[0], sb.tl[0], split_tile(rhs[0]), zero, c.m, c.h);
+    const SplitTile u0s = split_tile(u[0]);
+    const f32x16 z1 = mm3<kBL>(sb.xh, sb.xl, u0s, rhs[1], c.m, c.h);
+    u[1] = mm3<kBL>(sb.th[1], sb.tl[1], split_tile(z1), zero, c.m, c.h);
+    o[0] = mm3<kBL>(sb.yh[0], sb.yl[0], u0s, P[0], c.m, c.h);
+    o[1] = mm3<kBL>(sb.yh[1], sb.yl[1], u0s, P[1], c.m, c.h);
+    o[1] = mm3<kBL>(sb.yh[2], sb.yl[2], split_tile(u[1]), o[1], c.m, c.h);
+}
+
+// this lane's entries of output rows 64 hf + 32 t + crow(r, h), rows < n
+__device__ __forceinline__ void store_out(const Lane &c, const Seq &s, int hf,
+                                          const f32x16 (&o)[2], float *out) {
+    float *orow = out + s.base + c.col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 64 * hf + 32 * t + crow(r, c.h);
+            if (i < s.n) orow[(size_t)i * s.rstride] = o[t][r];
+        }
+}
+
+__device__ __forceinline__ void store_nan(const Lane &c, const Seq &s, float *out) {
+    float *orow = out + s.base + c.col;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 32 * t + crow(r, c.h);
+            if (i < s.n) orow[(size_t)i * s.rstride] = __builtin_nanf("");
+        }
+}
+
+}  // namespace tv128
+}  // namespace gdn

@@ -1,0 +1,125 @@
+// MFMA tree-verify kernel for bf16 q/k/v, d_k = d_v = 128 and trees of
+// 65..128 nodes (gfx950).  One workgroup per (sequence, head), four waves,
+// wave w owning d_v columns [32 w, 32 w + 32); the stages and the two-half
+// solve are in tree_verify128.hpp.  LDS: the 128-row Q/K tiles (68 KB), one
+// region that holds the V tile and then the 64-node solve blocks of each
+// half in turn plus the four cross blocks (82 KB), and the topology (5.5 KB):
+// one workgroup per CU.  The state slab is requested one 32-row tile at a
+// time between the phases that do not need it.
+#include "internal.hpp"
+#include "tree_verify128.hpp"
+
+namespace gdn {
+namespace {
+
+using namespace tv128;
+
+struct Smem {
+    QKTiles t;
+    union {
+        uint16_t v[kN][kQK];
+        struct {
+            SolveBlocks s;
+            Cross x;
+        } sx;
+    } b;
+    Topo tp;
+};
+
+static_assert(sizeof(Smem) <= 163840, "one workgroup per CU");
+static_assert(sizeof(uint16_t) * kN * kQK <= sizeof(SolveBlocks),
+              "the V tile must not reach the cross blocks");
+
+__global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ beta,
+    const int32_t *__restrict__ parent, const float *__restrict__ S0, float *__restrict__ out,
+    int n, int H, int32_t *__restrict__ status) {
+    __shared__ Smem sm;
+    const Lane c = tv::lane_coords();
+    const Seq s = tv::seq_coords(blockIdx.x, n, H);
+    const float *slab = S0 + (size_t)blockIdx.x * kD * kD;
+
+    // ---- 1. topology (wave 3), then the Q, K, V tiles
+    if (c.w == 3) tv128::topology(c, s, parent, alpha, beta, sm.tp, status, s.hd == 0);
+    {
+        uint4 x[8];
+        tv128::load_rows(c, s, q, x);
+        tv128::store_rows_permuted(c, x, sm.t.q);
+        tv128::load_rows(c, s, k, x);
+        tv128::store_rows_permuted(c, x, sm.t.k);
+        tv128::load_rows(c, s, v, x);
+        tv128::store_rows(c, x, sm.b.v);
+    }
+    f32x16 st[4];
+    load_state_tile(st[0], 0, slab, c.col, c.h);
+    lds_barrier();
+
+    // ---- 2. cross blocks (one per wave), V -> registers
+    tv128::cross_block(c, sm.t, sm.tp, sm.b.sx.x);
+    uint32_t vpk[4][8];
+    tv128::v_to_regs(c, sm.b.v, vpk);
+    load_state_tile(st[1], 1, slab, c.col, c.h);
+    lds_barrier();
+    if (sm.tp.bad) {
+        tv128::store_nan(c, s, out);
+        return;
+    }
+
+    // ---- 3. half 0: blocks, inverse, P / R, solve, outputs
+    if (c.w < 3) tv128::half_blocks(c, sm.t, sm.tp, 0, sm.b.sx.s);
+    load_state_tile(st[2], 2, slab, c.col, c.h);
+    lds_barrier();
+    tv::inverse(c, sm.b.sx.s);
+    load_state_tile(st[3], 3, slab, c.col, c.h);
+    lds_barrier();
+    f32x16 u01[2];
+    {
+        f32x16 P[2], R[2], rhs[2], o[2];
+        tv128::contract(c, sm.t, 0, st, P, R);
+        tv128::rhs_and_decay(c, sm.tp, 0, P, R, vpk, rhs);
+        tv128::solve_half(c, sm.b.sx.s, rhs, P, u01, o);
+        tv128::store_out(c, s, 0, o, out);
+    }
+    lds_barrier();   // every wave is done with half 0's solve blocks
+
+    // ---- 4. half 1, with the cross terms of half 0's pseudo-values
+    if (c.w < 3) tv128::half_blocks(c, sm.t, sm.tp, 1, sm.b.sx.s);
+    lds_barrier();
+    tv::inverse(c, sm.b.sx.s);
+    lds_barrier();
+    {
+        f32x16 P[2], R[2], rhs[2], u[2], o[2];
+        tv128::contract(c, sm.t, 1, st, P, R);
+        tv128::rhs_and_decay(c, sm.tp, 1, P, R, vpk, rhs);
+        const Cross &cr = sm.b.sx.x;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const SplitTile ub = split_tile(u01[b]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                rhs[t] = mm3<kBL>(cr.xh[t][b], cr.xl[t][b], ub, rhs[t], c.m, c.h);
+                P[t] = mm3<kBL>(cr.yh[t][b], cr.yl[t][b], ub, P[t], c.m, c.h);
+            }
+        }
+        tv128::solve_half(c, sm.b.sx.s, rhs, P, u, o);
+        tv128::store_out(c, s, 1, o, out);
+    }
+}
+
+}  // namespace
+
+bool verify_mfma128_supports(const VerifyArgs &a) {
+    // byte extents of a head's rows must fit the 32-bit buffer ranges
+    return a.dtype == GDN_DTYPE_BF16 && a.dk == kD && a.dv == kD && a.n > 64 && a.n <= kN &&
+           a.H <= 4096;
+}
+
+hipError_t launch_verify_mfma128(const VerifyArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(verify_mfma_n128_kernel, dim3((unsigned)(a.batch * a.H)), dim3(kThreads),
+                       0, s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, a.status);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -357,6 +357,25 @@ def make_config(i: int, s: int = 0, layer: int = 0, chain: bool = False,
     return ts
 
 
+# Tree-size-126 workload for the tree-vs-branch comparison (the pages time
+# their fused kernel against single-branch recurrent verification at 126 tree
+# tokens): one layer, batch 16, 32 heads, d 128, bf16, width-8 best-first
+# trees of 126 nodes (16 expansion rounds, max depth 16).
+TREE126 = Workload("gdn-layer-b16-h32-d128-n126", 16, 126, 32, 128, 128, "bf16",
+                   description="width-8 best-first trees of 126 nodes, max depth 16")
+
+
+def make_tree126(s: int = 0, batch: int | None = None) -> TensorSet:
+    """Input set of the 126-node comparison workload, seed 9000 + s."""
+    w = TREE126
+    b = w.batch if batch is None else batch
+    rng = np.random.Generator(np.random.PCG64(9000 + s))
+    parent = np.stack([best_first_tree(rng, w.n, 8, 16) for _ in range(b)])
+    ts = make_set(parent, w.H, w.d_k, w.d_v, w.dtype, 9000 + s, rng=rng)
+    ts.meta.update({"workload": w.name})
+    return ts
+
+
 def slice_set(ts: TensorSet, batch: int | None, heads: int | None) -> TensorSet:
     b = slice(None) if batch is None else slice(0, batch)
     h = slice(None) if heads is None else slice(0, heads)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 2
+#define GDN_TREE_ABI_VERSION 3
 #define GDN_MAX_NODES 128
 #define GDN_MAX_DIM 128
 
@@ -88,6 +88,23 @@ gdn_status gdn_tree_verify(const void *q, const void *k, const void *v,
                            const float *S0, float *out, int batch, int n,
                            int H, int d_k, int d_v, int32_t *status,
                            void *stream);
+
+/*
+ * Single-branch recurrent verification (the baseline of the experimental
+ * results section of the DFlash-TfM page: the fused tree kernel is compared
+ * with verifying one branch at a time by the recurrence).  Same arguments,
+ * layouts, fault behaviour and result as gdn_tree_verify (up to rounding
+ * order): every root-to-leaf branch is run from S0 as its own chain by the
+ * GDN update, and each node's output S_i^T q_i is written by the branches
+ * through it.  S0 is read once per branch and shared prefixes are
+ * recomputed per branch.  Meant for measurement, not for serving.
+ */
+gdn_status gdn_branch_verify(const void *q, const void *k, const void *v,
+                             gdn_dtype qkv_dtype, const float *alpha,
+                             const float *beta, const int32_t *parent,
+                             const float *S0, float *out, int batch, int n,
+                             int H, int d_k, int d_v, int32_t *status,
+                             void *stream);
 
 /*
  * State commit along the accepted branch (the delayed commitment of the

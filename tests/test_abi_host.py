@@ -31,7 +31,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_commit_verify", "gdn_tree_path",
+    assert {"gdn_tree_verify", "gdn_branch_verify", "gdn_tree_commit", "gdn_tree_commit_verify",
+            "gdn_tree_path",
             "gdn_tree_index", "gdn_status_string", "gdn_tree_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
@@ -44,17 +45,19 @@ def test_abi_version_and_strings(lib):
         assert isinstance(g.status_string(code), str) and g.status_string(code)
 
 
-def _verify(lib, ptr=FAKE, batch=1, n=8, H=1, dk=16, dv=16, dtype=1, null=None, status=None):
+def _verify(lib, ptr=FAKE, batch=1, n=8, H=1, dk=16, dv=16, dtype=1, null=None, status=None,
+            fn="gdn_tree_verify"):
     p = [ptr] * 8
     if null is not None:
         p[null] = None
-    return lib.gdn_tree_verify(p[0], p[1], p[2], dtype, p[3], p[4], p[5], p[6], p[7],
-                               batch, n, H, dk, dv, status, None)
+    return getattr(lib, fn)(p[0], p[1], p[2], dtype, p[3], p[4], p[5], p[6], p[7],
+                            batch, n, H, dk, dv, status, None)
 
 
+@pytest.mark.parametrize("fn", ["gdn_tree_verify", "gdn_branch_verify"])
 @pytest.mark.parametrize("null", range(8))
-def test_verify_null_pointer(lib, null):
-    assert _verify(lib, null=null) == -1
+def test_verify_null_pointer(lib, null, fn):
+    assert _verify(lib, null=null, fn=fn) == -1
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -63,8 +66,9 @@ def test_verify_null_pointer(lib, null):
     (dict(dtype=7), -1), (dict(ptr=MISALIGNED), -1), (dict(status=MISALIGNED), -1),
     (dict(batch=1 << 20, H=1 << 12), -2),
 ])
-def test_verify_rejects(lib, kw, code):
-    assert _verify(lib, **kw) == code
+@pytest.mark.parametrize("fn", ["gdn_tree_verify", "gdn_branch_verify"])
+def test_verify_rejects(lib, kw, code, fn):
+    assert _verify(lib, fn=fn, **kw) == code
 
 
 def test_commit_rejects(lib):

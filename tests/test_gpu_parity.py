@@ -280,6 +280,64 @@ def test_commit_empty_path_is_noop(gpu_lib):
 
 
 # ---------------------------------------------------------------------------
+# single-branch recurrent baseline: the same outputs as the tree verify
+# ---------------------------------------------------------------------------
+def run_branch(g, ts):
+    d = upload(ts)
+    st = torch.full((ts.parent.shape[0],), -7, dtype=torch.int32, device="cuda")
+    out = g.branch_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S0"],
+                          status=st)
+    torch.cuda.synchronize()
+    return host(out), host(st), d
+
+
+@pytest.mark.parametrize("cfg,chain", [(0, False), (0, True), (1, False), (2, False)])
+def test_branch_verify_parity(gpu_lib, cfg, chain):
+    say("branch verify cfg", cfg, "chain", chain)
+    ts = gs.make_config(cfg, chain=chain)
+    out, st, _ = run_branch(gpu_lib, ts)
+    ref, rst = oracle.verify_set(ts)
+    assert st.tolist() == rst.tolist()
+    err = oracle.rel_err(out, ref)
+    say("rel err", err)
+    assert err <= gate(ts)
+
+
+def test_branch_verify_tree126_sampled(gpu_lib):
+    """the comparison workload (126-node width-8 best-first trees), full
+    launch, checked on four sequences"""
+    ts = gs.make_tree126(0)
+    out, st, _ = run_branch(gpu_lib, ts)
+    assert st.tolist() == [0] * 16
+    pick = [0, 5, 10, 15]
+    ref, _ = oracle.verify_set(gs.select(ts, pick))
+    assert oracle.rel_err(out[pick], ref) <= BF16_GATE
+
+
+@pytest.mark.parametrize("shape", ["chain", "star", "bfs16"])
+def test_branch_verify_extreme_trees(gpu_lib, shape):
+    par = {"chain": gs.chain_tree(128), "star": gs.star_tree(128),
+           "bfs16": gs.kary_bfs_tree(128, 16)}[shape]
+    ts = gs.make_set(np.stack([par, par]), 2, 128, 128, "bf16", seed=11)
+    out, _, _ = run_branch(gpu_lib, ts)
+    ref, _ = oracle.verify_set(ts)
+    assert oracle.rel_err(out, ref) <= BF16_GATE
+
+
+def test_branch_verify_shapes_and_faults(gpu_lib):
+    rng = np.random.default_rng(12)
+    par = np.stack([gs.random_recursive_tree(rng, 37, max_depth=9) for _ in range(3)])
+    par[1, 20] = 25
+    ts = gs.make_set(par, 3, 48, 40, "fp32", seed=12)
+    out, st, _ = run_branch(gpu_lib, ts)
+    ref, rst = oracle.verify_set(ts)
+    assert st.tolist() == rst.tolist() == [0, 1, 0]
+    assert np.isnan(out[1]).all()
+    for b in (0, 2):
+        assert oracle.rel_err(out[b], ref[b]) <= FP32_GATE
+
+
+# ---------------------------------------------------------------------------
 # fused commit (previous tree's path) + verify (next tree)
 # ---------------------------------------------------------------------------
 def run_commit_verify(g, prev, cur, path, plen):
