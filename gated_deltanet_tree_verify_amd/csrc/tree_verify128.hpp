@@ -48,10 +48,11 @@ struct Topo {
 };
 
 // wave 3, two nodes per lane (l and 64 + l): parent validation, ancestor
-// bitmasks and log2 decay prefix by pointer jumping (7 rounds cover 128)
+// bitmasks and log2 decay prefix by pointer jumping (7 rounds cover 128).
+// status[b] gets the fault flag (ORed into what is there when status_or).
 __device__ __forceinline__ void topology(const Lane &c, const Seq &s, const int32_t *parent,
                                          const float *alpha, const float *beta, Topo &tp,
-                                         int32_t *status, bool write_status) {
+                                         int32_t *status, bool write_status, bool status_or) {
     int par[2], jmp[2];
     float gs[2], bt[2];
     bool live[2], badi[2];
@@ -124,7 +125,8 @@ __device__ __forceinline__ void topology(const Lane &c, const Seq &s, const int3
     }
     if (c.l == 0) {
         tp.bad = bad;
-        if (write_status && status) status[s.b] = bad ? kFaultBadParent : 0;
+        if (write_status && status)
+            status[s.b] = (status_or ? status[s.b] : 0) | (bad ? kFaultBadParent : 0);
     }
 }
 

@@ -34,14 +34,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta,
     const int32_t *__restrict__ parent, const float *__restrict__ S0, float *__restrict__ out,
-    int n, int H, int32_t *__restrict__ status) {
+    int n, int H, int32_t *__restrict__ status, bool status_or) {
     __shared__ Smem sm;
     const Lane c = tv::lane_coords();
     const Seq s = tv::seq_coords(blockIdx.x, n, H);
     const float *slab = S0 + (size_t)blockIdx.x * kD * kD;
 
     // ---- 1. topology (wave 3), then the Q, K, V tiles
-    if (c.w == 3) tv128::topology(c, s, parent, alpha, beta, sm.tp, status, s.hd == 0);
+    if (c.w == 3)
+        tv128::topology(c, s, parent, alpha, beta, sm.tp, status, s.hd == 0, status_or);
     {
         uint4 x[8];
         tv128::load_rows(c, s, q, x);
@@ -118,7 +119,8 @@ bool verify_mfma128_supports(const VerifyArgs &a) {
 hipError_t launch_verify_mfma128(const VerifyArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(verify_mfma_n128_kernel, dim3((unsigned)(a.batch * a.H)), dim3(kThreads),
                        0, s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, a.status);
+                       a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, a.status,
+                       a.status_or);
     return hipGetLastError();
 }
 

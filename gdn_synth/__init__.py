@@ -357,6 +357,43 @@ def make_config(i: int, s: int = 0, layer: int = 0, chain: bool = False,
     return ts
 
 
+# ----------------------------------------------------------------------------
+# token ids for the acceptance walk (synthetic: no model produces them here)
+# ----------------------------------------------------------------------------
+def make_accept_tokens(rng: np.random.Generator, parent: np.ndarray, vocab: int = 32768,
+                       p_match: float = 0.7):
+    """Draft token ids per node (siblings distinct) and verifier greedy ids.
+
+    For a node with children the verifier's id equals one child's draft id
+    (uniform among the children) with probability p_match, else an id no
+    child carries; for a leaf it is uniform.  Returns (draft, verify), int32
+    arrays shaped like `parent`.
+    """
+    parent = np.asarray(parent)
+    draft = np.zeros(parent.shape, dtype=np.int32)
+    verify = np.zeros(parent.shape, dtype=np.int32)
+    for b in range(parent.shape[0]):
+        par = parent[b]
+        n = len(par)
+        kids = [[] for _ in range(n)]
+        roots = []
+        for i in range(n):
+            (kids[par[i]] if par[i] >= 0 else roots).append(i)
+        for group in [roots] + kids:
+            if group:
+                draft[b, group] = rng.choice(vocab, size=len(group), replace=False)
+        for i in range(n):
+            if kids[i] and rng.random() < p_match:
+                verify[b, i] = draft[b, kids[i][int(rng.integers(0, len(kids[i])))]]
+            else:
+                taken = set(int(x) for x in draft[b, kids[i]])
+                t = int(rng.integers(0, vocab))
+                while t in taken:
+                    t = int(rng.integers(0, vocab))
+                verify[b, i] = t
+    return draft, verify
+
+
 # Tree-size-126 workload for the tree-vs-branch comparison (the pages time
 # their fused kernel against single-branch recurrent verification at 126 tree
 # tokens): one layer, batch 16, 32 heads, d 128, bf16, width-8 best-first

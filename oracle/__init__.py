@@ -60,6 +60,8 @@ def _load():
             lib.oracle_path.restype = None
             lib.oracle_index.argtypes = [P, P, P, I, I, P]
             lib.oracle_index.restype = None
+            lib.oracle_accept.argtypes = [P] * 6 + [I, I, P]
+            lib.oracle_accept.restype = None
             _lib = lib
     return _lib
 
@@ -141,6 +143,22 @@ def index(parent):
     status = np.zeros(batch, dtype=np.int32)
     lib.oracle_index(_p(parent), _p(depth), _p(anc), batch, n, _p(status))
     return depth, anc, status
+
+
+def accept(parent, draft, verify):
+    """Greedy acceptance walk.  Returns (accepted, accept_len, bonus, status),
+    int32 [batch] each."""
+    lib = _load()
+    parent, draft, verify = _i32(parent), _i32(draft), _i32(verify)
+    batch, n = parent.shape
+    assert draft.shape == (batch, n) and verify.shape == (batch, n)
+    acc = np.zeros(batch, dtype=np.int32)
+    alen = np.zeros(batch, dtype=np.int32)
+    bonus = np.zeros(batch, dtype=np.int32)
+    status = np.zeros(batch, dtype=np.int32)
+    lib.oracle_accept(_p(parent), _p(draft), _p(verify), _p(acc), _p(alen), _p(bonus), batch, n,
+                      _p(status))
+    return acc, alen, bonus, status
 
 
 def verify_set(ts, **kw):

@@ -28,6 +28,9 @@
  *
  *   Tree indexing: depth and the ancestor-or-self set of each node.
  *
+ *   Acceptance walk: the greedy walk from the root that makes the accepted
+ *   branch known (see oracle_accept for the reading adopted).
+ *
  * Every sum runs in a fixed order (row index ascending).  The memoised
  * verify computes the state of node i from the stored state of parent(i)
  * with exactly the same operations in the same order as the literal walk, so
@@ -303,5 +306,55 @@ void oracle_index(const int32_t *parent, int32_t *depth, uint32_t *anc,
                     dep[i] += 1;
             }
         }
+    }
+}
+
+/*
+ * Greedy acceptance walk (the step that makes the accepted branch known;
+ * DFlash-TfM page, "Verifica dell'Albero Senza Rollback per GDN": the
+ * commitment waits for the accepted branch).  Reading adopted: node 0 is the
+ * tree's root and is always accepted; from an accepted node p the walk moves
+ * to the child c whose draft token equals the verifier's greedy token at p
+ * (draft[c] == verify[p]), the lowest such id when several siblings match,
+ * and stops when no child matches.  Roots other than node 0 are never
+ * reached.  Outputs: the last accepted node, the number of accepted nodes
+ * (its depth + 1) and the verifier's token at it (the token the step emits
+ * after the accepted draft).  A malformed parent row gives accepted -1,
+ * length 0, token -1 and ORACLE_BAD_PARENT.
+ */
+void oracle_accept(const int32_t *parent, const int32_t *draft, const int32_t *verify,
+                   int32_t *accepted, int32_t *accept_len, int32_t *bonus, int batch, int n,
+                   int32_t *status)
+{
+    for (int b = 0; b < batch; ++b) {
+        const int32_t *par = parent + (size_t)b * n;
+        const int32_t *dr = draft + (size_t)b * n;
+        const int32_t *vf = verify + (size_t)b * n;
+        if (!tree_ok(par, n)) {
+            accepted[b] = -1;
+            accept_len[b] = 0;
+            bonus[b] = -1;
+            if (status)
+                status[b] = ORACLE_BAD_PARENT;
+            continue;
+        }
+        int cur = 0, len = 1;
+        for (;;) {
+            int next = -1;
+            for (int c = cur + 1; c < n; ++c)
+                if (par[c] == cur && dr[c] == vf[cur]) {
+                    next = c;
+                    break;
+                }
+            if (next < 0)
+                break;
+            cur = next;
+            ++len;
+        }
+        accepted[b] = cur;
+        accept_len[b] = len;
+        bonus[b] = vf[cur];
+        if (status)
+            status[b] = 0;
     }
 }

@@ -451,3 +451,77 @@ def test_generators_topological_and_deterministic():
     assert d.max() <= 8
     d, _, _ = oracle.index(gs.make_config(3).parent)
     assert d[:16].max() == 127 and d[32:].max() <= 16
+
+
+# ---------------------------------------------------------------------------
+# greedy acceptance walk (integer; pinned by brute force over all paths)
+# ---------------------------------------------------------------------------
+def _brute_accept(par, draft, verify):
+    """every node whose whole path from node 0 matches (each edge p -> c has
+    draft[c] == verify[p]); with distinct sibling tokens these nodes form one
+    chain, whose deepest node is the accepted one"""
+    n = len(par)
+    ok = []
+    for i in range(n):
+        path = gs.path_to(par, i)
+        if path[0] != 0:
+            continue
+        if all(draft[c] == verify[p] for p, c in zip(path[:-1], path[1:])):
+            ok.append(i)
+    deepest = max(ok, key=lambda i: len(gs.path_to(par, i)))
+    return deepest, len(gs.path_to(par, deepest)), int(verify[deepest]), ok
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_accept_vs_brute_force(seed):
+    rng = np.random.default_rng(500 + seed)
+    par = np.stack([gs.best_first_tree(rng, 40, 4, 10) for _ in range(4)]
+                   + [gs.random_recursive_tree(rng, 40) for _ in range(4)])
+    draft, verify = gs.make_accept_tokens(rng, par, vocab=50, p_match=0.8)
+    acc, alen, bonus, st = oracle.accept(par, draft, verify)
+    assert st.tolist() == [0] * 8
+    for b in range(8):
+        d, L, t, ok = _brute_accept(par[b], draft[b], verify[b])
+        # the matching nodes form a single chain from node 0
+        depths = sorted(len(gs.path_to(par[b], i)) for i in ok)
+        assert depths == list(range(1, len(ok) + 1))
+        assert (acc[b], alen[b], bonus[b]) == (d, L, t)
+
+
+def test_accept_chain_and_star():
+    n = 12
+    par = gs.chain_tree(n)[None]
+    draft = np.arange(100, 100 + n, dtype=np.int32)[None]
+    verify = np.full((1, n), 7, np.int32)
+    verify[0, :5] = draft[0, 1:6]          # nodes 1..5 match, node 6 does not
+    acc, alen, bonus, _ = oracle.accept(par, draft, verify)
+    assert (acc[0], alen[0], bonus[0]) == (5, 6, 7)
+    star = gs.star_tree(6)[None]
+    d2 = np.array([[9, 10, 11, 12, 13, 14]], np.int32)
+    v2 = np.array([[13, 0, 0, 0, 0, 0]], np.int32)
+    acc, alen, bonus, _ = oracle.accept(star, d2, v2)
+    assert (acc[0], alen[0], bonus[0]) == (4, 2, 0)
+    # no child matches: only the root is accepted
+    acc, alen, bonus, _ = oracle.accept(star, d2, np.full((1, 6), 99, np.int32))
+    assert (acc[0], alen[0], bonus[0]) == (0, 1, 99)
+
+
+def test_accept_ties_forests_and_faults():
+    # two siblings carry the matching token: the lower id is taken
+    par = np.array([[-1, 0, 0, 1, 2]], np.int32)
+    draft = np.array([[0, 5, 5, 6, 6]], np.int32)
+    verify = np.array([[5, 6, 6, 0, 0]], np.int32)
+    acc, alen, _, _ = oracle.accept(par, draft, verify)
+    assert (acc[0], alen[0]) == (3, 3)
+    # a second root is never reached, whatever its tokens
+    par = np.array([[-1, 0, -1, 2]], np.int32)
+    draft = np.array([[1, 2, 3, 4]], np.int32)
+    verify = np.array([[3, 9, 4, 9]], np.int32)
+    acc, alen, _, st = oracle.accept(par, draft, verify)
+    assert (acc[0], alen[0], st[0]) == (0, 1, 0)
+    # malformed parents
+    par = np.array([[-1, 0, 3, 1], [-1, 0, 1, 2]], np.int32)
+    z = np.zeros((2, 4), np.int32)
+    acc, alen, bonus, st = oracle.accept(par, z, z)
+    assert acc.tolist() == [-1, 3] and alen.tolist() == [0, 4] and st.tolist() == [1, 0]
+    assert bonus.tolist() == [-1, 0]
