@@ -237,6 +237,30 @@ def main():
     achieved = fbytes / step_s / 1e9
     traffic = read_traffic()
 
+    # the acceptance walk and path extraction that produce the next step's
+    # commit input (integer kernels, launch-latency bound), same trees
+    ts0 = host0[0]
+    draft, vtok = gs.make_accept_tokens(np.random.default_rng(0), ts0.parent, p_match=0.8)
+    dpar, ddraft, dvtok = dev(ts0.parent), dev(draft), dev(vtok)
+    acc_call = g.accept(dpar, ddraft, dvtok, stream=stream, prepare=True)
+    acc_t, _, _ = acc_call()
+    path_call = g.path(dpar, acc_t, max_path, stream=stream, prepare=True)
+
+    def timed_call(call, reps=200):
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    accept_us = timed_call(acc_call)
+    path_us = timed_call(path_call)
+
     # tree-size-126 comparison: the tree verify against single-branch
     # recurrent verification (one chain per root-to-leaf branch) on the same
     # inputs, 8 rotating sets of width-8 best-first trees of 126 nodes
@@ -327,6 +351,8 @@ def main():
         "commit_hbm_gbps": cbytes / (com_ms * 1e-3) / 1e9,
         "host_enqueue_us_per_step": host_s["fused"] * 1e6,
         "copy_gbps": copy_gbps,
+        "accept_us": accept_us,
+        "path_us": path_us,
         "tree126_vs_branch": cmp126,
     }
     if not args.no_cpu_baseline:

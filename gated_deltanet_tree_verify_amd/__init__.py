@@ -11,6 +11,7 @@ is no CPU or PyTorch fallback, and a missing library raises.
     commit(S, path, path_len, k, v, alpha, beta, parent)     (gdn_tree_commit, in place)
     commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent)
                                                     -> out   (gdn_tree_commit_verify)
+    accept(parent, draft_tok, verify_tok)           -> (accepted, accept_len, bonus_tok)
     path(parent, accepted, max_path)                -> (path, path_len)
     index(parent)                                   -> (depth, anc)
 """
@@ -20,7 +21,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["load", "lib_path", "verify", "branch_verify", "commit", "commit_verify", "path", "Launch", "index", "status_string",
+__all__ = ["load", "lib_path", "verify", "branch_verify", "commit", "commit_verify", "accept", "path", "Launch", "index", "status_string",
            "GdnError", "FAULT_BAD_PARENT", "FAULT_BAD_PATH", "DTYPE_F32", "DTYPE_BF16",
            "MAX_NODES", "MAX_DIM", "build"]
 
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_tree_commit_verify.argtypes = [P, P, P, I, P, P, P, P, P, I, P, P, P, I, P, P, P,
                                                P, I, I, I, I, I, P, P]
         lib.gdn_tree_commit_verify.restype = I
+        lib.gdn_tree_accept.argtypes = [P, P, P, P, P, P, I, I, P, P]
+        lib.gdn_tree_accept.restype = I
         lib.gdn_tree_path.argtypes = [P, P, P, P, I, I, I, P, P]
         lib.gdn_tree_path.restype = I
         lib.gdn_tree_index.argtypes = [P, P, P, I, I, P, P]
@@ -284,7 +287,28 @@ def commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent, out=Non
                   prepare)
 
 
-def path(parent, accepted, max_path, out=None, path_len=None, status=None, stream=None):
+def accept(parent, draft_tok, verify_tok, status=None, stream=None, prepare=False):
+    """gdn_tree_accept: (accepted, accept_len, bonus_tok), int32 [batch] each."""
+    torch = _torch()
+    lib = load()
+    _need(parent, "parent", (torch.int32,))
+    batch, n = parent.shape
+    _need(draft_tok, "draft_tok", (torch.int32,), (batch, n))
+    _need(verify_tok, "verify_tok", (torch.int32,), (batch, n))
+    acc = torch.empty((batch,), dtype=torch.int32, device=parent.device)
+    alen = torch.empty((batch,), dtype=torch.int32, device=parent.device)
+    bonus = torch.empty((batch,), dtype=torch.int32, device=parent.device)
+    if status is not None:
+        _need(status, "status", (torch.int32,), (batch,))
+    args = (_ptr(parent), _ptr(draft_tok), _ptr(verify_tok), _ptr(acc), _ptr(alen), _ptr(bonus),
+            batch, n, _ptr(status), _stream(stream))
+    return _issue("gdn_tree_accept", lib.gdn_tree_accept, args,
+                  (parent, draft_tok, verify_tok, acc, alen, bonus, status), (acc, alen, bonus),
+                  prepare)
+
+
+def path(parent, accepted, max_path, out=None, path_len=None, status=None, stream=None,
+         prepare=False):
     """gdn_tree_path: (path int32 [batch][max_path], path_len int32 [batch])."""
     torch = _torch()
     lib = load()
@@ -299,10 +323,10 @@ def path(parent, accepted, max_path, out=None, path_len=None, status=None, strea
     _need(path_len, "path_len", (torch.int32,), (batch,))
     if status is not None:
         _need(status, "status", (torch.int32,), (batch,))
-    rc = lib.gdn_tree_path(_ptr(parent), _ptr(accepted), _ptr(out), _ptr(path_len), batch, n,
-                           int(max_path), _ptr(status), _stream(stream))
-    _check("gdn_tree_path", rc)
-    return out, path_len
+    args = (_ptr(parent), _ptr(accepted), _ptr(out), _ptr(path_len), batch, n, int(max_path),
+            _ptr(status), _stream(stream))
+    return _issue("gdn_tree_path", lib.gdn_tree_path, args,
+                  (parent, accepted, out, path_len, status), (out, path_len), prepare)
 
 
 def index(parent, status=None, stream=None):

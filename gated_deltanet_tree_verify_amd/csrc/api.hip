@@ -149,6 +149,20 @@ gdn_status gdn_tree_path(const int32_t *parent, const int32_t *accepted, int32_t
                                      static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_tree_accept(const int32_t *parent, const int32_t *draft_tok,
+                           const int32_t *verify_tok, int32_t *accepted, int32_t *accept_len,
+                           int32_t *bonus_tok, int batch, int n, int32_t *status, void *stream) {
+    if (!parent || !draft_tok || !verify_tok || !accepted) return GDN_ERR_INVALID_ARG;
+    if (batch < 1 || n < 1) return GDN_ERR_INVALID_ARG;
+    if (n > GDN_MAX_NODES) return GDN_ERR_UNSUPPORTED;
+    const void *ptrs[] = {parent, draft_tok, verify_tok, accepted, accept_len, bonus_tok, status};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_accept(parent, draft_tok, verify_tok, accepted, accept_len,
+                                       bonus_tok, batch, n, status,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_tree_index(const int32_t *parent, int32_t *depth, uint32_t *anc, int batch, int n,
                           int32_t *status, void *stream) {
     if (!parent || !depth || !anc) return GDN_ERR_INVALID_ARG;

@@ -59,6 +59,9 @@ hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s);
 hipError_t launch_path(const int32_t *parent, const int32_t *accepted,
                        int32_t *path, int32_t *path_len, int batch, int n,
                        int max_path, int32_t *status, hipStream_t s);
+hipError_t launch_accept(const int32_t *parent, const int32_t *draft, const int32_t *verify,
+                         int32_t *accepted, int32_t *accept_len, int32_t *bonus, int batch, int n,
+                         int32_t *status, hipStream_t s);
 hipError_t launch_index(const int32_t *parent, int32_t *depth, uint32_t *anc,
                         int batch, int n, int32_t *status, hipStream_t s);
 

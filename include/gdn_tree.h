@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 3
+#define GDN_TREE_ABI_VERSION 4
 #define GDN_MAX_NODES 128
 #define GDN_MAX_DIM 128
 
@@ -156,6 +156,26 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path,
                                   float *out, int batch, int n, int H,
                                   int d_k, int d_v, int32_t *status,
                                   void *stream);
+
+/*
+ * Greedy acceptance walk: finds the accepted branch whose commitment the
+ * section above defers to the next iteration.  draft_tok [batch][n] holds
+ * each node's draft token id, verify_tok [batch][n] the verifier's greedy
+ * token id after the node's root-to-node prefix.  Node 0 (the tree's root)
+ * is accepted; from an accepted node p the walk moves to the lowest-id child
+ * c with draft_tok[c] == verify_tok[p] and stops when no child matches.
+ * Roots other than node 0 are never reached.  Writes accepted[b] (the last
+ * accepted node: feed it to gdn_tree_path), and, when not NULL,
+ * accept_len[b] (accepted nodes, depth + 1) and bonus_tok[b] (the
+ * verifier's token at the last accepted node).  A malformed parent row gives
+ * GDN_FAULT_BAD_PARENT, accepted -1, length 0, token -1.  Integer work,
+ * bit-exact.  The pages do not spell out the acceptance rule; this greedy
+ * match is the reading adopted.
+ */
+gdn_status gdn_tree_accept(const int32_t *parent, const int32_t *draft_tok,
+                           const int32_t *verify_tok, int32_t *accepted,
+                           int32_t *accept_len, int32_t *bonus_tok, int batch,
+                           int n, int32_t *status, void *stream);
 
 /*
  * Accepted path: path[b][0..m) = root .. accepted[b] (root first), the rest

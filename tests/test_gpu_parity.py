@@ -432,6 +432,56 @@ def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype):
 
 
 # ---------------------------------------------------------------------------
+# greedy acceptance walk: bit-exact, then path + fused step from it
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_accept_bit_exact(gpu_lib, cfg):
+    ts = gs.make_config(cfg)
+    rng = np.random.default_rng(cfg)
+    draft, verify = gs.make_accept_tokens(rng, ts.parent, p_match=0.8)
+    st = torch.full((ts.parent.shape[0],), -7, dtype=torch.int32, device="cuda")
+    acc, alen, bonus = gpu_lib.accept(dev(ts.parent), dev(draft), dev(verify), status=st)
+    torch.cuda.synchronize()
+    ra, rl, rb, rs = oracle.accept(ts.parent, draft, verify)
+    assert np.array_equal(host(acc), ra) and np.array_equal(host(alen), rl)
+    assert np.array_equal(host(bonus), rb) and np.array_equal(host(st), rs)
+
+
+def test_accept_ties_and_faults_on_gpu(gpu_lib):
+    rng = np.random.default_rng(9)
+    par = np.stack([gs.random_recursive_tree(rng, 100) for _ in range(6)])
+    draft = rng.integers(0, 3, size=par.shape).astype(np.int32)    # many sibling ties
+    verify = rng.integers(0, 3, size=par.shape).astype(np.int32)
+    par[2, 50] = 70
+    par[4, 0] = 0
+    st = torch.full((6,), -7, dtype=torch.int32, device="cuda")
+    acc, alen, bonus = gpu_lib.accept(dev(par), dev(draft), dev(verify), status=st)
+    torch.cuda.synchronize()
+    ra, rl, rb, rs = oracle.accept(par, draft, verify)
+    assert np.array_equal(host(acc), ra) and np.array_equal(host(alen), rl)
+    assert np.array_equal(host(bonus), rb) and np.array_equal(host(st), rs)
+    assert rs.tolist() == [0, 0, 1, 0, 1, 0]
+
+
+def test_accept_then_path_then_fused_step(gpu_lib):
+    """the decode-loop order: accept on the verified tree, extract the path,
+    commit it fused with the next tree's verify"""
+    prev, cur = gs.make_config(2, s=3), gs.make_config(2, s=4)
+    rng = np.random.default_rng(4)
+    draft, verify = gs.make_accept_tokens(rng, prev.parent, p_match=0.8)
+    dpar = dev(prev.parent)
+    acc, _, _ = gpu_lib.accept(dpar, dev(draft), dev(verify))
+    p, pl = gpu_lib.path(dpar, acc, 13)
+    ra, _, _, _ = oracle.accept(prev.parent, draft, verify)
+    rp, rpl, _ = oracle.path(prev.parent, ra, 13)
+    assert np.array_equal(host(p), rp) and np.array_equal(host(pl), rpl)
+    out, S, st = run_commit_verify(gpu_lib, prev, cur, rp, rpl)
+    oref, Sref, rst = oracle_commit_verify(prev, cur, rp, rpl)
+    assert st.tolist() == rst.tolist() == [0] * 16
+    assert oracle.rel_err(S, Sref) <= BF16_GATE and oracle.rel_err(out, oref) <= BF16_GATE
+
+
+# ---------------------------------------------------------------------------
 # integer work: bit-exact
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
