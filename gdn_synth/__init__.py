@@ -394,6 +394,26 @@ def make_accept_tokens(rng: np.random.Generator, parent: np.ndarray, vocab: int 
     return draft, verify
 
 
+def candidate_table(rng: np.random.Generator, batch: int, n: int, K: int,
+                    vocab: int = 32768):
+    """Synthetic child-candidate table for the tree builder: for every node
+    row, c ~ Geometric(1/2) candidates (at most K) whose log-probabilities
+    are the log of a Dirichlet(1) split sorted descending, -inf in the other
+    slots, and distinct token ids.  Rows are drawn in node order, so with a
+    large enough max_depth the table replays best_first_tree's draws.
+    Returns (logp float32 [batch][n][K], tok int32 [batch][n][K],
+    root_tok int32 [batch])."""
+    lp = np.full((batch, n, K), -np.inf, dtype=np.float64)
+    tok = np.full((batch, n, K), -1, dtype=np.int32)
+    for b in range(batch):
+        for i in range(n):
+            c = min(int(rng.geometric(0.5)), K)
+            lp[b, i, :c] = np.sort(np.log(rng.dirichlet(np.ones(c))))[::-1]
+            tok[b, i, :c] = rng.choice(vocab, size=c, replace=False)
+    root = rng.integers(0, vocab, size=batch).astype(np.int32)
+    return lp.astype(np.float32), tok, root
+
+
 # Tree-size-126 workload for the tree-vs-branch comparison (the pages time
 # their fused kernel against single-branch recurrent verification at 126 tree
 # tokens): one layer, batch 16, 32 heads, d 128, bf16, width-8 best-first

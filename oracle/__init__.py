@@ -9,6 +9,8 @@ Two independent implementations live here:
     along each node's root-to-node path, fp64, literal or memoised walk.
   * brute.py: a NumPy per-branch brute force (every root-to-leaf branch run
     on its own, each node read off the branch that contains it).
+  * tree_build.py: the width-w best-first draft-tree construction as a
+    plain heap.
 
 Inputs are widened exactly to fp64 (bf16 -> fp32 -> fp64 loses nothing).
 """
@@ -22,6 +24,7 @@ import threading
 import numpy as np
 
 from .brute import brute_verify, brute_commit, brute_path, brute_index  # noqa: F401
+from .tree_build import build_tree, build_trees  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")

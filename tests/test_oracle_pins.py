@@ -525,3 +525,108 @@ def test_accept_ties_forests_and_faults():
     acc, alen, bonus, st = oracle.accept(par, z, z)
     assert acc.tolist() == [-1, 3] and alen.tolist() == [0, 4] and st.tolist() == [1, 0]
     assert bonus.tolist() == [-1, 0]
+
+
+# ---------------------------------------------------------------------------
+# width-w best-first tree construction (oracle/tree_build.py)
+# ---------------------------------------------------------------------------
+def _table_replaying_best_first(seed, n, K):
+    """the candidate rows best_first_tree draws, node by node (every node
+    proposes when max_depth >= n), as a table"""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lp = np.full((n, K), -np.inf)
+    for i in range(n):
+        c = int(rng.geometric(0.5))
+        assert c <= K, "seed draws more children than the table holds"
+        lp[i, :c] = np.sort(np.log(rng.dirichlet(np.ones(c))))[::-1]
+    return lp
+
+
+@pytest.mark.parametrize("seed,n,w", [(1, 32, 4), (2, 64, 8), (3, 64, 1), (4, 40, 64)])
+def test_tree_build_replays_the_best_first_generator(seed, n, w):
+    """an independent implementation (the generator interleaves its random
+    draws with its own heap) gives the same tree"""
+    lp = _table_replaying_best_first(seed, n, 24)
+    ref = gs.best_first_tree(np.random.Generator(np.random.PCG64(seed)), n, w, n)
+    par, _, _, nb = oracle.build_tree(lp, np.zeros(lp.shape, np.int32), 0, n, w, n,
+                                      dtype=np.float64)
+    assert nb == n
+    assert np.array_equal(par, ref)
+
+
+def _strict_best_first(lp, n, max_depth):
+    """w = 1 by brute force: every step scans all unused candidates of all
+    inserted nodes (no heap)"""
+    K = lp.shape[1]
+    parent, score, depth, used = [-1], [np.float32(0)], [0], set()
+    while len(parent) < n:
+        best = None
+        for i in range(len(parent)):
+            if depth[i] + 1 > max_depth:
+                continue
+            for j in range(K):
+                if (i, j) in used or not np.isfinite(lp[i, j]):
+                    continue
+                s = np.float32(score[i]) + np.float32(lp[i, j])
+                if best is None or s > best[0]:      # ties: first in (i, j) order
+                    best = (s, i, j)
+        if best is None:
+            break
+        used.add(best[1:])
+        parent.append(best[1])
+        score.append(best[0])
+        depth.append(depth[best[1]] + 1)
+    return np.array(parent, np.int32)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tree_build_width_one_is_strict_best_first(seed):
+    lp, tok, root = gs.candidate_table(np.random.default_rng(seed), 1, 30, 6)
+    for md in (3, 30):
+        par, _, _, nb = oracle.build_tree(lp[0], tok[0], root[0], 30, 1, md)
+        ref = _strict_best_first(lp[0], 30, md)
+        assert np.array_equal(par[:nb], ref)
+
+
+@pytest.mark.parametrize("w", [2, 8])
+def test_tree_build_rounds_take_the_best_available(w):
+    """replay the rounds: each popped group is the w best candidates
+    available at that round's start, in order; new nodes wait a round"""
+    lp, tok, root = gs.candidate_table(np.random.default_rng(20 + w), 1, 48, 8)
+    par, tk, sc, nb = oracle.build_tree(lp[0], tok[0], root[0], 48, w, 6)
+    assert nb > 40 and tk[0] == root[0]
+    depth = [0]
+    for i in range(1, nb):
+        depth.append(depth[par[i]] + 1)
+        assert par[i] < i and depth[i] <= 6
+        j = list(tok[0][par[i]]).index(tk[i])
+        assert sc[i] == np.float32(sc[par[i]]) + np.float32(lp[0][par[i], j])
+    start, inserted = 1, 1
+    while start < nb:
+        avail = []
+        for i in range(inserted):
+            if depth[i] + 1 > 6:
+                continue
+            for j in range(8):
+                if np.isfinite(lp[0][i, j]):
+                    avail.append((-(np.float32(sc[i]) + np.float32(lp[0][i, j])), i, j))
+        taken = {(par[x], list(tok[0][par[x]]).index(tk[x])) for x in range(1, start)}
+        avail = sorted(a for a in avail if a[1:] not in taken)
+        grp = list(range(start, start + min(w, len(avail), nb - start)))
+        assert [(par[x], list(tok[0][par[x]]).index(tk[x])) for x in grp] == \
+            [a[1:] for a in avail[:len(grp)]]
+        inserted = start + len(grp)
+        start += len(grp)
+
+
+def test_tree_build_runs_dry_and_depth_cap():
+    lp = np.full((10, 3), -np.inf, np.float32)
+    lp[0, :2] = [-0.1, -0.5]
+    lp[1, 0] = -0.2
+    par, tk, sc, nb = oracle.build_tree(lp, np.arange(30).reshape(10, 3), 7, 10, 4, 5)
+    assert nb == 4 and par.tolist()[:4] == [-1, 0, 0, 1]
+    assert par[4:].tolist() == [-1] * 6 and tk[4:].tolist() == [-1] * 6
+    assert np.isneginf(sc[4:]).all()
+    lp2, tok2, root2 = gs.candidate_table(np.random.default_rng(7), 1, 64, 8)
+    par, _, _, nb = oracle.build_tree(lp2[0], tok2[0], root2[0], 64, 8, 1)
+    assert (par[1:nb] == 0).all()        # depth cap 1: a star under the root
