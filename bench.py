@@ -260,6 +260,12 @@ def main():
 
     accept_us = timed_call(acc_call)
     path_us = timed_call(path_call)
+    # the step before verify: width-8 best-first construction of the same
+    # batch's 64-node trees from a synthetic candidate table (K = 8)
+    clp, ctok, croot = gs.candidate_table(np.random.default_rng(1), batch, n, 8)
+    build_call = g.build_tree(dev(clp), dev(ctok), dev(croot), 8, 12, stream=stream,
+                              prepare=True)
+    build_us = timed_call(build_call)
 
     # tree-size-126 comparison: the tree verify against single-branch
     # recurrent verification (one chain per root-to-leaf branch) on the same
@@ -351,6 +357,7 @@ def main():
         "commit_hbm_gbps": cbytes / (com_ms * 1e-3) / 1e9,
         "host_enqueue_us_per_step": host_s["fused"] * 1e6,
         "copy_gbps": copy_gbps,
+        "tree_build_us": build_us,
         "accept_us": accept_us,
         "path_us": path_us,
         "tree126_vs_branch": cmp126,

@@ -11,6 +11,8 @@ is no CPU or PyTorch fallback, and a missing library raises.
     commit(S, path, path_len, k, v, alpha, beta, parent)     (gdn_tree_commit, in place)
     commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent)
                                                     -> out   (gdn_tree_commit_verify)
+    build_tree(cand_logp, cand_tok, root_tok, width, max_depth)
+                                                    -> (parent, token, score, n_built)
     accept(parent, draft_tok, verify_tok)           -> (accepted, accept_len, bonus_tok)
     path(parent, accepted, max_path)                -> (path, path_len)
     index(parent)                                   -> (depth, anc)
@@ -21,7 +23,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["load", "lib_path", "verify", "branch_verify", "commit", "commit_verify", "accept", "path", "Launch", "index", "status_string",
+__all__ = ["load", "lib_path", "verify", "branch_verify", "commit", "commit_verify", "build_tree", "accept", "path", "Launch", "index", "status_string",
            "GdnError", "FAULT_BAD_PARENT", "FAULT_BAD_PATH", "DTYPE_F32", "DTYPE_BF16",
            "MAX_NODES", "MAX_DIM", "build"]
 
@@ -34,6 +36,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 MAX_NODES = 128
 MAX_DIM = 128
+MAX_CANDIDATES = 32
 
 _lock = threading.Lock()
 _lib = None
@@ -77,6 +80,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_tree_commit_verify.argtypes = [P, P, P, I, P, P, P, P, P, I, P, P, P, I, P, P, P,
                                                P, I, I, I, I, I, P, P]
         lib.gdn_tree_commit_verify.restype = I
+        lib.gdn_tree_build.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+        lib.gdn_tree_build.restype = I
         lib.gdn_tree_accept.argtypes = [P, P, P, P, P, P, I, I, P, P]
         lib.gdn_tree_accept.restype = I
         lib.gdn_tree_path.argtypes = [P, P, P, P, I, I, I, P, P]
@@ -285,6 +290,31 @@ def commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent, out=Non
     return _issue("gdn_tree_commit_verify", lib.gdn_tree_commit_verify, args,
                   (S, path, path_len, *prev, q, k, v, alpha, beta, parent, out, status), out,
                   prepare)
+
+
+def build_tree(cand_logp, cand_tok, root_tok, width, max_depth, stream=None, prepare=False):
+    """gdn_tree_build: (parent, token, score, n_built) from a candidate table
+    cand_logp fp32 [batch][n][K], cand_tok int32 [batch][n][K]; root_tok
+    int32 [batch] or None."""
+    torch = _torch()
+    lib = load()
+    _need(cand_logp, "cand_logp", (torch.float32,))
+    if cand_logp.dim() != 3:
+        raise ValueError("cand_logp must be [batch][n][K]")
+    batch, n, K = cand_logp.shape
+    _need(cand_tok, "cand_tok", (torch.int32,), (batch, n, K))
+    if root_tok is not None:
+        _need(root_tok, "root_tok", (torch.int32,), (batch,))
+    dev = cand_logp.device
+    parent = torch.empty((batch, n), dtype=torch.int32, device=dev)
+    token = torch.empty((batch, n), dtype=torch.int32, device=dev)
+    score = torch.empty((batch, n), dtype=torch.float32, device=dev)
+    n_built = torch.empty((batch,), dtype=torch.int32, device=dev)
+    args = (_ptr(cand_logp), _ptr(cand_tok), _ptr(root_tok), _ptr(parent), _ptr(token),
+            _ptr(score), _ptr(n_built), batch, n, K, int(width), int(max_depth), _stream(stream))
+    return _issue("gdn_tree_build", lib.gdn_tree_build, args,
+                  (cand_logp, cand_tok, root_tok, parent, token, score, n_built),
+                  (parent, token, score, n_built), prepare)
 
 
 def accept(parent, draft_tok, verify_tok, status=None, stream=None, prepare=False):

@@ -149,6 +149,20 @@ gdn_status gdn_tree_path(const int32_t *parent, const int32_t *accepted, int32_t
                                      static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_tree_build(const float *cand_logp, const int32_t *cand_tok, const int32_t *root_tok,
+                          int32_t *parent, int32_t *token, float *score, int32_t *n_built,
+                          int batch, int n, int K, int width, int max_depth, void *stream) {
+    if (!cand_logp || !cand_tok || !parent || !token || !score) return GDN_ERR_INVALID_ARG;
+    if (batch < 1 || n < 1 || K < 1 || width < 1 || max_depth < 0) return GDN_ERR_INVALID_ARG;
+    if (n > GDN_MAX_NODES || K > GDN_MAX_CANDIDATES) return GDN_ERR_UNSUPPORTED;
+    const void *ptrs[] = {cand_logp, cand_tok, root_tok, parent, token, score, n_built};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+    return from_hip(gdn::launch_tree_build(cand_logp, cand_tok, root_tok, parent, token, score,
+                                           n_built, batch, n, K, width, max_depth,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_tree_accept(const int32_t *parent, const int32_t *draft_tok,
                            const int32_t *verify_tok, int32_t *accepted, int32_t *accept_len,
                            int32_t *bonus_tok, int batch, int n, int32_t *status, void *stream) {

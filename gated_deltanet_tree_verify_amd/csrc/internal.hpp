@@ -62,6 +62,10 @@ hipError_t launch_path(const int32_t *parent, const int32_t *accepted,
 hipError_t launch_accept(const int32_t *parent, const int32_t *draft, const int32_t *verify,
                          int32_t *accepted, int32_t *accept_len, int32_t *bonus, int batch, int n,
                          int32_t *status, hipStream_t s);
+hipError_t launch_tree_build(const float *cand_logp, const int32_t *cand_tok,
+                             const int32_t *root_tok, int32_t *parent, int32_t *token,
+                             float *score, int32_t *n_built, int batch, int n, int K, int width,
+                             int max_depth, hipStream_t s);
 hipError_t launch_index(const int32_t *parent, int32_t *depth, uint32_t *anc,
                         int batch, int n, int32_t *status, hipStream_t s);
 

@@ -53,9 +53,10 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 4
+#define GDN_TREE_ABI_VERSION 5
 #define GDN_MAX_NODES 128
 #define GDN_MAX_DIM 128
+#define GDN_MAX_CANDIDATES 32   /* child candidates per node, gdn_tree_build */
 
 typedef enum {
     GDN_OK = 0,
@@ -156,6 +157,32 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path,
                                   float *out, int batch, int n, int H,
                                   int d_k, int d_v, int32_t *status,
                                   void *stream);
+
+/*
+ * Width-w best-first draft-tree construction (the DFlash-TfM page's tree
+ * construction section: top-w candidates are taken off the candidate heap
+ * and expanded together, ceil(B/w) rounds for a budget of B nodes).
+ * cand_logp [batch][n][K] fp32 and cand_tok [batch][n][K] int32: row i holds
+ * the K child candidates that the i-th inserted node proposes (log-probs,
+ * -inf or NaN for an absent slot, token ids); node ids are insertion order.
+ * Node 0 is the root (score 0, depth 0, token root_tok[b], or -1 when
+ * root_tok is NULL).  An inserted node proposes its candidates with score
+ * = its score + log-prob (one fp32 addition) unless the child would be
+ * deeper than max_depth; each round takes up to `width` candidates, best
+ * first (higher score, then lower node id, then lower slot), and the new
+ * nodes propose from the next round on.  Writes parent/token/score
+ * [batch][n] (a topologically sorted tree, ready for gdn_tree_verify) and,
+ * when not NULL, n_built[b]: fewer than n when the candidates run out, the
+ * unused rows then hold parent -1, token -1, score -inf.  The score order
+ * decides integers, so it is fp32 exactly as stated; results are bit-exact.
+ * 1 <= n <= GDN_MAX_NODES, 1 <= K <= GDN_MAX_CANDIDATES, width >= 1,
+ * max_depth >= 0.
+ */
+gdn_status gdn_tree_build(const float *cand_logp, const int32_t *cand_tok,
+                          const int32_t *root_tok, int32_t *parent,
+                          int32_t *token, float *score, int32_t *n_built,
+                          int batch, int n, int K, int width, int max_depth,
+                          void *stream);
 
 /*
  * Greedy acceptance walk: finds the accepted branch whose commitment the

@@ -32,7 +32,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"gdn_tree_verify", "gdn_branch_verify", "gdn_tree_commit", "gdn_tree_commit_verify",
-            "gdn_tree_path", "gdn_tree_accept",
+            "gdn_tree_path", "gdn_tree_accept", "gdn_tree_build",
             "gdn_tree_index", "gdn_status_string", "gdn_tree_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
@@ -113,6 +113,12 @@ def test_commit_verify_rejects(lib, kw, code):
 
 def test_path_and_index_reject(lib):
     P = FAKE
+    assert lib.gdn_tree_build(None, P, None, P, P, P, None, 1, 8, 4, 2, 4, None) == -1
+    assert lib.gdn_tree_build(P, P, None, P, P, P, None, 1, 8, 4, 0, 4, None) == -1
+    assert lib.gdn_tree_build(P, P, None, P, P, P, None, 1, 8, 4, 2, -1, None) == -1
+    assert lib.gdn_tree_build(P, P, None, P, P, P, None, 1, 8, 33, 2, 4, None) == -2
+    assert lib.gdn_tree_build(P, P, None, P, P, P, None, 1, 129, 4, 2, 4, None) == -2
+    assert lib.gdn_tree_build(P, P, MISALIGNED, P, P, P, None, 1, 8, 4, 2, 4, None) == -1
     assert lib.gdn_tree_accept(None, P, P, P, None, None, 1, 8, None, None) == -1
     assert lib.gdn_tree_accept(P, P, P, None, None, None, 1, 8, None, None) == -1
     assert lib.gdn_tree_accept(P, P, P, P, None, None, 0, 8, None, None) == -1

@@ -432,6 +432,38 @@ def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype):
 
 
 # ---------------------------------------------------------------------------
+# width-w best-first tree construction: bit-exact (fp32 score order)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("batch,n,K,w,md", [(16, 64, 8, 8, 12), (4, 128, 32, 16, 16),
+                                            (3, 40, 5, 1, 6), (2, 126, 8, 8, 16),
+                                            (5, 64, 3, 64, 2), (1, 1, 4, 2, 3)])
+def test_tree_build_bit_exact(gpu_lib, batch, n, K, w, md):
+    say("tree build", batch, n, K, w, md)
+    lp, tok, root = gs.candidate_table(np.random.default_rng(n + K + w), batch, n, K)
+    if batch > 1:
+        lp[1, 3, :] = np.nan            # a node with no candidates
+    par, tk, sc, nb = gpu_lib.build_tree(dev(lp), dev(tok), dev(root), w, md)
+    torch.cuda.synchronize()
+    rp, rt, rs, rn = oracle.build_trees(lp, tok, root, w, md)
+    assert np.array_equal(host(nb), rn)
+    assert np.array_equal(host(par), rp) and np.array_equal(host(tk), rt)
+    assert np.array_equal(host(sc).view(np.uint32), rs.view(np.uint32))
+
+
+def test_tree_build_ties_and_dry(gpu_lib):
+    lp = np.zeros((2, 20, 4), np.float32)   # every score ties: the order alone decides
+    lp[:, :, 3] = -np.inf
+    lp[1, 1:, :] = -np.inf                  # sequence 1 runs dry after the root's children
+    tok = np.arange(2 * 20 * 4, dtype=np.int32).reshape(2, 20, 4)
+    par, tk, sc, nb = gpu_lib.build_tree(dev(lp), dev(tok), None, 3, 20)
+    torch.cuda.synchronize()
+    rp, rt, rs, rn = oracle.build_trees(lp, tok, np.full(2, -1, np.int32), 3, 20)
+    assert host(nb).tolist() == rn.tolist() == [20, 4]
+    assert np.array_equal(host(par), rp) and np.array_equal(host(tk), rt)
+    assert np.array_equal(host(sc).view(np.uint32), rs.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
 # greedy acceptance walk: bit-exact, then path + fused step from it
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg", [1, 2, 3])
