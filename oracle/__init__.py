@@ -65,6 +65,8 @@ def _load():
             lib.oracle_index.restype = None
             lib.oracle_accept.argtypes = [P] * 6 + [I, I, P]
             lib.oracle_accept.restype = None
+            lib.oracle_pseudo.argtypes = [P] * 7 + [I] * 6 + [P]
+            lib.oracle_pseudo.restype = I
             _lib = lib
     return _lib
 
@@ -146,6 +148,25 @@ def index(parent):
     status = np.zeros(batch, dtype=np.int32)
     lib.oracle_index(_p(parent), _p(depth), _p(anc), batch, n, _p(status))
     return depth, anc, status
+
+
+def pseudo(k, v, alpha, beta, parent, S0, nthreads=0):
+    """Pseudo-values u_i = beta_i (v_i - alpha_i S_parent^T k_i) of every node.
+    Returns (U fp64 [batch][n][H][dv], status)."""
+    lib = _load()
+    k, v, alpha, beta, S0 = map(_f64, (k, v, alpha, beta, S0))
+    parent = _i32(parent)
+    batch, n, H, dk = k.shape
+    dv = v.shape[-1]
+    U = np.zeros((batch, n, H, dv), dtype=np.float64)
+    status = np.zeros(batch, dtype=np.int32)
+    lib.oracle_pseudo(_p(k), _p(v), _p(alpha), _p(beta), _p(parent), _p(S0), _p(U), batch, n,
+                      H, dk, dv, int(nthreads), _p(status))
+    return U, status
+
+
+def pseudo_set(ts, S0=None, **kw):
+    return pseudo(ts.k, ts.v, ts.alpha, ts.beta, ts.parent, ts.S0 if S0 is None else S0, **kw)
 
 
 def accept(parent, draft, verify):

@@ -358,3 +358,67 @@ void oracle_accept(const int32_t *parent, const int32_t *draft, const int32_t *v
             status[b] = 0;
     }
 }
+
+/*
+ * Pseudo-values of the tree (the u of the chunked form; DFlash-TfM page,
+ * "Verifica dell'Albero Senza Rollback per GDN", the system (I + X) U = ...).
+ * Written out from the update itself: with S_p the state at the parent of
+ * node i (S0 for a root),
+ *     S_i = alpha_i (I - beta_i k_i k_i^T) S_p + beta_i k_i v_i^T
+ *         = alpha_i S_p + k_i u_i^T,   u_i = beta_i (v_i - alpha_i S_p^T k_i),
+ * so the committed state after a path is e^{g_a} S0 + sum_s e^{g_a - g_s}
+ * k_s u_s^T.  U [batch][n][H][dv].  A malformed tree gives NaN rows and
+ * ORACLE_BAD_PARENT.  States are formed by the same memoised walk as the
+ * verify (state of i from the stored state of parent(i)).
+ */
+int oracle_pseudo(const double *k, const double *v, const double *alpha,
+                  const double *beta, const int32_t *parent, const double *S0,
+                  double *U, int batch, int n, int H, int dk, int dv, int nthreads,
+                  int32_t *status)
+{
+    const int nt = default_threads(nthreads);
+    for (int b = 0; b < batch; ++b) {
+        int ok = tree_ok(parent + (size_t)b * n, n);
+        if (status)
+            status[b] = ok ? 0 : ORACLE_BAD_PARENT;
+        if (!ok)
+            for (size_t e = 0; e < (size_t)n * H * dv; ++e)
+                U[(size_t)b * n * H * dv + e] = NAN;
+    }
+    const long pairs = (long)batch * H;
+#pragma omp parallel num_threads(nt)
+    {
+        const size_t ss = (size_t)dk * dv;
+        double *st = malloc((size_t)n * ss * sizeof(double));
+        double *w = malloc((size_t)dv * sizeof(double));
+#pragma omp for schedule(dynamic)
+        for (long bh = 0; bh < pairs; ++bh) {
+            const int b = (int)(bh / H), h = (int)(bh % H);
+            const int32_t *par = parent + (size_t)b * n;
+            if (!tree_ok(par, n))
+                continue;
+            const double *s0 = S0 + (size_t)bh * ss;
+            for (int i = 0; i < n; ++i) {
+                const size_t row = ((size_t)b * n + i) * H + h;
+                const double *kt = k + row * dk, *vt = v + row * dv;
+                const double a = alpha[row], be = beta[row];
+                const double *Sp = par[i] < 0 ? s0 : st + (size_t)par[i] * ss;
+                /* w = S_p^T k, then u = beta (v - alpha w) */
+                for (int c = 0; c < dv; ++c)
+                    w[c] = 0.0;
+                for (int r = 0; r < dk; ++r)
+                    for (int c = 0; c < dv; ++c)
+                        w[c] += Sp[(size_t)r * dv + c] * kt[r];
+                for (int c = 0; c < dv; ++c)
+                    U[row * dv + c] = be * (vt[c] - a * w[c]);
+                /* the node's state, for its children */
+                double *Si = st + (size_t)i * ss;
+                memcpy(Si, Sp, ss * sizeof(double));
+                gdn_update(Si, dk, dv, kt, vt, a, be, w);
+            }
+        }
+        free(st);
+        free(w);
+    }
+    return nt;
+}

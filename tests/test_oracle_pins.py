@@ -630,3 +630,58 @@ def test_tree_build_runs_dry_and_depth_cap():
     lp2, tok2, root2 = gs.candidate_table(np.random.default_rng(7), 1, 64, 8)
     par, _, _, nb = oracle.build_tree(lp2[0], tok2[0], root2[0], 64, 8, 1)
     assert (par[1:nb] == 0).all()        # depth cap 1: a star under the root
+
+
+# ---------------------------------------------------------------------------
+# pseudo-values u (what the next iteration's commit can reuse)
+# ---------------------------------------------------------------------------
+def _decay_path(ts, b, h, path):
+    return np.cumsum(np.log(ts.alpha[b, path, h].astype(np.float64)))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_pseudo_values_rebuild_the_committed_state(seed):
+    """e^{g_a} S0 + sum_{s in path(a)} e^{g_a - g_s} k_s u_s^T equals the
+    explicit recurrence along path(a) (the commit oracle), for every node a"""
+    rng = np.random.default_rng(70 + seed)
+    par = np.stack([gs.random_recursive_tree(rng, 14, max_depth=6) for _ in range(2)])
+    ts = gs.make_set(par, 2, 8, 6, "fp32", seed=70 + seed)
+    U, st = oracle.pseudo_set(ts)
+    assert st.tolist() == [0, 0]
+    for b in range(2):
+        for a in range(14):
+            path = gs.path_to(ts.parent[b], a)
+            Sref, _ = oracle.commit(ts.S0[b:b + 1], path[None].astype(np.int32),
+                                    np.array([len(path)], np.int32), ts.k[b:b + 1],
+                                    ts.v[b:b + 1], ts.alpha[b:b + 1], ts.beta[b:b + 1],
+                                    ts.parent[b:b + 1])
+            for h in range(2):
+                g = _decay_path(ts, b, h, path)
+                S = np.exp(g[-1]) * ts.S0[b, h].astype(np.float64)
+                for j, s in enumerate(path):
+                    S += np.exp(g[-1] - g[j]) * np.outer(ts.k[b, s, h], U[b, s, h])
+                np.testing.assert_allclose(S, Sref[0, h], rtol=1e-12, atol=1e-13)
+
+
+def test_pseudo_values_give_the_outputs():
+    """o_i = e^{g_i} S0^T q_i + sum_{s in anc*(i)} e^{g_i - g_s} (q_i . k_s) u_s
+    equals the explicit walk's outputs"""
+    ts = gs.make_config(0)
+    U, _ = oracle.pseudo_set(ts)
+    out, _ = oracle.verify_set(ts)
+    par = ts.parent[0]
+    for i in range(len(par)):
+        path = gs.path_to(par, i)
+        g = _decay_path(ts, 0, 0, path)
+        qi = ts.q[0, i, 0].astype(np.float64)
+        o = np.exp(g[-1]) * ts.S0[0, 0].T.astype(np.float64) @ qi
+        for j, s in enumerate(path):
+            o += np.exp(g[-1] - g[j]) * float(qi @ ts.k[0, s, 0].astype(np.float64)) * U[0, s, 0]
+        np.testing.assert_allclose(o, out[0, i, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_pseudo_values_bad_tree():
+    ts = gs.make_config(2, batch=2, heads=2)
+    ts.parent[1, 5] = 9
+    U, st = oracle.pseudo_set(ts)
+    assert st.tolist() == [0, 1] and np.isnan(U[1]).all() and np.isfinite(U[0]).all()
