@@ -104,18 +104,20 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path, const int32_t *path_le
 gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *path_len,
                                   int max_path, const void *k_prev, const void *v_prev,
                                   const float *alpha_prev, const float *beta_prev,
-                                  const int32_t *parent_prev, int n_prev, const void *q,
-                                  const void *k, const void *v, gdn_dtype qkv_dtype,
-                                  const float *alpha, const float *beta, const int32_t *parent,
-                                  float *out, int batch, int n, int H, int d_k, int d_v,
-                                  int32_t *status, void *stream) {
+                                  const int32_t *parent_prev, const float *u_prev, int n_prev,
+                                  const void *q, const void *k, const void *v,
+                                  gdn_dtype qkv_dtype, const float *alpha, const float *beta,
+                                  const int32_t *parent, float *out, float *u_out, int batch,
+                                  int n, int H, int d_k, int d_v, int32_t *status,
+                                  void *stream) {
     if (!S || !path || !path_len || !k_prev || !v_prev || !alpha_prev || !beta_prev ||
         !parent_prev || !q || !k || !v || !alpha || !beta || !parent || !out)
         return GDN_ERR_INVALID_ARG;
     if (qkv_dtype != GDN_DTYPE_F32 && qkv_dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID_ARG;
     if (max_path < 1) return GDN_ERR_INVALID_ARG;
-    const void *ptrs[] = {S, path, path_len, k_prev, v_prev, alpha_prev, beta_prev, parent_prev,
-                          q, k, v, alpha, beta, parent, out, status};
+    const void *ptrs[] = {S,    path, path_len, k_prev, v_prev, alpha_prev, beta_prev, parent_prev,
+                          u_prev, q,  k,        v,      alpha,  beta,       parent,    out,
+                          u_out, status};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
     gdn_status st = shape_status(batch, n_prev, H, d_k, d_v);
@@ -124,11 +126,15 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
     gdn::CommitVerifyArgs a{
         {S, path, path_len, max_path, k_prev, v_prev, qkv_dtype, alpha_prev, beta_prev,
          parent_prev, batch, n_prev, H, d_k, d_v, status},
-        {q, k, v, qkv_dtype, alpha, beta, parent, S, out, batch, n, H, d_k, d_v, status, true}};
+        {q, k, v, qkv_dtype, alpha, beta, parent, S, out, batch, n, H, d_k, d_v, status, true},
+        u_prev,
+        u_out};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::commit_verify_mfma_supports(a)) return from_hip(gdn::launch_commit_verify_mfma(a, s));
-    // other shapes: the two halves as separate launches on the same stream,
-    // the verify ORing its flag into what the commit wrote
+    if (u_out) return GDN_ERR_UNSUPPORTED;
+    // other shapes: the two halves as separate launches on the same stream
+    // (the commit solves for the pseudo-values itself, so u_prev is not
+    // needed), the verify ORing its flag into what the commit wrote
     const hipError_t e = gdn::commit_mfma_supports(a.c) ? gdn::launch_commit_mfma(a.c, s)
                                                         : gdn::launch_commit(a.c, s);
     if (e != hipSuccess) return GDN_ERR_HIP;

@@ -44,14 +44,17 @@ struct Smem {
     union {
         uint16_t v[kN][kQK];
         SolveBlocks s;
-        pc::Chunk16 ch;   // over d / tinv, dead once the inverse has finished
+        pc::Chunk16 ch;      // over d / tinv, dead once the inverse has finished
+        pc::KeyChunk32 kc;   // same place, when the pseudo-values are given
     } b;
     Topo tp;
     pc::Chunk16Aux cx;
+    int pid[kMaxPathIds];    // previous path ids, when the pseudo-values are given
     int commit_ok;
 };
 
-static_assert(sizeof(pc::Chunk16) <= offsetof(SolveBlocks, th),
+static_assert(sizeof(pc::Chunk16) <= offsetof(SolveBlocks, th) &&
+                  sizeof(pc::KeyChunk32) <= offsetof(SolveBlocks, th),
               "the commit chunk must fit in the inverse scratch of the solve blocks");
 static_assert(sizeof(Smem) <= 81920, "two workgroups per CU");
 
@@ -88,14 +91,20 @@ __device__ __forceinline__ bool path_valid(const PathLanes &p, int m, int max_pa
     return __ballot(bad) == 0ull;
 }
 
+// kU: the previous tree's pseudo-values u_prev are given, so the commit is
+// the rank-m update S <- e^{g_a} S + sum_s e^{g_a - g_s} k_s u_s^T with no
+// solve; otherwise the commit solves for them chunk by chunk.  kUout: the
+// new tree's pseudo-values are written to u_out.
+template <bool kU, bool kUout>
 __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     float *__restrict__ S, const int32_t *__restrict__ path, const int32_t *__restrict__ path_len,
     int max_path, const uint16_t *__restrict__ k_prev, const uint16_t *__restrict__ v_prev,
     const float *__restrict__ alpha_prev, const float *__restrict__ beta_prev,
-    const int32_t *__restrict__ parent_prev, int n_prev, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const float *__restrict__ alpha, const float *__restrict__ beta,
-    const int32_t *__restrict__ parent, float *__restrict__ out, int n, int H, int ncu,
+    const int32_t *__restrict__ parent_prev, const float *__restrict__ u_prev, int n_prev,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const float *__restrict__ alpha,
+    const float *__restrict__ beta, const int32_t *__restrict__ parent,
+    float *__restrict__ out, float *__restrict__ u_out, int n, int H, int ncu,
     int32_t *__restrict__ status) {
     __shared__ Smem sm;
     const Lane c = lane_coords();
@@ -129,18 +138,31 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     // until the memory system has accepted all of it
     f32x16 st[4];
     pc::Rows16 r16;
+    pc::KeyRows32 k32;
     if (c.w == 3) {
         // parents of the path ids (ids out of range fail validation by
         // themselves) and the first chunk's rows and gates
         if (pl.id0 >= 0 && pl.id0 < n_prev) pl.par0 = ppar[pl.id0];
         if (pl.id1 >= 0 && pl.id1 < n_prev) pl.par1 = ppar[pl.id1];
-        const int mc0 = min(pc::kC16, mlen);
-        const int rj = c.l >> 2;
-        const int rid = slot_id(pl, rj);
-        r16 = pc::load_rows16(rid, rj < mc0 && rid >= 0 && rid < n_prev, pl.id0,
-                              c.l < mc0 && pl.id0 >= 0 && pl.id0 < n_prev, k_prev + prow0,
-                              v_prev + prow0, alpha_prev + pgate0, beta_prev + pgate0, H * kD, H,
-                              pbytes, c.l);
+        if constexpr (kU) {
+            // ids for every wave's u loads; the first chunk's keys and gates
+            if (pl.id0 >= 0) sm.pid[c.l] = pl.id0;
+            if (pl.id1 >= 0) sm.pid[64 + c.l] = pl.id1;
+            const int mc0 = min(32, mlen);
+            const int rj = c.l >> 1;
+            const int rid = slot_id(pl, rj);
+            k32 = pc::load_keys32(rid, rj < mc0 && rid >= 0 && rid < n_prev, pl.id0,
+                                  c.l < mc0 && pl.id0 >= 0 && pl.id0 < n_prev, k_prev + prow0,
+                                  alpha_prev + pgate0, H * kD, H, pbytes, c.l);
+        } else {
+            const int mc0 = min(pc::kC16, mlen);
+            const int rj = c.l >> 2;
+            const int rid = slot_id(pl, rj);
+            r16 = pc::load_rows16(rid, rj < mc0 && rid >= 0 && rid < n_prev, pl.id0,
+                                  c.l < mc0 && pl.id0 >= 0 && pl.id0 < n_prev, k_prev + prow0,
+                                  v_prev + prow0, alpha_prev + pgate0, beta_prev + pgate0,
+                                  H * kD, H, pbytes, c.l);
+        }
         topology(c, s, gt, sm.tp, status, false);
         // zero rows for the padded slots of the commit chunk operands
         for (int i = c.l; i < pc::kKP; i += 64) sm.cx.zk[i] = 0;
@@ -151,6 +173,15 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     store_rows(c, rv, sm.b.v);
     load_state_tile(st[0], 0, slab, c.col, c.h);
     lds_barrier();
+
+    // the first chunk's pseudo-values (this wave's columns), in flight
+    // during the tree matrices
+    const float *u_head = u_prev + prow0;
+    const uint32_t ubytes = (uint32_t)((size_t)n_prev * H * kD * 4);
+    f32x16 U0 = {};
+    if constexpr (kU)
+        if (mlen > 0 && mlen <= kMaxPathIds)
+            U0 = pc::load_u_chunk(u_head, ubytes, sm.pid, 0, min(32, mlen), H * kD, c.col, c.h);
 
     // ---- 2. the new tree's Gram, masks and block inverses (no state needed)
     f32x16 gc, ga;
@@ -179,27 +210,51 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             if (s.hd == 0 && status)
                 status[s.b] = (ok ? 0 : kFaultBadPath) | (tree_ok ? 0 : kFaultBadParent);
         }
-        if (ok && mlen > 0) pc::build16(sm.b.ch, sm.cx, r16, min(pc::kC16, mlen), c.l);
+        if (ok && mlen > 0) {
+            if constexpr (kU)
+                pc::build_keys32(sm.b.kc, sm.cx, k32, min(32, mlen), c.l);
+            else
+                pc::build16(sm.b.ch, sm.cx, r16, min(pc::kC16, mlen), c.l);
+        }
     }
     lds_barrier();
     const bool commit = sm.commit_ok && mlen > 0;
     if (commit) {
         bf16x8 ident[2];
         pc::key_identity(ident, c.m, c.h);
-        pc::apply16(sm.b.ch, sm.cx, st, ident, c.m, c.h, c.col);
-        for (int c0 = pc::kC16; c0 < mlen; c0 += pc::kC16) {
-            lds_barrier();   // every wave is done with the previous chunk
-            if (c.w == 3) {
-                const int mc = min(pc::kC16, mlen - c0);
-                const int rj = c.l >> 2;
-                const pc::Rows16 rr = pc::load_rows16(
-                    slot_id(pl, c0 + rj), rj < mc, slot_id(pl, c0 + (c.l & 15)), c.l < mc,
-                    k_prev + prow0, v_prev + prow0, alpha_prev + pgate0, beta_prev + pgate0,
-                    H * kD, H, pbytes, c.l);
-                pc::build16(sm.b.ch, sm.cx, rr, mc, c.l);
+        if constexpr (kU) {
+            pc::apply_known_u(sm.b.kc, sm.cx, U0, st, ident, c.m, c.h);
+            for (int c0 = 32; c0 < mlen; c0 += 32) {
+                const int mc = min(32, mlen - c0);
+                const f32x16 Uc =
+                    pc::load_u_chunk(u_head, ubytes, sm.pid, c0, mc, H * kD, c.col, c.h);
+                lds_barrier();   // every wave is done with the previous chunk
+                if (c.w == 3) {
+                    const int rj = c.l >> 1;
+                    const pc::KeyRows32 kr = pc::load_keys32(
+                        slot_id(pl, c0 + rj), rj < mc, slot_id(pl, c0 + (c.l & 31)), c.l < mc,
+                        k_prev + prow0, alpha_prev + pgate0, H * kD, H, pbytes, c.l);
+                    pc::build_keys32(sm.b.kc, sm.cx, kr, mc, c.l);
+                }
+                lds_barrier();
+                pc::apply_known_u(sm.b.kc, sm.cx, Uc, st, ident, c.m, c.h);
             }
-            lds_barrier();
+        } else {
             pc::apply16(sm.b.ch, sm.cx, st, ident, c.m, c.h, c.col);
+            for (int c0 = pc::kC16; c0 < mlen; c0 += pc::kC16) {
+                lds_barrier();   // every wave is done with the previous chunk
+                if (c.w == 3) {
+                    const int mc = min(pc::kC16, mlen - c0);
+                    const int rj = c.l >> 2;
+                    const pc::Rows16 rr = pc::load_rows16(
+                        slot_id(pl, c0 + rj), rj < mc, slot_id(pl, c0 + (c.l & 15)), c.l < mc,
+                        k_prev + prow0, v_prev + prow0, alpha_prev + pgate0, beta_prev + pgate0,
+                        H * kD, H, pbytes, c.l);
+                    pc::build16(sm.b.ch, sm.cx, rr, mc, c.l);
+                }
+                lds_barrier();
+                pc::apply16(sm.b.ch, sm.cx, st, ident, c.m, c.h, c.col);
+            }
         }
     }
 
@@ -208,14 +263,21 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     if (!tree_ok) {
         if (commit) store_state(st, slab, c.col, c.h);
         store_nan(c, s, out);
+        if constexpr (kUout) store_nan(c, s, u_out);
         return;
     }
     f32x16 P[2], R[2];
     contract(c, sm.a.t, st, P, R, commit ? slab : nullptr);
     lds_barrier();
     f32x16 o0, o1;
-    solve_output(c, sm.tp, sm.b.s, P, R, vpk, o0, o1);
-    store_output(c, s, sm.a.o, o0, o1, out);
+    if constexpr (kUout) {
+        f32x16 u[2];
+        solve_output(c, sm.tp, sm.b.s, P, R, vpk, o0, o1, u);
+        store_output_u(c, s, sm.a.o, o0, o1, out, u[0], u[1], u_out);
+    } else {
+        solve_output(c, sm.tp, sm.b.s, P, R, vpk, o0, o1);
+        store_output(c, s, sm.a.o, o0, o1, out);
+    }
 }
 
 }  // namespace
@@ -227,12 +289,16 @@ bool commit_verify_mfma_supports(const CommitVerifyArgs &a) {
 }
 
 hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(commit_verify_mfma_kernel, dim3((unsigned)(a.v.batch * a.v.H)),
-                       dim3(kThreads), 0, s, a.c.S, a.c.path, a.c.path_len, a.c.max_path,
-                       (const uint16_t *)a.c.k, (const uint16_t *)a.c.v, a.c.alpha, a.c.beta,
-                       a.c.parent, a.c.n, (const uint16_t *)a.v.q, (const uint16_t *)a.v.k,
-                       (const uint16_t *)a.v.v, a.v.alpha, a.v.beta, a.v.parent, a.v.out, a.v.n,
-                       a.v.H, device_cu_count(), a.v.status);
+    auto kern = a.u_prev ? (a.u_out ? commit_verify_mfma_kernel<true, true>
+                                    : commit_verify_mfma_kernel<true, false>)
+                         : (a.u_out ? commit_verify_mfma_kernel<false, true>
+                                    : commit_verify_mfma_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.v.batch * a.v.H)), dim3(kThreads), 0, s, a.c.S,
+                       a.c.path, a.c.path_len, a.c.max_path, (const uint16_t *)a.c.k,
+                       (const uint16_t *)a.c.v, a.c.alpha, a.c.beta, a.c.parent, a.u_prev,
+                       a.c.n, (const uint16_t *)a.v.q, (const uint16_t *)a.v.k,
+                       (const uint16_t *)a.v.v, a.v.alpha, a.v.beta, a.v.parent, a.v.out,
+                       a.u_out, a.v.n, a.v.H, device_cu_count(), a.v.status);
     return hipGetLastError();
 }
 

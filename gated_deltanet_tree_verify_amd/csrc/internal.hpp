@@ -38,6 +38,8 @@ struct CommitArgs {
 struct CommitVerifyArgs {
     CommitArgs c;
     VerifyArgs v;
+    const float *u_prev;   // previous tree's pseudo-values, or null (solve for them)
+    float *u_out;          // this tree's pseudo-values, or null
 };
 
 // number of compute units of the current device (cached per device); only

@@ -286,6 +286,42 @@ struct ChunkView {
     float glast;
 };
 
+// S <- e^{g_last} S + K_p^T W with W_j = e^{g_last - g_j} u_j, for the chunk's
+// pseudo-values U held as a result tile (rows = path slots crow(r, h)).  The
+// key tile of rows 32q.. is put in the result layout by an exact identity
+// product; that layout is the A operand of K_p^T with the path slots in the
+// order W holds them.
+template <int NR>
+__device__ __forceinline__ void apply_update(const ChunkView &cv, const f32x16 &U,
+                                             f32x16 (&st)[4], const bf16x8 (&ident)[2], int h) {
+    constexpr int KS = NR / 16;
+    bf16x8 wh[2], wl[2];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        float wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[j] = cv.wdec[crow(8 * kk + j, h)] * U[8 * kk + j];
+        split8(wv, wh[kk], wl[kk]);
+    }
+    const float gl = cv.glast;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f32x16 kt = {};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) kt = mfma(lds8(cv.kp_row + 32 * q + 16 * kb + 8 * h), ident[kb], kt);
+        f32x16 acc = st[q] * gl;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            bf16x8 a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = static_cast<__bf16>(kt[8 * kk + e]);
+            acc = mfma(a, wh[kk], acc);
+            acc = mfma(a, wl[kk], acc);
+        }
+        st[q] = acc;
+    }
+}
+
 // Apply a prepared chunk of NR (16 or 32) path slots to this wave's state
 // slab (no barrier inside).
 template <int NR>
@@ -330,35 +366,7 @@ __device__ __forceinline__ void apply_rows(const ChunkView &cv, f32x16 (&st)[4],
         U = mfma(ah, bll, U);
         U = mfma(al, bhh, U);
     }
-    bf16x8 wh[2], wl[2];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        float wv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wv[j] = cv.wdec[crow(8 * kk + j, h)] * U[8 * kk + j];
-        split8(wv, wh[kk], wl[kk]);
-    }
-
-    // ---- S <- e^{g_last} S + K_p^T W.  The key tile of rows 32q.. is put
-    // in the result layout by an exact identity product; that layout is
-    // the A operand of K_p^T with the path slots in the order W holds them.
-    const float gl = cv.glast;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        f32x16 kt = {};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kt = mfma(lds8(cv.kp_row + 32 * q + 16 * kb + 8 * h), ident[kb], kt);
-        f32x16 acc = st[q] * gl;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            bf16x8 a;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = static_cast<__bf16>(kt[8 * kk + e]);
-            acc = mfma(a, wh[kk], acc);
-            acc = mfma(a, wl[kk], acc);
-        }
-        st[q] = acc;
-    }
+    apply_update<NR>(cv, U, st, ident, h);
 }
 
 __device__ __forceinline__ void apply_chunk(const ChunkTiles &sm, f32x16 (&st)[4],
@@ -520,6 +528,79 @@ __device__ __forceinline__ void apply16(const Chunk16 &ch, const Chunk16Aux &ax,
                        ax.eg,                  ax.wdec,
                        ax.beta,                ax.glast};
     apply_rows<kC16>(cv, st, ident, h, col);
+}
+
+// ---- commit from known pseudo-values (u_s written by the verify that ran on
+// the same state): S <- e^{g_last} S + K_p^T W per chunk of 32 path slots, no
+// solve.  One wave loads a chunk's keys and gates; every wave loads its own
+// columns of the chunk's u rows.
+struct KeyChunk32 {
+    uint16_t kp[32][kKP];   // path keys, d_k permuted within 16-blocks; zero past the chunk
+};
+
+// lane l holds bytes [128 (l & 1), 128 (l & 1) + 128) of slot l >> 1's key
+// row, and lanes < 32 slot l's log2 decay
+struct KeyRows32 {
+    uint4 k[8];
+    float la;
+};
+
+__device__ __forceinline__ KeyRows32 load_keys32(int row_id, bool row_live, int gate_id,
+                                                 bool gate_live, const uint16_t *k,
+                                                 const float *alpha, int rs, int gs,
+                                                 uint32_t bytes, int l) {
+    KeyRows32 r;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k, bytes);
+    const uint32_t base = row_live ? (uint32_t)(row_id * rs + 64 * (l & 1)) * 2 : bytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.k[i] = load16(kr, row_live ? base + 16 * i : bytes);
+    const int gi = gate_live ? gate_id : 0;
+    const float a = alpha[(size_t)gi * gs];
+    r.la = gate_live ? log2f(a) : 0.f;
+    return r;
+}
+
+// one wave: keys into the chunk tile, decay-to-chunk-end weights and the
+// chunk's total decay (no barrier inside: one wave's LDS accesses are ordered)
+__device__ __forceinline__ void build_keys32(KeyChunk32 &kc, Chunk16Aux &ax, const KeyRows32 &r,
+                                             int mc, int l) {
+    const int j = l >> 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) store_row8_permuted(kc.kp[j], 64 * (l & 1) + 8 * i, r.k[i]);
+    float gs = (l < mc) ? r.la : 0.f;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+        const float t = __shfl_up(gs, o, 32);
+        if ((l & 31) >= o) gs += t;
+    }
+    const float gl = __shfl(gs, mc - 1, 32);
+    if (l < 32) ax.wdec[l] = l < mc ? exp2f(gl - gs) : 0.f;
+    if (l == 0) ax.glast = exp2f(gl);
+}
+
+// this lane's u entries of the chunk's slots crow(r, h) (zero past the chunk):
+// u_head points at node 0 of this (sequence, head) of a [batch][n][H][128]
+// fp32 tensor, rs = H * 128, bytes = n * rs * 4
+__device__ __forceinline__ f32x16 load_u_chunk(const float *u_head, uint32_t bytes, const int *pid,
+                                               int c0, int mc, int rs, int col, int h) {
+    const __amdgpu_buffer_rsrc_t ur = make_rsrc(u_head, bytes);
+    f32x16 U;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int j = crow(r, h);
+        const uint32_t off =
+            j < mc ? (uint32_t)(pid[min(c0 + j, kMaxPath - 1)] * rs + col) * 4 : bytes;
+        U[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ur, (int)off, 0, 0));
+    }
+    return U;
+}
+
+__device__ __forceinline__ void apply_known_u(const KeyChunk32 &kc, const Chunk16Aux &ax,
+                                              const f32x16 &U, f32x16 (&st)[4],
+                                              const bf16x8 (&ident)[2], int m, int h) {
+    const ChunkView cv{kc.kp[m], nullptr, nullptr, nullptr, 0,
+                       nullptr,  ax.wdec, nullptr, ax.glast};
+    apply_update<32>(cv, U, st, ident, h);
 }
 
 }  // namespace pc

@@ -360,11 +360,12 @@ __device__ __forceinline__ void contract(const Lane &c, const QKTiles &t, const 
 }
 
 // right-hand side, tiled forward substitution and output tiles o0 (rows
-// 0..31) and o1 (rows 32..63) of this wave's columns
+// 0..31) and o1 (rows 32..63) of this wave's columns; the pseudo-value tiles
+// too when u_ret is given
 __device__ __forceinline__ void solve_output(const Lane &c, const Topo &tp, const SolveBlocks &sb,
                                              f32x16 (&P)[2], const f32x16 (&R)[2],
                                              const uint32_t (&vpk)[2][8], f32x16 &o0,
-                                             f32x16 &o1) {
+                                             f32x16 &o1, f32x16 *u_ret = nullptr) {
     f32x16 rhs[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -388,6 +389,11 @@ __device__ __forceinline__ void solve_output(const Lane &c, const Topo &tp, cons
     const SplitTile u0s = split_tile(u0);
     const f32x16 z1 = mm3<kBL>(sb.xh, sb.xl, u0s, rhs[1], c.m, c.h);
     const f32x16 u1 = mm3<kBL>(sb.th[1], sb.tl[1], split_tile(z1), zero, c.m, c.h);
+    // the pseudo-values themselves, when asked for (the next commit reuses them)
+    if (u_ret) {
+        u_ret[0] = u0;
+        u_ret[1] = u1;
+    }
     o0 = mm3<kBL>(sb.yh[0], sb.yl[0], u0s, P[0], c.m, c.h);
     o1 = mm3<kBL>(sb.yh[1], sb.yl[1], u0s, P[1], c.m, c.h);
     o1 = mm3<kBL>(sb.yh[2], sb.yl[2], split_tile(u1), o1, c.m, c.h);
@@ -410,6 +416,17 @@ __device__ __forceinline__ void store_output(const Lane &c, const Seq &s, float 
             *reinterpret_cast<float4 *>(out + s.base + row * s.rstride + c4) =
                 *reinterpret_cast<const float4 *>(&ostage[row][c4]);
     }
+}
+
+// The output rows and then the pseudo-value rows, both through the same LDS
+// staging area as whole 512-byte rows.  Contains three barriers.
+__device__ __forceinline__ void store_output_u(const Lane &c, const Seq &s,
+                                               float (*ostage)[kD + 4], const f32x16 &o0,
+                                               const f32x16 &o1, float *out, const f32x16 &u0,
+                                               const f32x16 &u1, float *u_out) {
+    store_output(c, s, ostage, o0, o1, out);
+    lds_barrier();   // every thread has read its output rows from the staging area
+    store_output(c, s, ostage, u0, u1, u_out);
 }
 
 // NaN rows for a sequence whose tree is malformed (this lane's entries)

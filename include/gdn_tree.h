@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 5
+#define GDN_TREE_ABI_VERSION 6
 #define GDN_MAX_NODES 128
 #define GDN_MAX_DIM 128
 #define GDN_MAX_CANDIDATES 32   /* child candidates per node, gdn_tree_build */
@@ -141,21 +141,36 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path,
  * halves' flags: GDN_FAULT_BAD_PATH leaves S[b] bit-unchanged and the
  * verify runs from it; GDN_FAULT_BAD_PARENT (of the new tree) sets that
  * element's out rows to NaN and does not undo its commit.  path_len[b] = 0
- * commits nothing.  out must not alias any input, S must not alias any
- * other argument; the previous-tree tensors may be the same tensors as the
- * new ones.  1 <= n_prev <= GDN_MAX_NODES, 1 <= max_path.
+ * commits nothing.
+ *
+ * Pseudo-values (optional).  The verify solves for u_i = beta_i (v_i -
+ * alpha_i S_p^T k_i) of every node (S_p: the state at i's parent), and the
+ * state after a path is e^{g} S + sum_s e^{g - g_s} k_s u_s^T.  u_out
+ * [batch][n][H][d_v] fp32, when not NULL, receives the new tree's u (NaN
+ * rows for a malformed tree).  u_prev [batch][n_prev][H][d_v], when not
+ * NULL, must be the u_out that the call verifying the previous tree wrote
+ * from this same S: the commit then applies that sum directly instead of
+ * solving again (faster; same result up to rounding).  Other u_prev values
+ * give that sum, not the commit.  The first call of a decode loop passes
+ * path_len = 0 and u_prev = NULL.  u_out needs bf16, d_k = d_v = 128 and
+ * n <= 64 (else GDN_ERR_UNSUPPORTED); u_prev is ignored on other shapes.
+ *
+ * out and u_out must not alias any input, S must not alias any other
+ * argument; the previous-tree tensors may be the same tensors as the new
+ * ones.  1 <= n_prev <= GDN_MAX_NODES, 1 <= max_path.
  */
 gdn_status gdn_tree_commit_verify(float *S, const int32_t *path,
                                   const int32_t *path_len, int max_path,
                                   const void *k_prev, const void *v_prev,
                                   const float *alpha_prev,
                                   const float *beta_prev,
-                                  const int32_t *parent_prev, int n_prev,
+                                  const int32_t *parent_prev,
+                                  const float *u_prev, int n_prev,
                                   const void *q, const void *k, const void *v,
                                   gdn_dtype qkv_dtype, const float *alpha,
                                   const float *beta, const int32_t *parent,
-                                  float *out, int batch, int n, int H,
-                                  int d_k, int d_v, int32_t *status,
+                                  float *out, float *u_out, int batch, int n,
+                                  int H, int d_k, int d_v, int32_t *status,
                                   void *stream);
 
 /*

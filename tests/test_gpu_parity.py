@@ -432,6 +432,81 @@ def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype):
 
 
 # ---------------------------------------------------------------------------
+# fused step with pseudo-values carried from one call to the next
+# ---------------------------------------------------------------------------
+def test_commit_verify_pseudo_values_decode_loop(gpu_lib):
+    """call 1 verifies tree A (no commit) and writes its u; call 2 commits
+    A's accepted path from that u (no solve) and verifies tree B; every
+    output against the oracle"""
+    say("commit-verify with pseudo-values")
+    A, B = gs.make_config(2, s=5), gs.make_config(2, s=6)
+    dA, dB = upload(A), upload(B)
+    S = dA["S0"].clone()
+    prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
+    uA = torch.full(dA["v"].shape, 7.0, dtype=torch.float32, device="cuda")
+    uB = torch.full(dB["v"].shape, 7.0, dtype=torch.float32, device="cuda")
+    st = torch.full((16,), -7, dtype=torch.int32, device="cuda")
+    zero = dev(np.zeros(16, np.int32))
+    pathA, plenA = A.paths(max_path=13)
+    outA = gpu_lib.commit_verify(S, dev(pathA), zero, prevA, dA["q"], dA["k"], dA["v"],
+                                 dA["alpha"], dA["beta"], dA["parent"], u_out=uA, status=st)
+    torch.cuda.synchronize()
+    refA, _ = oracle.verify_set(A)
+    UA, _ = oracle.pseudo_set(A)
+    assert host(st).tolist() == [0] * 16 and torch.equal(S, dA["S0"])
+    assert oracle.rel_err(host(outA), refA) <= BF16_GATE
+    eu = oracle.rel_err(host(uA), UA)
+    say("u rel err", eu)
+    assert eu <= BF16_GATE
+    outB = gpu_lib.commit_verify(S, dev(pathA), dev(plenA), prevA, dB["q"], dB["k"], dB["v"],
+                                 dB["alpha"], dB["beta"], dB["parent"], u_prev=uA, u_out=uB,
+                                 status=st)
+    torch.cuda.synchronize()
+    oref, Sref, rst = oracle_commit_verify(A, B, pathA, plenA)
+    UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert host(st).tolist() == rst.tolist() == [0] * 16
+    es, eo, eu = (oracle.rel_err(host(S), Sref), oracle.rel_err(host(outB), oref),
+                  oracle.rel_err(host(uB), UB))
+    say("rel err S", es, "out", eo, "u", eu)
+    assert es <= BF16_GATE and eo <= BF16_GATE and eu <= BF16_GATE
+
+
+def test_commit_verify_pseudo_values_long_path_and_faults(gpu_lib):
+    """a 64-node chain (two 32-slot chunks of known u), a bad path (state
+    untouched) and a malformed new tree (NaN outputs and u)"""
+    chain = gs.chain_tree(64)
+    rng = np.random.default_rng(31)
+    pcur = np.stack([gs.random_recursive_tree(rng, 40, max_depth=9) for _ in range(3)])
+    A = gs.make_set(np.stack([chain] * 3), 2, 128, 128, "bf16", seed=31,
+                    accepted=np.full(3, 63, np.int32))
+    B = gs.make_set(pcur, 2, 128, 128, "bf16", seed=32)
+    B.parent[2, 10] = 20
+    dA, dB = upload(A), upload(B)
+    S = dA["S0"].clone()
+    prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
+    uA = torch.empty(dA["v"].shape, dtype=torch.float32, device="cuda")
+    uB = torch.empty(dB["v"].shape, dtype=torch.float32, device="cuda")
+    path, plen = A.paths(max_path=64)
+    gpu_lib.commit_verify(S, dev(path), dev(np.zeros(3, np.int32)), prevA, dA["q"], dA["k"],
+                          dA["v"], dA["alpha"], dA["beta"], dA["parent"], u_out=uA)
+    path[1, 5] = 70                                   # sequence 1: invalid path
+    st = torch.full((3,), -7, dtype=torch.int32, device="cuda")
+    outB = gpu_lib.commit_verify(S, dev(path), dev(plen), prevA, dB["q"], dB["k"], dB["v"],
+                                 dB["alpha"], dB["beta"], dB["parent"], u_prev=uA, u_out=uB,
+                                 status=st)
+    torch.cuda.synchronize()
+    oref, Sref, rst = oracle_commit_verify(A, B, path, plen)
+    assert host(st).tolist() == rst.tolist() == [0, 2, 1]
+    Sh, oh, uh = host(S), host(outB), host(uB)
+    assert np.array_equal(Sh[1], A.S0[1])
+    assert oracle.rel_err(Sh[[0, 2]], Sref[[0, 2]]) <= BF16_GATE
+    assert oracle.rel_err(oh[[0, 1]], oref[[0, 1]]) <= BF16_GATE
+    assert np.isnan(oh[2]).all() and np.isnan(uh[2]).all()
+    UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert oracle.rel_err(uh[[0, 1]], UB[[0, 1]]) <= BF16_GATE
+
+
+# ---------------------------------------------------------------------------
 # width-w best-first tree construction: bit-exact (fp32 score order)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("batch,n,K,w,md", [(16, 64, 8, 8, 12), (4, 128, 32, 16, 16),
