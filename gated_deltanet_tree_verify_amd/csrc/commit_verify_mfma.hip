@@ -269,15 +269,14 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     f32x16 P[2], R[2];
     contract(c, sm.a.t, st, P, R, commit ? slab : nullptr);
     lds_barrier();
-    f32x16 o0, o1;
-    if constexpr (kUout) {
-        f32x16 u[2];
-        solve_output(c, sm.tp, sm.b.s, P, R, vpk, o0, o1, u);
-        store_output_u(c, s, sm.a.o, o0, o1, out, u[0], u[1], u_out);
-    } else {
-        solve_output(c, sm.tp, sm.b.s, P, R, vpk, o0, o1);
-        store_output(c, s, sm.a.o, o0, o1, out);
-    }
+    // the first block's rows leave while the second block is solved
+    SolveCarry cy;
+    f32x16 u0, o0, u1, o1;
+    solve_block0(c, sm.tp, sm.b.s, P, R, vpk, u0, o0, cy);
+    store_block<kUout>(c, s, sm.a.o, o0, out, u0, u_out, 0);
+    solve_block1(c, sm.b.s, P, cy, u1, o1);
+    lds_barrier();   // every thread has read the first block from the staging area
+    store_block<kUout>(c, s, sm.a.o, o1, out, u1, u_out, 32);
 }
 
 }  // namespace

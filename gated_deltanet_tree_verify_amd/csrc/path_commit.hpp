@@ -590,7 +590,7 @@ __device__ __forceinline__ f32x16 load_u_chunk(const float *u_head, uint32_t byt
         const int j = crow(r, h);
         const uint32_t off =
             j < mc ? (uint32_t)(pid[min(c0 + j, kMaxPath - 1)] * rs + col) * 4 : bytes;
-        U[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ur, (int)off, 0, 0));
+        U[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ur, (int)off, 0, kNT));
     }
     return U;
 }

@@ -359,13 +359,21 @@ __device__ __forceinline__ void contract(const Lane &c, const QKTiles &t, const 
     }
 }
 
-// right-hand side, tiled forward substitution and output tiles o0 (rows
-// 0..31) and o1 (rows 32..63) of this wave's columns; the pseudo-value tiles
-// too when u_ret is given
-__device__ __forceinline__ void solve_output(const Lane &c, const Topo &tp, const SolveBlocks &sb,
+// The solve in two halves, one per 32-row block, so that the first block's
+// rows can be stored while the second block is still being solved.
+// solve_block0: right-hand sides of both blocks (block 1's kept in the
+// carry), U_0 = T_0 RHS_0 and O_0 = e^g P_0 + Y_00 U_0; P is scaled by e^g
+// in place.  solve_block1: U_1 = T_1 (RHS_1 - X_10 U_0) and
+// O_1 = e^g P_1 + Y_10 U_0 + Y_11 U_1.
+struct SolveCarry {
+    f32x16 rhs1;
+    SplitTile u0s;
+};
+
+__device__ __forceinline__ void solve_block0(const Lane &c, const Topo &tp, const SolveBlocks &sb,
                                              f32x16 (&P)[2], const f32x16 (&R)[2],
-                                             const uint32_t (&vpk)[2][8], f32x16 &o0,
-                                             f32x16 &o1, f32x16 *u_ret = nullptr) {
+                                             const uint32_t (&vpk)[2][8], f32x16 &u0,
+                                             f32x16 &o0, SolveCarry &cy) {
     f32x16 rhs[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -385,18 +393,32 @@ __device__ __forceinline__ void solve_output(const Lane &c, const Topo &tp, cons
             }
         }
     const f32x16 zero = {};
-    const f32x16 u0 = mm3<kBL>(sb.th[0], sb.tl[0], split_tile(rhs[0]), zero, c.m, c.h);
-    const SplitTile u0s = split_tile(u0);
-    const f32x16 z1 = mm3<kBL>(sb.xh, sb.xl, u0s, rhs[1], c.m, c.h);
-    const f32x16 u1 = mm3<kBL>(sb.th[1], sb.tl[1], split_tile(z1), zero, c.m, c.h);
-    // the pseudo-values themselves, when asked for (the next commit reuses them)
-    if (u_ret) {
-        u_ret[0] = u0;
-        u_ret[1] = u1;
-    }
-    o0 = mm3<kBL>(sb.yh[0], sb.yl[0], u0s, P[0], c.m, c.h);
-    o1 = mm3<kBL>(sb.yh[1], sb.yl[1], u0s, P[1], c.m, c.h);
+    u0 = mm3<kBL>(sb.th[0], sb.tl[0], split_tile(rhs[0]), zero, c.m, c.h);
+    cy.u0s = split_tile(u0);
+    cy.rhs1 = rhs[1];
+    o0 = mm3<kBL>(sb.yh[0], sb.yl[0], cy.u0s, P[0], c.m, c.h);
+}
+
+__device__ __forceinline__ void solve_block1(const Lane &c, const SolveBlocks &sb,
+                                             const f32x16 (&P)[2], const SolveCarry &cy,
+                                             f32x16 &u1, f32x16 &o1) {
+    const f32x16 zero = {};
+    const f32x16 z1 = mm3<kBL>(sb.xh, sb.xl, cy.u0s, cy.rhs1, c.m, c.h);
+    u1 = mm3<kBL>(sb.th[1], sb.tl[1], split_tile(z1), zero, c.m, c.h);
+    o1 = mm3<kBL>(sb.yh[1], sb.yl[1], cy.u0s, P[1], c.m, c.h);
     o1 = mm3<kBL>(sb.yh[2], sb.yl[2], split_tile(u1), o1, c.m, c.h);
+}
+
+// right-hand side, tiled forward substitution and output tiles o0 (rows
+// 0..31) and o1 (rows 32..63) of this wave's columns
+__device__ __forceinline__ void solve_output(const Lane &c, const Topo &tp, const SolveBlocks &sb,
+                                             f32x16 (&P)[2], const f32x16 (&R)[2],
+                                             const uint32_t (&vpk)[2][8], f32x16 &o0,
+                                             f32x16 &o1) {
+    SolveCarry cy;
+    f32x16 u0, u1;
+    solve_block0(c, tp, sb, P, R, vpk, u0, o0, cy);
+    solve_block1(c, sb, P, cy, u1, o1);
 }
 
 // Output rows through LDS (ostage aliases dead tiles), then stored as whole
@@ -413,20 +435,34 @@ __device__ __forceinline__ void store_output(const Lane &c, const Seq &s, float 
     for (int it = 0; it < 8; ++it) {
         const int e = c.tid + kThreads * it, row = e >> 5, c4 = (e & 31) * 4;
         if (row < s.n)
-            *reinterpret_cast<float4 *>(out + s.base + row * s.rstride + c4) =
-                *reinterpret_cast<const float4 *>(&ostage[row][c4]);
+            store16(out + s.base + row * s.rstride + c4,
+                    *reinterpret_cast<const float4 *>(&ostage[row][c4]));
     }
 }
 
-// The output rows and then the pseudo-value rows, both through the same LDS
-// staging area as whole 512-byte rows.  Contains three barriers.
-__device__ __forceinline__ void store_output_u(const Lane &c, const Seq &s,
-                                               float (*ostage)[kD + 4], const f32x16 &o0,
-                                               const f32x16 &o1, float *out, const f32x16 &u0,
-                                               const f32x16 &u1, float *u_out) {
-    store_output(c, s, ostage, o0, o1, out);
-    lds_barrier();   // every thread has read its output rows from the staging area
-    store_output(c, s, ostage, u0, u1, u_out);
+// Rows row0 .. row0 + 31 of one or two [batch][n][H][128] fp32 outputs, from
+// a 32-row result tile each, through LDS as whole 512-byte rows: tile a goes
+// to dst_a through staging rows 0..31, tile b (when kPair) to dst_b through
+// rows 32..63.  Contains one barrier; the staging area must be free.
+template <bool kPair>
+__device__ __forceinline__ void store_block(const Lane &c, const Seq &s, float (*ostage)[kD + 4],
+                                            const f32x16 &a, float *dst_a, const f32x16 &b,
+                                            float *dst_b, int row0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        ostage[crow(r, c.h)][c.col] = a[r];
+        if constexpr (kPair) ostage[32 + crow(r, c.h)][c.col] = b[r];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int it = 0; it < (kPair ? 8 : 4); ++it) {
+        const int e = c.tid + kThreads * it, row = e >> 5, c4 = (e & 31) * 4;
+        const int node = row0 + (row & 31);
+        float *dst = (kPair && row >= 32) ? dst_b : dst_a;
+        if (node < s.n)
+            store16(dst + s.base + node * s.rstride + c4,
+                    *reinterpret_cast<const float4 *>(&ostage[row][c4]));
+    }
 }
 
 // NaN rows for a sequence whose tree is malformed (this lane's entries)

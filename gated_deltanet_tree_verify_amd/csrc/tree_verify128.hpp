@@ -329,7 +329,8 @@ __device__ __forceinline__ void store_out(const Lane &c, const Seq &s, int hf,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 64 * hf + 32 * t + crow(r, c.h);
-            if (i < s.n) orow[(size_t)i * s.rstride] = o[t][r];
+            const float x = o[t][r];
+            if (i < s.n) __builtin_nontemporal_store(x, orow + (size_t)i * s.rstride);
         }
 }
 
