@@ -132,7 +132,6 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     uint4 rq[4], rk[4], rv[4];
     load_rows(c, s, q, rq);
     load_rows(c, s, k, rk);
-    load_rows(c, s, v, rv);
     // the state slab is requested one 32-row tile at a time, between the
     // tree-matrix phases: a wave that issues a whole 64 KiB slab stalls
     // until the memory system has accepted all of it
@@ -170,9 +169,12 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     }
     store_rows_permuted(c, rq, sm.a.t.q);
     store_rows_permuted(c, rk, sm.a.t.k);
-    store_rows(c, rv, sm.b.v);
+    // v only once q and k are in: every workgroup's Gram operands are
+    // fetched before any of the bulk behind them
+    load_rows(c, s, v, rv);
     load_state_tile(st[0], 0, slab, c.col, c.h);
     lds_barrier();
+    load_state_tile(st[1], 1, slab, c.col, c.h);
 
     // the first chunk's pseudo-values (this wave's columns), in flight
     // during the tree matrices
@@ -186,20 +188,21 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     // ---- 2. the new tree's Gram, masks and block inverses (no state needed)
     f32x16 gc, ga;
     if (c.w < 3) gram(c, sm.a.t, gc, ga);
+    store_rows(c, rv, sm.b.v);
+    lds_barrier();
     uint32_t vpk[2][8];
     v_to_regs(c, sm.b.v, vpk);
-    load_state_tile(st[1], 1, slab, c.col, c.h);
+    load_state_tile(st[2], 2, slab, c.col, c.h);
     lds_barrier();
     const bool tree_ok = !sm.tp.bad;
     if (tree_ok) {
         if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
-        load_state_tile(st[2], 2, slab, c.col, c.h);
+        load_state_tile(st[3], 3, slab, c.col, c.h);
         lds_barrier();
         inverse(c, sm.b.s);
     } else {
-        load_state_tile(st[2], 2, slab, c.col, c.h);
+        load_state_tile(st[3], 3, slab, c.col, c.h);
     }
-    load_state_tile(st[3], 3, slab, c.col, c.h);
     lds_barrier();   // the inverse scratch is free from here on
 
     // ---- 3. commit: wave 3 validates the path and prepares the first chunk

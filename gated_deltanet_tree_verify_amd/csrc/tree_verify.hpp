@@ -258,7 +258,17 @@ __device__ __forceinline__ void mask(const Lane &c, const Topo &tp, const f32x16
 // Z_b = B_b A_b^{-1}, L_b = -C_b^{-1} Z_b, then T_b = [[A^-1, 0], [L, C^-1]]
 // as bf16 hi/lo operand rows.  Starts and ends with the caller's barriers
 // around it; contains three of its own.
+// The two parts of inverse(): the substitution is wave 3's alone, so the
+// other waves may do other work (issue loads) in between.
+__device__ __forceinline__ void inverse_subst(const Lane &c, SolveBlocks &sb);
+__device__ __forceinline__ void inverse_finish(const Lane &c, SolveBlocks &sb);
+
 __device__ __forceinline__ void inverse(const Lane &c, SolveBlocks &sb) {
+    inverse_subst(c, sb);
+    inverse_finish(c, sb);
+}
+
+__device__ __forceinline__ void inverse_subst(const Lane &c, SolveBlocks &sb) {
     if (c.w == 3) {
         const int sbk = c.l >> 4, col = c.l & 15, blk = sbk >> 1, o16 = 16 * (sbk & 1);
         float t[16];
@@ -278,6 +288,9 @@ __device__ __forceinline__ void inverse(const Lane &c, SolveBlocks &sb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sb.tinv[sbk][r][col] = t[r];
     }
+}
+
+__device__ __forceinline__ void inverse_finish(const Lane &c, SolveBlocks &sb) {
     lds_barrier();
     // Z_b into the upper-left sub-block of d[b] (read only by the substitution)
 #pragma unroll
