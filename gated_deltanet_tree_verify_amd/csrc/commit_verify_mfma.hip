@@ -270,6 +270,11 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
         return;
     }
     f32x16 P[2], R[2];
+    // Every state load has landed by now (the commit consumed the tiles),
+    // but the compiler cannot see that on the no-commit path and would wait
+    // on the memory counter inside the contraction, i.e. for the slab
+    // stores issued there.  One explicit wait here settles it.
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
     contract(c, sm.a.t, st, P, R, commit ? slab : nullptr);
     lds_barrier();
     // the first block's rows leave while the second block is solved

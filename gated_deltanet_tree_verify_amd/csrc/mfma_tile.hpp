@@ -149,6 +149,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // same cache space (measured: a step's memory traffic finishes ~25% sooner).
 constexpr int kNT = 2;
 
+// s_waitcnt operand that waits for the vector memory counter alone to reach
+// zero (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt
+// 11:8 left at their maxima)
+constexpr int kVmcntZero = 0x0F70;
+
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNT));
 }
