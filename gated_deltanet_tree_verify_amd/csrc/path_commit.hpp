@@ -398,7 +398,7 @@ struct Chunk16Aux {
 
 // A chunk's rows in the registers of the wave that prepares it: lane l holds
 // bytes [64 (l & 3), 64 (l & 3) + 64) of slot l >> 2's key and value rows,
-// and lanes < 16 hold slot l's gates.
+// and lanes < 16 hold slot l's gates (la = alpha itself).
 struct Rows16 {
     uint4 k[4], v[4];
     float la, bt;
@@ -422,8 +422,11 @@ __device__ __forceinline__ Rows16 load_rows16(int row_id, bool row_live, int gat
     }
     const int gi = gate_live ? gate_id : 0;
     const float a = alpha[(size_t)gi * gs], be = beta[(size_t)gi * gs];
-    r.la = gate_live ? log2f(a) : 0.f;
-    r.bt = gate_live ? be : 0.f;
+    // raw values: the build masks slots past the chunk and takes the log2,
+    // so nothing here makes the wave wait for the loads issued before these
+    // (a slot whose gate is not live belongs to a path the build never sees)
+    r.la = a;
+    r.bt = be;
     return r;
 }
 
@@ -444,7 +447,7 @@ __device__ __forceinline__ void build16(Chunk16 &ch, Chunk16Aux &ax, const Rows1
     }
     // inclusive prefix of the log2 decays over the chunk (slots past mc: 0)
     {
-        float gs = (l < mc) ? r.la : 0.f;
+        float gs = (l < mc) ? log2f(r.la) : 0.f;
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) {
             const float t = __shfl_up(gs, o, 32);
@@ -539,7 +542,7 @@ struct KeyChunk32 {
 };
 
 // lane l holds bytes [128 (l & 1), 128 (l & 1) + 128) of slot l >> 1's key
-// row, and lanes < 32 slot l's log2 decay
+// row, and lanes < 32 slot l's decay alpha
 struct KeyRows32 {
     uint4 k[8];
     float la;
@@ -556,7 +559,7 @@ __device__ __forceinline__ KeyRows32 load_keys32(int row_id, bool row_live, int 
     for (int i = 0; i < 8; ++i) r.k[i] = load16(kr, row_live ? base + 16 * i : bytes);
     const int gi = gate_live ? gate_id : 0;
     const float a = alpha[(size_t)gi * gs];
-    r.la = gate_live ? log2f(a) : 0.f;
+    r.la = a;   // masked and log2'd at build time (see load_rows16)
     return r;
 }
 
@@ -567,7 +570,7 @@ __device__ __forceinline__ void build_keys32(KeyChunk32 &kc, Chunk16Aux &ax, con
     const int j = l >> 1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) store_row8_permuted(kc.kp[j], 64 * (l & 1) + 8 * i, r.k[i]);
-    float gs = (l < mc) ? r.la : 0.f;
+    float gs = (l < mc) ? log2f(r.la) : 0.f;
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
         const float t = __shfl_up(gs, o, 32);
