@@ -341,31 +341,41 @@ __device__ __forceinline__ void inverse_finish(const Lane &c, SolveBlocks &sb) {
     }
 }
 
-// P = Q S0 and R = K S0 for this wave's 32 columns; the state slab (four
-// result tiles of S0 rows) is the B operand, split hi/lo
+// One state tile's share of P = Q S0 and R = K S0 for this wave's 32
+// columns: tile q holds rows 32 q .. 32 q + 31 of S0, i.e. contraction
+// indices 32 q .. 32 q + 31; it enters as the B operand, split hi/lo.  P and
+// R accumulate, so the tiles may be taken one at a time as they arrive;
+// taken in order 0..3 the sums are the same as contract()'s.
+__device__ __forceinline__ void contract_tile(const Lane &c, const QKTiles &t, const f32x16 &stq,
+                                              int q, f32x16 (&P)[2], f32x16 (&R)[2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        float sv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] = stq[8 * kk + j];
+        bf16x8 sh, sl;
+        split8(sv, sh, sl);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const bf16x8 aq = lds8(&t.q[32 * tt + c.m][32 * q + 16 * kk + 8 * c.h]);
+            const bf16x8 ak = lds8(&t.k[32 * tt + c.m][32 * q + 16 * kk + 8 * c.h]);
+            P[tt] = mfma(aq, sh, P[tt]);
+            P[tt] = mfma(aq, sl, P[tt]);
+            R[tt] = mfma(ak, sh, R[tt]);
+            R[tt] = mfma(ak, sl, R[tt]);
+        }
+    }
+}
+
+// P = Q S0 and R = K S0 for this wave's 32 columns from the whole slab
+// (four result tiles of S0 rows)
 __device__ __forceinline__ void contract(const Lane &c, const QKTiles &t, const f32x16 (&st)[4],
                                          f32x16 (&P)[2], f32x16 (&R)[2],
                                          float *store_slab = nullptr) {
     P[0] = P[1] = R[0] = R[1] = f32x16{};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float sv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sv[j] = st[q][8 * kk + j];
-            bf16x8 sh, sl;
-            split8(sv, sh, sl);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const bf16x8 aq = lds8(&t.q[32 * tt + c.m][32 * q + 16 * kk + 8 * c.h]);
-                const bf16x8 ak = lds8(&t.k[32 * tt + c.m][32 * q + 16 * kk + 8 * c.h]);
-                P[tt] = mfma(aq, sh, P[tt]);
-                P[tt] = mfma(aq, sl, P[tt]);
-                R[tt] = mfma(ak, sh, R[tt]);
-                R[tt] = mfma(ak, sl, R[tt]);
-            }
-        }
+        contract_tile(c, t, st[q], q, P, R);
         // optionally write the state tile back as soon as it has been read,
         // spreading the slab's stores over the contraction
         if (store_slab) store_state_tile(st[q], q, store_slab, c.col, c.h);
