@@ -15,8 +15,10 @@
 // One wave per sequence.  Every table row is sorted once (descending score,
 // ties by slot) into LDS, so a node's best remaining candidate is the head
 // of its sorted row: the heap becomes "best head over the live nodes", one
-// wave-wide argmax per popped candidate.  Lane l owns nodes l and 64 + l and
-// keeps their head value in registers.
+// wave-wide maximum per popped candidate.  Lane l owns nodes l and 64 + l
+// and keeps their heads, and the entries after them, in registers; a
+// candidate is one 64-bit word whose unsigned order is the pop order, so the
+// maximum is one compare per DPP step.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -26,51 +28,68 @@ namespace {
 constexpr int kMaxN = GDN_MAX_NODES;
 constexpr int kMaxK = GDN_MAX_CANDIDATES;
 
-struct Cand {
-    float v;   // score of the node's best remaining candidate (-inf: none)
-    int key;   // node * 64 + original slot (ties: lower key first)
-};
-
-__device__ __forceinline__ bool better(float v, int key, float bv, int bkey) {
-    return v > bv || (v == bv && key < bkey);
+// A candidate as one 64-bit word whose unsigned order is the pop order:
+// the high half is the score mapped to an order-preserving integer (higher
+// score, larger word), the low half (8191 - key) << 8 | depth, so a lower key
+// (node * 64 + original slot, the earlier push) wins a tie; the depth of the
+// proposing node rides along in the low byte (keys are unique, so it never
+// decides).  0 means "no candidate": every real score maps above it.
+__device__ __forceinline__ unsigned long long pack(float v, int key, int dep) {
+    const uint32_t b = __float_as_uint(v + 0.f);   // -0 -> +0: equal scores, equal words
+    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((unsigned long long)o << 32) | ((uint32_t)(8191 - key) << 8) | (uint32_t)dep;
 }
 
-// one DPP step of the wave-wide (value, key) maximum: take the candidate the
-// DPP pattern moves into this lane when it is better (lanes with no source
-// see the (-inf, max) sentinel)
+__device__ __forceinline__ float unpack_score(unsigned long long w) {
+    const uint32_t o = (uint32_t)(w >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// one DPP step of the wave-wide maximum of a 64-bit word (lanes with no
+// source see 0, the identity)
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_best(float &bv, int &bk) {
-    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(
-        (int)0xff800000, __float_as_int(bv), CTRL, ROW_MASK, 0xf, false));
-    const int ok = __builtin_amdgcn_update_dpp(0x7fffffff, bk, CTRL, ROW_MASK, 0xf, false);
-    if (better(ov, ok, bv, bk)) {
-        bv = ov;
-        bk = ok;
-    }
+__device__ __forceinline__ unsigned long long dpp_max(unsigned long long x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROW_MASK,
+                                                              0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL,
+                                                              ROW_MASK, 0xf, false);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    return o > x ? o : x;
 }
 
-// best (value, key) over the wave, returned uniform: row_shr 1, 2, 4, 8 leave
-// each 16-lane row's best in its lane 15; row_bcast 15 and 31 carry those
+// maximum over the wave, returned uniform: row_shr 1, 2, 4, 8 leave each
+// 16-lane row's maximum in its lane 15; row_bcast 15 and 31 carry those
 // into lane 63, which is read out
-__device__ __forceinline__ void wave_best(float &bv, int &bk) {
-    dpp_best<0x111, 0xf>(bv, bk);
-    dpp_best<0x112, 0xf>(bv, bk);
-    dpp_best<0x114, 0xf>(bv, bk);
-    dpp_best<0x118, 0xf>(bv, bk);
-    dpp_best<0x142, 0xa>(bv, bk);
-    dpp_best<0x143, 0xc>(bv, bk);
-    bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 63));
-    bk = __builtin_amdgcn_readlane(bk, 63);
+__device__ __forceinline__ unsigned long long wave_max(unsigned long long x) {
+    x = dpp_max<0x111, 0xf>(x);
+    x = dpp_max<0x112, 0xf>(x);
+    x = dpp_max<0x114, 0xf>(x);
+    x = dpp_max<0x118, 0xf>(x);
+    x = dpp_max<0x142, 0xa>(x);
+    x = dpp_max<0x143, 0xc>(x);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
 }
+
+// One tree node owned by a lane.  x / j: log-probability and original slot
+// of its best remaining candidate (the head of its sorted row); xn / jn: the
+// entry after it, read ahead so that advancing the head waits for no LDS.
+struct Node {
+    bool live;
+    int head, dep, par, slot;
+    float sc, x, xn;
+    int j, jn;
+};
 
 __global__ __launch_bounds__(64) void tree_build_kernel(
     const float *__restrict__ cand_logp, const int32_t *__restrict__ cand_tok,
     const int32_t *__restrict__ root_tok, int32_t *__restrict__ parent_out,
     int32_t *__restrict__ token_out, float *__restrict__ score_out,
     int32_t *__restrict__ n_built_out, int n, int K, int width, int max_depth) {
-    __shared__ float s_lp[kMaxN][kMaxK];          // sorted log-probs of each row
-    __shared__ unsigned char s_j[kMaxN][kMaxK];   // their original slots
-    __shared__ float s_raw[kMaxN * kMaxK];        // the table as read
+    __shared__ float s_lp[kMaxN][kMaxK + 2];          // sorted log-probs of each row, -inf padded
+    __shared__ unsigned char s_j[kMaxN][kMaxK + 2];   // their original slots
+    __shared__ float s_raw[kMaxN * kMaxK];            // the table as read
     const int b = blockIdx.x, l = threadIdx.x;
     const float *lp = cand_logp + (size_t)b * n * K;
 
@@ -80,45 +99,82 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    for (int e = l; e < n * K; e += 64) {
-        const int i = e / K, j = e % K;
-        const float v = s_raw[e];
-        const bool fin = isfinite(v);
-        int rank = 0;
-        for (int t = 0; t < K; ++t) {
-            const float u = s_raw[i * K + t];
-            const bool ufin = isfinite(u);
-            // finite slots first, by descending value, ties by slot
-            if (ufin && (!fin || u > v || (u == v && t < j))) ++rank;
-            else if (!ufin && !fin && t < j) ++rank;
+    // lane l sorts rows l and 64 + l: slot j's rank is the number of slots
+    // whose sort word is larger.  The word orders finite slots first, by
+    // descending value, then by slot; non-finite slots after them, by slot.
+    auto sort_word = [](float v, int j) -> unsigned long long {
+        const uint32_t b = __float_as_uint(v + 0.f);   // -0 -> +0
+        const uint32_t o = isfinite(v) ? ((b & 0x80000000u) ? ~b : (b | 0x80000000u)) : 0u;
+        return ((unsigned long long)o << 32) | (uint32_t)(255 - j);
+    };
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = 64 * u + l;
+        const bool row = i < n;
+        unsigned long long w[kMaxK];
+#pragma unroll
+        for (int t = 0; t < kMaxK; ++t)
+            w[t] = (t < K && row) ? sort_word(s_raw[i * K + t], t) : 0ull;
+        for (int j = 0; j < K; ++j) {
+            const float vj = row ? s_raw[i * K + j] : 0.f;
+            const unsigned long long wj = sort_word(vj, j);
+            int rank = 0;
+#pragma unroll
+            for (int t = 0; t < kMaxK; ++t)
+                if (t < K) rank += w[t] > wj ? 1 : 0;   // K is uniform
+            if (row) {
+                s_lp[i][rank] = isfinite(vj) ? vj : -INFINITY;
+                s_j[i][rank] = (unsigned char)j;
+            }
         }
-        s_lp[i][rank] = fin ? v : -INFINITY;
-        s_j[i][rank] = (unsigned char)j;
+    }
+    // two -inf entries past the end of every row, so reading ahead of the
+    // head never leaves the row
+    for (int i = l; i < n; i += 64) {
+        s_lp[i][K] = s_lp[i][K + 1] = -INFINITY;
+        s_j[i][K] = s_j[i][K + 1] = 0;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-    // ---- per node (two per lane): live flag, head, depth, score, parent, slot
-    bool live[2] = {false, false};
-    int head[2] = {0, 0}, dep[2] = {0, 0}, par[2] = {-1, -1}, slot[2] = {-1, -1};
-    float sc[2] = {0.f, 0.f};
-    Cand cur[2];
-    auto refresh = [&](int u) {
+    // ---- lane l owns nodes l (u = 0) and 64 + l (u = 1)
+    Node nd[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) nd[u] = Node{false, 0, 0, -1, -1, 0.f, -INFINITY, -INFINITY, 0, 0};
+    // the candidate word of node u (0: none): live, below the depth cap and
+    // with a finite head
+    auto cand = [&](int u) -> unsigned long long {
+        const Node &d = nd[u];
         const int i = 64 * u + l;
-        cur[u].v = -INFINITY;
-        cur[u].key = 0x7fffffff;
-        if (live[u] && dep[u] + 1 <= max_depth && head[u] < K && i < n) {
-            const float x = s_lp[i][head[u]];
-            if (x != -INFINITY) {
-                cur[u].v = sc[u] + x;   // one fp32 addition, parent score first
-                cur[u].key = i * 64 + s_j[i][head[u]];
-            }
+        if (!d.live || d.dep + 1 > max_depth || d.x == -INFINITY) return 0ull;
+        return pack(d.sc + d.x, i * 64 + d.j, d.dep);   // one fp32 addition, parent score first
+    };
+    // node u becomes live with its head at slot rank 0
+    auto make_live = [&](int u) {
+        const int i = 64 * u + l;
+        nd[u].live = i < n;
+        nd[u].head = 0;
+        if (i < n) {
+            nd[u].x = s_lp[i][0];
+            nd[u].j = s_j[i][0];
+            nd[u].xn = s_lp[i][1];
+            nd[u].jn = s_j[i][1];
         }
     };
-    if (l == 0) live[0] = true;   // node 0: the root, score 0, depth 0
-    refresh(0);
-    refresh(1);
+    // node u's head moves one rank on; the entry after it is read ahead
+    auto advance = [&](int u) {
+        const int i = 64 * u + l;
+        Node &d = nd[u];
+        ++d.head;
+        d.x = d.xn;
+        d.j = d.jn;
+        const int r = min(d.head + 1, K + 1);
+        d.xn = s_lp[i][r];
+        d.jn = s_j[i][r];
+    };
+    if (l == 0) make_live(0);   // node 0: the root, score 0, depth 0
+    unsigned long long c0 = cand(0), c1 = cand(1);
 
     int nn = 1;
     bool dry = false;
@@ -126,41 +182,43 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
         const int cnt = min(width, n - nn);
         int popped = 0;
         for (; popped < cnt; ++popped) {
-            // best head over the live nodes
-            float bv = cur[0].v;
-            int bk = cur[0].key;
-            if (better(cur[1].v, cur[1].key, bv, bk)) { bv = cur[1].v; bk = cur[1].key; }
-            wave_best(bv, bk);
-            if (bv == -INFINITY) break;   // nothing left this round
-            const int pnode = bk >> 6, pslot = bk & 63;
+            const unsigned long long best = wave_max(c0 > c1 ? c0 : c1);
+            if (best == 0ull) break;   // nothing left this round
+            const int key = 8191 - (int)(((uint32_t)best >> 8) & 0xffffffu);
+            const int pnode = key >> 6, pslot = key & 63;
+            const int pdep = (int)(best & 0xffu);
             const int id = nn + popped;
-            // the parent's depth, from the lane that owns it
-            const int pdep = __builtin_amdgcn_readlane(pnode < 64 ? dep[0] : dep[1], pnode & 63);
             // the new node's lane records it (live only from the next round)
             if ((id & 63) == l) {
-                const int u = id >> 6;
-                par[u] = pnode;
-                slot[u] = pslot;
-                sc[u] = bv;
-                dep[u] = pdep + 1;
-                head[u] = 0;
+                auto record = [&](Node &d) {
+                    d.par = pnode;
+                    d.slot = pslot;
+                    d.sc = unpack_score(best);
+                    d.dep = pdep + 1;
+                };
+                // id is uniform: a branch, not an indexed register array
+                if (id < 64) record(nd[0]);
+                else record(nd[1]);
             }
-            // the parent's lane advances its head
+            // the parent's lane advances its head (u is uniform)
             if ((pnode & 63) == l) {
-                const int u = pnode >> 6;
-                ++head[u];
-                refresh(u);
+                if (pnode < 64) {
+                    advance(0);
+                    c0 = cand(0);
+                } else {
+                    advance(1);
+                    c1 = cand(1);
+                }
             }
         }
         // the round's nodes become live
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int i = 64 * u + l;
-            if (i >= nn && i < nn + popped) {
-                live[u] = true;
-                refresh(u);
-            }
+            if (i >= nn && i < nn + popped) make_live(u);
         }
+        c0 = cand(0);
+        c1 = cand(1);
         nn += popped;
         // a round that found nothing at all leaves nothing for later rounds
         dry = popped == 0;
@@ -171,15 +229,15 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = 64 * u + l;
-        if (i >= n) continue;
-        if (i == 0) {
+        if (i >= n) {
+        } else if (i == 0) {
             parent_out[row0] = -1;
             token_out[row0] = root_tok ? root_tok[b] : -1;
             score_out[row0] = 0.f;
         } else if (i < nn) {
-            parent_out[row0 + i] = par[u];
-            token_out[row0 + i] = cand_tok[((size_t)b * n + par[u]) * K + slot[u]];
-            score_out[row0 + i] = sc[u];
+            parent_out[row0 + i] = nd[u].par;
+            token_out[row0 + i] = cand_tok[((size_t)b * n + nd[u].par) * K + nd[u].slot];
+            score_out[row0 + i] = nd[u].sc;
         } else {
             parent_out[row0 + i] = -1;
             token_out[row0 + i] = -1;

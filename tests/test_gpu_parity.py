@@ -538,6 +538,24 @@ def test_tree_build_ties_and_dry(gpu_lib):
     assert np.array_equal(host(sc).view(np.uint32), rs.view(np.uint32))
 
 
+def test_tree_build_overflowing_scores(gpu_lib):
+    # scores that overflow to -inf are still candidates (popped last, by push
+    # order), and a +inf score is popped first
+    lp = np.full((2, 12, 3), -3e38, np.float32)
+    lp[1, 0, 1] = np.float32(3e38)
+    lp[1, 1, 0] = np.float32(3e38)           # node 1 (3e38) proposes +inf
+    tok = np.arange(2 * 12 * 3, dtype=np.int32).reshape(2, 12, 3)
+    root = np.array([5, 6], np.int32)
+    par, tk, sc, nb = gpu_lib.build_tree(dev(lp), dev(tok), dev(root), 2, 6)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):
+        rp, rt, rs, rn = oracle.build_trees(lp, tok, root, 2, 6)
+    assert np.isneginf(rs).any() and np.isposinf(rs).any()
+    assert np.array_equal(host(nb), rn)
+    assert np.array_equal(host(par), rp) and np.array_equal(host(tk), rt)
+    assert np.array_equal(host(sc).view(np.uint32), rs.view(np.uint32))
+
+
 # ---------------------------------------------------------------------------
 # greedy acceptance walk: bit-exact, then path + fused step from it
 # ---------------------------------------------------------------------------
