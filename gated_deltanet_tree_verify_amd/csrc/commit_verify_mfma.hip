@@ -45,7 +45,12 @@ struct Smem {
         uint16_t v[kN][kQK];
         SolveBlocks s;
         pc::Chunk16 ch;      // over d / tinv, dead once the inverse has finished
-        pc::KeyChunk32 kc;   // same place, when the pseudo-values are given
+        pc::KeyChunk32 kc;   // same place, for the later key chunks of a long path
+        struct {
+            unsigned char skip[offsetof(SolveBlocks, th)];
+            pc::KeyChunk32 kc;   // the first key chunk, over the T rows (th / tl),
+                                 // which the inverse writes only in its last step
+        } kt;
     } b;
     Topo tp;
     pc::Chunk16Aux cx;
@@ -56,6 +61,8 @@ struct Smem {
 static_assert(sizeof(pc::Chunk16) <= offsetof(SolveBlocks, th) &&
                   sizeof(pc::KeyChunk32) <= offsetof(SolveBlocks, th),
               "the commit chunk must fit in the inverse scratch of the solve blocks");
+static_assert(offsetof(SolveBlocks, th) + sizeof(pc::KeyChunk32) <= offsetof(SolveBlocks, xh),
+              "the first key chunk must stay inside the T rows, clear of what the mask writes");
 static_assert(sizeof(Smem) <= 81920, "two workgroups per CU");
 
 // Previous path as seen by wave 3: lane l holds the ids of slots l and
@@ -195,43 +202,44 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     load_state_tile(st[2], 2, slab, c.col, c.h);
     lds_barrier();
     const bool tree_ok = !sm.tp.bad;
-    if (tree_ok) {
-        if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
-        load_state_tile(st[3], 3, slab, c.col, c.h);
-        lds_barrier();
-        inverse(c, sm.b.s);
-    } else {
-        load_state_tile(st[3], 3, slab, c.col, c.h);
-    }
-    lds_barrier();   // the inverse scratch is free from here on
-
-    // ---- 3. commit: wave 3 validates the path and prepares the first chunk
-    if (c.w == 3) {
+    // wave 3: the previous path's validity (and the fault flags)
+    auto validate = [&]() -> bool {
         const bool ok = path_valid(pl, mlen, max_path, n_prev, c.l);
         if (c.l == 0) {
             sm.commit_ok = ok;
             if (s.hd == 0 && status)
                 status[s.b] = (ok ? 0 : kFaultBadPath) | (tree_ok ? 0 : kFaultBadParent);
         }
-        if (ok && mlen > 0) {
-            if constexpr (kU)
-                pc::build_keys32(sm.b.kc, sm.cx, k32, min(32, mlen), c.l);
-            else
-                pc::build16(sm.b.ch, sm.cx, r16, min(pc::kC16, mlen), c.l);
+        return ok;
+    };
+    bool commit;
+    bf16x8 ident[2];
+    pc::key_identity(ident, c.m, c.h);
+    if constexpr (kU) {
+        // ---- 3. wave 3 validates the path and lays out the first key chunk
+        //         (over the T rows) while the others mask; the chunk is applied
+        //         between the inverse's Z / L steps and its last step
+        if (c.w == 3) {
+            if (validate() && mlen > 0)
+                pc::build_keys32(sm.b.kt.kc, sm.cx, k32, min(32, mlen), c.l);
+        } else if (tree_ok) {
+            mask(c, sm.tp, gc, ga, sm.b.s);
         }
-    }
-    lds_barrier();
-    const bool commit = sm.commit_ok && mlen > 0;
-    if (commit) {
-        bf16x8 ident[2];
-        pc::key_identity(ident, c.m, c.h);
-        if constexpr (kU) {
-            pc::apply_known_u(sm.b.kc, sm.cx, U0, st, ident, c.m, c.h);
+        load_state_tile(st[3], 3, slab, c.col, c.h);
+        lds_barrier();
+        commit = sm.commit_ok && mlen > 0;
+        if (tree_ok) {
+            inverse_subst(c, sm.b.s);
+            inverse_zl(c, sm.b.s);
+        }
+        if (commit) pc::apply_known_u(sm.b.kt.kc, sm.cx, U0, st, ident, c.m, c.h);
+        if (tree_ok) inverse_split(c, sm.b.s);   // starts with a barrier: the chunk is read
+        lds_barrier();                           // the inverse scratch is free from here on
+        if (commit) {
             for (int c0 = 32; c0 < mlen; c0 += 32) {
                 const int mc = min(32, mlen - c0);
                 const f32x16 Uc =
                     pc::load_u_chunk(u_head, ubytes, sm.pid, c0, mc, H * kD, c.col, c.h);
-                lds_barrier();   // every wave is done with the previous chunk
                 if (c.w == 3) {
                     const int rj = c.l >> 1;
                     const pc::KeyRows32 kr = pc::load_keys32(
@@ -241,8 +249,29 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
                 }
                 lds_barrier();
                 pc::apply_known_u(sm.b.kc, sm.cx, Uc, st, ident, c.m, c.h);
+                lds_barrier();   // every wave is done with this chunk
             }
+        }
+    } else {
+        if (tree_ok) {
+            if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
+            load_state_tile(st[3], 3, slab, c.col, c.h);
+            lds_barrier();
+            inverse(c, sm.b.s);
         } else {
+            load_state_tile(st[3], 3, slab, c.col, c.h);
+        }
+        lds_barrier();   // the inverse scratch is free from here on
+
+        // ---- 3. commit: wave 3 validates the path and prepares the first
+        //         chunk, every wave applies it
+        if (c.w == 3) {
+            if (validate() && mlen > 0)
+                pc::build16(sm.b.ch, sm.cx, r16, min(pc::kC16, mlen), c.l);
+        }
+        lds_barrier();
+        commit = sm.commit_ok && mlen > 0;
+        if (commit) {
             pc::apply16(sm.b.ch, sm.cx, st, ident, c.m, c.h, c.col);
             for (int c0 = pc::kC16; c0 < mlen; c0 += pc::kC16) {
                 lds_barrier();   // every wave is done with the previous chunk

@@ -258,10 +258,18 @@ __device__ __forceinline__ void mask(const Lane &c, const Topo &tp, const f32x16
 // Z_b = B_b A_b^{-1}, L_b = -C_b^{-1} Z_b, then T_b = [[A^-1, 0], [L, C^-1]]
 // as bf16 hi/lo operand rows.  Starts and ends with the caller's barriers
 // around it; contains three of its own.
-// The two parts of inverse(): the substitution is wave 3's alone, so the
-// other waves may do other work (issue loads) in between.
+// The parts of inverse(): the substitution is wave 3's alone, so the other
+// waves may do other work in between; after inverse_zl the T rows area
+// (th / tl) has not been written yet, so a caller may keep other data there
+// until inverse_split, which starts with a barrier.
 __device__ __forceinline__ void inverse_subst(const Lane &c, SolveBlocks &sb);
-__device__ __forceinline__ void inverse_finish(const Lane &c, SolveBlocks &sb);
+__device__ __forceinline__ void inverse_zl(const Lane &c, SolveBlocks &sb);
+__device__ __forceinline__ void inverse_split(const Lane &c, SolveBlocks &sb);
+
+__device__ __forceinline__ void inverse_finish(const Lane &c, SolveBlocks &sb) {
+    inverse_zl(c, sb);
+    inverse_split(c, sb);
+}
 
 __device__ __forceinline__ void inverse(const Lane &c, SolveBlocks &sb) {
     inverse_subst(c, sb);
@@ -290,7 +298,7 @@ __device__ __forceinline__ void inverse_subst(const Lane &c, SolveBlocks &sb) {
     }
 }
 
-__device__ __forceinline__ void inverse_finish(const Lane &c, SolveBlocks &sb) {
+__device__ __forceinline__ void inverse_zl(const Lane &c, SolveBlocks &sb) {
     lds_barrier();
     // Z_b into the upper-left sub-block of d[b] (read only by the substitution)
 #pragma unroll
@@ -311,6 +319,9 @@ __device__ __forceinline__ void inverse_finish(const Lane &c, SolveBlocks &sb) {
         for (int s = 0; s < 16; ++s) acc = fmaf(sb.tinv[2 * blk + 1][r][s], sb.d[blk][s][col], acc);
         sb.d[blk][16 + r][col] = -acc;
     }
+}
+
+__device__ __forceinline__ void inverse_split(const Lane &c, SolveBlocks &sb) {
     lds_barrier();
     {
         // one 8-entry chunk per thread: permuted positions 8 seg .. 8 seg + 7,
