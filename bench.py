@@ -78,6 +78,21 @@ def fused_bytes(batch, n, H, dk, dv, path_lens):
             - batch * H * 4 * dk * dv)
 
 
+FP32_VECTOR_PEAK = 157.3e12   # MI355X fp32 vector FLOP/s (published)
+
+
+def branch_node_steps(parent):
+    """Node updates of the single-branch baseline on one tree: every
+    root-to-leaf branch runs its whole path, so sum over leaves of depth + 1."""
+    import numpy as np
+    import gdn_synth as gs
+    parent = np.asarray(parent)
+    depth = np.zeros(len(parent), np.int64)
+    for i, p in enumerate(parent):
+        depth[i] = 0 if p < 0 else depth[p] + 1
+    return int(sum(depth[j] + 1 for j in gs.leaves(parent)))
+
+
 def kernel_source_digest():
     p = os.path.join(ROOT, "gated_deltanet_tree_verify_amd", "csrc")
     h = hashlib.sha256()
@@ -329,7 +344,8 @@ def main():
                                k=dev(ts.k_bits.view(np.int16)).view(torch.bfloat16),
                                v=dev(ts.v_bits.view(np.int16)).view(torch.bfloat16),
                                alpha=dev(ts.alpha), beta=dev(ts.beta), parent=dev(ts.parent),
-                               S=dev(ts.S0), leaves=sum(len(gs.leaves(p)) for p in ts.parent)))
+                               S=dev(ts.S0), leaves=sum(len(gs.leaves(p)) for p in ts.parent),
+                               steps=sum(branch_node_steps(p) for p in ts.parent)))
         for d in c_sets:
             d["out"] = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
         tv126 = [g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"],
@@ -353,14 +369,26 @@ def main():
         t_tree = timed_list(tv126, 40)
         t_branch = timed_list(bv126, 10)
         w126 = gs.TREE126
+        # what the branch baseline computes: per branch node and head,
+        # w = S^T k (2 d^2 flops), the update alpha S + (beta k)(v - alpha w)^T
+        # (3 d^2) and o = S^T q (2 d^2); on the fp32 vector peak this is a
+        # floor for any recurrent branch verify on this chip
+        steps = float(np.mean([d["steps"] for d in c_sets]))   # per set, all sequences
+        branch_flop = steps * w126.H * 7 * w126.d_k * w126.d_v
+        floor_us = branch_flop / FP32_VECTOR_PEAK * 1e6
         cmp126 = {"workload": w126.name, "tree_verify_us": t_tree, "branch_verify_us": t_branch,
                   "speedup": t_branch / t_tree,
+                  "branch_node_steps_per_tree": steps / w126.batch,
+                  "branch_tflop_per_s": branch_flop / (t_branch * 1e-6) / 1e12,
+                  "branch_fp32_floor_us": floor_us,
+                  "speedup_vs_branch_floor": floor_us / t_tree,
                   "mean_leaves_per_tree": float(np.mean([d["leaves"] / w126.batch
                                                          for d in c_sets])),
                   "tree_verify_nodes_per_s": w126.batch * w126.n / (t_tree * 1e-6),
                   "pages_speedup_b200": 7.1}
         log(f"n=126: tree verify {t_tree:.1f} us, branch verify {t_branch:.1f} us, "
-            f"speedup {t_branch / t_tree:.2f}")
+            f"speedup {t_branch / t_tree:.2f} (branch at {cmp126['branch_tflop_per_s']:.1f} "
+            f"TFLOP/s; its fp32 floor {floor_us:.0f} us, {floor_us / t_tree:.2f}x the tree)")
         c_sets = tv126 = bv126 = None
 
     # achievable-bandwidth line: a plain 1 GiB device copy
