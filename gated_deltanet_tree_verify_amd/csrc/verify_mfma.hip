@@ -81,9 +81,14 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     lds_barrier();
 
     // ---- 6. solve and output, 7. whole-row stores
-    f32x16 o0, o1;
-    solve_output(c, sm.tp, sm.b.s, P, R, vpk, o0, o1);
-    store_output(c, s, sm.a.o, o0, o1, out);
+    // the first block's rows leave while the second block is solved
+    SolveCarry cy;
+    f32x16 u0, o0, u1, o1;
+    solve_block0(c, sm.tp, sm.b.s, P, R, vpk, u0, o0, cy);
+    store_block<false>(c, s, sm.a.o, o0, out, u0, nullptr, 0);
+    solve_block1(c, sm.b.s, P, cy, u1, o1);
+    lds_barrier();   // every thread has read the first block from the staging area
+    store_block<false>(c, s, sm.a.o, o1, out, u1, nullptr, 32);
 }
 
 }  // namespace
