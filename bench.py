@@ -94,11 +94,17 @@ def branch_node_steps(parent):
 
 
 def kernel_source_digest():
+    """Digest of the fused kernel's code: its sources with // comments and
+    blank lines dropped, so that a comment edit does not void a traffic
+    measurement but any code change does."""
     p = os.path.join(ROOT, "gated_deltanet_tree_verify_amd", "csrc")
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(p, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(p, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -11,18 +11,28 @@
 //
 // Schedule.  The only verify work that needs the state is Q S, K S and what
 // follows; the Gram matrices, masks and block inverses of the new tree need
-// only q/k/v and the parents.  So every wave requests its q/k/v rows first
-// and its state slab right behind them; the tree matrices are built while
-// the state streams in.  Wave 3 also reads the previous path (ids, then the
-// parents that validate it and the first 16 path nodes' rows and gates) and
-// keeps the path rows in registers until the inverse's scratch is free; it
-// then prepares the commit chunk on its own (16-slot chunk tiles overlay
-// that scratch), every wave applies it to its slab, and the verify finishes
-// from the committed slab.  Longer paths continue chunk by chunk.
+// only q/k/v and the parents.  So every wave requests its q and k rows
+// first, its v rows and first state tile once q and k are in, and the rest
+// of its slab one tile per tree-matrix phase; the tree matrices are built
+// while the state streams in.  Wave 3 also reads the previous path (ids,
+// then the parents that validate it and the first chunk's rows and gates).
+//   * Pseudo-values carried (u_prev): while waves 0-2 compute the masks,
+//     wave 3 validates the path and lays out the first 32-slot key chunk
+//     over the T rows of the solve blocks, which the inverse writes only in
+//     its last step; every wave applies the chunk (a rank-m update, no
+//     solve) between the inverse's Z / L steps and that last step.
+//   * Otherwise wave 3 keeps the first 16 path rows in registers until the
+//     inverse's scratch is free, prepares the chunk on its own (Gram,
+//     substitution; 16-slot tiles over that scratch), and every wave
+//     applies it.
+// Longer paths continue chunk by chunk over the inverse scratch.  The verify
+// then finishes from the committed slab, writing the slab back tile by tile
+// as the contraction consumes it, and the solve's first 32-row block is
+// stored while the second is solved.
 //
 // LDS (80 KB, two workgroups per CU): Q/K tiles (later the output staging),
-// one region for the V tile, then the solve blocks, whose inverse scratch
-// later holds the commit chunk, and the topology / chunk gate arrays.
+// one region for the V tile, then the solve blocks, whose inverse scratch or
+// T rows hold the commit chunk in turn, and the topology / chunk gate arrays.
 #include <stddef.h>
 
 #include "internal.hpp"
