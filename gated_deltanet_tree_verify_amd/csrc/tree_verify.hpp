@@ -443,37 +443,6 @@ __device__ __forceinline__ void solve_block1(const Lane &c, const SolveBlocks &s
     o1 = mm3<kBL>(sb.yh[2], sb.yl[2], split_tile(u1), o1, c.m, c.h);
 }
 
-// right-hand side, tiled forward substitution and output tiles o0 (rows
-// 0..31) and o1 (rows 32..63) of this wave's columns
-__device__ __forceinline__ void solve_output(const Lane &c, const Topo &tp, const SolveBlocks &sb,
-                                             f32x16 (&P)[2], const f32x16 (&R)[2],
-                                             const uint32_t (&vpk)[2][8], f32x16 &o0,
-                                             f32x16 &o1) {
-    SolveCarry cy;
-    f32x16 u0, u1;
-    solve_block0(c, tp, sb, P, R, vpk, u0, o0, cy);
-    solve_block1(c, sb, P, cy, u1, o1);
-}
-
-// Output rows through LDS (ostage aliases dead tiles), then stored as whole
-// 512-byte rows.  Contains one barrier.
-__device__ __forceinline__ void store_output(const Lane &c, const Seq &s, float (*ostage)[kD + 4],
-                                             const f32x16 &o0, const f32x16 &o1, float *out) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        ostage[crow(r, c.h)][c.col] = o0[r];
-        ostage[32 + crow(r, c.h)][c.col] = o1[r];
-    }
-    lds_barrier();
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int e = c.tid + kThreads * it, row = e >> 5, c4 = (e & 31) * 4;
-        if (row < s.n)
-            store16(out + s.base + row * s.rstride + c4,
-                    *reinterpret_cast<const float4 *>(&ostage[row][c4]));
-    }
-}
-
 // Rows row0 .. row0 + 31 of one or two [batch][n][H][128] fp32 outputs, from
 // a 32-row result tile each, through LDS as whole 512-byte rows: tile a goes
 // to dst_a through staging rows 0..31, tile b (when kPair) to dst_b through
