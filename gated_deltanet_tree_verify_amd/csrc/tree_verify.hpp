@@ -280,44 +280,69 @@ __device__ __forceinline__ void inverse_subst(const Lane &c, SolveBlocks &sb) {
     if (c.w == 3) {
         const int sbk = c.l >> 4, col = c.l & 15, blk = sbk >> 1, o16 = 16 * (sbk & 1);
         float t[16];
+        // row r's entries are requested two rows ahead of their use, so the
+        // chain of rows waits on arithmetic rather than on LDS latency
+        float4 xr[16][4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == col) ? 1.f : 0.f;
+        for (int r = 0; r < 16 + 2; ++r) {
+            if (r < 16) {
 #pragma unroll
-            for (int s4 = 0; s4 < r; s4 += 4) {
-                const float4 xr = *reinterpret_cast<const float4 *>(&sb.d[blk][o16 + r][o16 + s4]);
-                acc = fmaf(-xr.x, t[s4], acc);
-                if (s4 + 1 < r) acc = fmaf(-xr.y, t[s4 + 1], acc);
-                if (s4 + 2 < r) acc = fmaf(-xr.z, t[s4 + 2], acc);
-                if (s4 + 3 < r) acc = fmaf(-xr.w, t[s4 + 3], acc);
+                for (int s4 = 0; s4 < r; s4 += 4)
+                    xr[r][s4 / 4] = *reinterpret_cast<const float4 *>(&sb.d[blk][o16 + r][o16 + s4]);
             }
-            t[r] = acc;
+            const int rr = r - 2;
+            if (rr >= 0) {
+                float acc = (rr == col) ? 1.f : 0.f;
+#pragma unroll
+                for (int s4 = 0; s4 < rr; s4 += 4) {
+                    const float4 x4 = xr[rr][s4 / 4];
+                    acc = fmaf(-x4.x, t[s4], acc);
+                    if (s4 + 1 < rr) acc = fmaf(-x4.y, t[s4 + 1], acc);
+                    if (s4 + 2 < rr) acc = fmaf(-x4.z, t[s4 + 2], acc);
+                    if (s4 + 3 < rr) acc = fmaf(-x4.w, t[s4 + 3], acc);
+                }
+                t[rr] = acc;
+            }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sb.tinv[sbk][r][col] = t[r];
     }
 }
-
 __device__ __forceinline__ void inverse_zl(const Lane &c, SolveBlocks &sb) {
+    // one thread per (block, row, four columns): rows of the left factor and
+    // of the right one are read four entries at a time
+    const int blk = (c.tid >> 6) & 1, r = (c.tid >> 2) & 15, c4 = 4 * (c.tid & 3);
+    const bool zl = c.tid < 128;
+    // a: 16 entries of one row; b: 16 rows, ldb floats apart, columns c4..c4+3
+    auto row_times = [&](const float *a, const float *b, int ldb) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < 16; s4 += 4) {
+            const float4 a4 = *reinterpret_cast<const float4 *>(&a[s4]);
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(&b[(s4 + e) * ldb + c4]);
+                acc[0] = fmaf(av[e], b4.x, acc[0]);
+                acc[1] = fmaf(av[e], b4.y, acc[1]);
+                acc[2] = fmaf(av[e], b4.z, acc[2]);
+                acc[3] = fmaf(av[e], b4.w, acc[3]);
+            }
+        }
+        return make_float4(acc[0], acc[1], acc[2], acc[3]);
+    };
     lds_barrier();
-    // Z_b into the upper-left sub-block of d[b] (read only by the substitution)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int idx = c.tid + kThreads * u, blk = idx >> 8, r = (idx >> 4) & 15, col = idx & 15;
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) acc = fmaf(sb.d[blk][16 + r][s], sb.tinv[2 * blk][s][col], acc);
-        sb.d[blk][r][col] = acc;
+    // Z_b = B_b A_b^-1 into the upper-left sub-block of d[b] (read only by
+    // the substitution); B_b is the lower-left sub-block
+    if (zl) {
+        const float4 z = row_times(&sb.d[blk][16 + r][0], &sb.tinv[2 * blk][0][0], 16);
+        *reinterpret_cast<float4 *>(&sb.d[blk][r][c4]) = z;
     }
     lds_barrier();
-    // L_b into the lower-left sub-block (B_b is no longer read)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int idx = c.tid + kThreads * u, blk = idx >> 8, r = (idx >> 4) & 15, col = idx & 15;
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) acc = fmaf(sb.tinv[2 * blk + 1][r][s], sb.d[blk][s][col], acc);
-        sb.d[blk][16 + r][col] = -acc;
+    // L_b = -C_b^-1 Z_b into the lower-left sub-block (B_b is no longer read)
+    if (zl) {
+        const float4 x = row_times(&sb.tinv[2 * blk + 1][r][0], &sb.d[blk][0][0], 32);
+        *reinterpret_cast<float4 *>(&sb.d[blk][16 + r][c4]) = make_float4(-x.x, -x.y, -x.z, -x.w);
     }
 }
 
