@@ -11,28 +11,34 @@
 //
 // Schedule.  The only verify work that needs the state is Q S, K S and what
 // follows; the Gram matrices, masks and block inverses of the new tree need
-// only q/k/v and the parents.  So every wave requests its q and k rows
-// first, its v rows and first state tile once q and k are in, and the rest
-// of its slab one tile per tree-matrix phase; the tree matrices are built
-// while the state streams in.  Wave 3 also reads the previous path (ids,
+// only q, k and the parents.  So every wave requests its q and k rows
+// first, its first state tiles once q and k are in, then the rest of its
+// slab (one tile per tree-matrix phase) and its v rows; the tree matrices
+// are built while the state streams in.  Wave 3 also reads the previous path (ids,
 // then the parents that validate it and the first chunk's rows and gates).
 //   * Pseudo-values carried (u_prev): while waves 0-2 compute the masks,
 //     wave 3 validates the path and lays out the first 32-slot key chunk
 //     over the T rows of the solve blocks, which the inverse writes only in
 //     its last step; every wave applies the chunk (a rank-m update, no
 //     solve) between the inverse's Z / L steps and that last step.
-//   * Otherwise wave 3 keeps the first 16 path rows in registers until the
-//     inverse's scratch is free, prepares the chunk on its own (Gram,
-//     substitution; 16-slot tiles over that scratch), and every wave
-//     applies it.
+//   * Otherwise (the commit solves for the pseudo-values) the first 16-slot
+//     chunk goes to the same place: wave 3 lays out its keys and builds its
+//     Gram and X during the masks, wave 0 its T = (I + X)^{-1} while wave 3
+//     substitutes the tree's blocks, and every wave holds its own columns of
+//     the chunk's value rows in registers; every wave applies it at the same
+//     point (R = K_p S, U = T RHS, then the update).
 // Longer paths continue chunk by chunk over the inverse scratch.  The verify
 // then finishes from the committed slab, writing the slab back tile by tile
 // as the contraction consumes it, and the solve's first 32-row block is
 // stored while the second is solved.
 //
-// LDS (80 KB, two workgroups per CU): Q/K tiles (later the output staging),
-// one region for the V tile, then the solve blocks, whose inverse scratch or
-// T rows hold the commit chunk in turn, and the topology / chunk gate arrays.
+// The new tree's v rows are needed only by the solve, so they are requested
+// behind the state and wait in registers; once the contraction has read the
+// K tile, the V tile passes through its place into each lane's columns.
+//
+// LDS (80 KB, two workgroups per CU): Q/K tiles (then the V tile, then the
+// output staging), the solve blocks, whose inverse scratch or T rows hold
+// the commit chunk in turn, and the topology / chunk gate arrays.
 #include <stddef.h>
 
 #include "internal.hpp"
@@ -52,7 +58,6 @@ struct Smem {
         float o[kN][kD + 4];
     } a;
     union {
-        uint16_t v[kN][kQK];
         SolveBlocks s;
         pc::Chunk16 ch;      // over d / tinv, dead once the inverse has finished
         pc::KeyChunk32 kc;   // same place, for the later key chunks of a long path
@@ -61,18 +66,23 @@ struct Smem {
             pc::KeyChunk32 kc;   // the first key chunk, over the T rows (th / tl),
                                  // which the inverse writes only in its last step
         } kt;
+        struct {
+            unsigned char skip[offsetof(SolveBlocks, th)];
+            pc::EarlyChunk16 ch;   // the first chunk of a solving commit, same place
+        } kt16;
     } b;
     Topo tp;
     pc::Chunk16Aux cx;
-    int pid[kMaxPathIds];    // previous path ids, when the pseudo-values are given
+    int pid[kMaxPathIds];    // previous path ids
     int commit_ok;
 };
 
 static_assert(sizeof(pc::Chunk16) <= offsetof(SolveBlocks, th) &&
                   sizeof(pc::KeyChunk32) <= offsetof(SolveBlocks, th),
               "the commit chunk must fit in the inverse scratch of the solve blocks");
-static_assert(offsetof(SolveBlocks, th) + sizeof(pc::KeyChunk32) <= offsetof(SolveBlocks, xh),
-              "the first key chunk must stay inside the T rows, clear of what the mask writes");
+static_assert(offsetof(SolveBlocks, th) + sizeof(pc::KeyChunk32) <= offsetof(SolveBlocks, xh) &&
+                  offsetof(SolveBlocks, th) + sizeof(pc::EarlyChunk16) <= offsetof(SolveBlocks, xh),
+              "the first commit chunk must stay inside the T rows, clear of what the mask writes");
 static_assert(sizeof(Smem) <= 81920, "two workgroups per CU");
 
 // Previous path as seen by wave 3: lane l holds the ids of slots l and
@@ -111,8 +121,12 @@ __device__ __forceinline__ bool path_valid(const PathLanes &p, int m, int max_pa
 // kU: the previous tree's pseudo-values u_prev are given, so the commit is
 // the rank-m update S <- e^{g_a} S + sum_s e^{g_a - g_s} k_s u_s^T with no
 // solve; otherwise the commit solves for them chunk by chunk.  kUout: the
-// new tree's pseudo-values are written to u_out.
-template <bool kU, bool kUout>
+// new tree's pseudo-values are written to u_out.  kLong: paths may be longer
+// than the first chunk (32 slots with pseudo-values given, else 16), so the
+// later chunks are applied too; without it a longer path is never read
+// (the host takes the kLong instance whenever max_path exceeds the first
+// chunk), and the kernel carries no code and no registers for them.
+template <bool kU, bool kUout, bool kLong>
 __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     float *__restrict__ S, const int32_t *__restrict__ path, const int32_t *__restrict__ path_len,
     int max_path, const uint16_t *__restrict__ k_prev, const uint16_t *__restrict__ v_prev,
@@ -153,17 +167,18 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     // tree-matrix phases: a wave that issues a whole 64 KiB slab stalls
     // until the memory system has accepted all of it
     f32x16 st[4];
-    pc::Rows16 r16;
+    pc::KeyRows16 r16;
     pc::KeyRows32 k32;
     if (c.w == 3) {
         // parents of the path ids (ids out of range fail validation by
         // themselves) and the first chunk's rows and gates
         if (pl.id0 >= 0 && pl.id0 < n_prev) pl.par0 = ppar[pl.id0];
         if (pl.id1 >= 0 && pl.id1 < n_prev) pl.par1 = ppar[pl.id1];
+        // ids for every wave's u or v loads
+        if (pl.id0 >= 0) sm.pid[c.l] = pl.id0;
+        if (pl.id1 >= 0) sm.pid[64 + c.l] = pl.id1;
         if constexpr (kU) {
-            // ids for every wave's u loads; the first chunk's keys and gates
-            if (pl.id0 >= 0) sm.pid[c.l] = pl.id0;
-            if (pl.id1 >= 0) sm.pid[64 + c.l] = pl.id1;
+            // the first chunk's keys and gates
             const int mc0 = min(32, mlen);
             const int rj = c.l >> 1;
             const int rid = slot_id(pl, rj);
@@ -174,10 +189,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             const int mc0 = min(pc::kC16, mlen);
             const int rj = c.l >> 2;
             const int rid = slot_id(pl, rj);
-            r16 = pc::load_rows16(rid, rj < mc0 && rid >= 0 && rid < n_prev, pl.id0,
+            r16 = pc::load_keys16(rid, rj < mc0 && rid >= 0 && rid < n_prev, pl.id0,
                                   c.l < mc0 && pl.id0 >= 0 && pl.id0 < n_prev, k_prev + prow0,
-                                  v_prev + prow0, alpha_prev + pgate0, beta_prev + pgate0,
-                                  H * kD, H, pbytes, c.l);
+                                  alpha_prev + pgate0, beta_prev + pgate0, H * kD, H, pbytes,
+                                  c.l);
         }
         topology(c, s, gt, sm.tp, status, false);
         // zero rows for the padded slots of the commit chunk operands
@@ -186,9 +201,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     }
     store_rows_permuted(c, rq, sm.a.t.q);
     store_rows_permuted(c, rk, sm.a.t.k);
-    // v only once q and k are in: every workgroup's Gram operands are
+    // the state once q and k are in: every workgroup's Gram operands are
     // fetched before any of the bulk behind them
-    load_rows(c, s, v, rv);
     load_state_tile(st[0], 0, slab, c.col, c.h);
     lds_barrier();
     load_state_tile(st[1], 1, slab, c.col, c.h);
@@ -198,19 +212,22 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     const float *u_head = u_prev + prow0;
     const uint32_t ubytes = (uint32_t)((size_t)n_prev * H * kD * 4);
     f32x16 U0 = {};
-    if constexpr (kU)
-        if (mlen > 0 && mlen <= kMaxPathIds)
+    if (mlen > 0 && mlen <= kMaxPathIds) {
+        if constexpr (kU)
             U0 = pc::load_u_chunk(u_head, ubytes, sm.pid, 0, min(32, mlen), H * kD, c.col, c.h);
+        else   // the first chunk's values, in this wave's columns
+            U0 = pc::load_v_chunk16(v_prev + prow0, pbytes, sm.pid, 0, min(pc::kC16, mlen),
+                                    H * kD, c.col, c.h);
+    }
 
     // ---- 2. the new tree's Gram, masks and block inverses (no state needed)
     f32x16 gc, ga;
     if (c.w < 3) gram(c, sm.a.t, gc, ga);
-    store_rows(c, rv, sm.b.v);
-    lds_barrier();
-    uint32_t vpk[2][8];
-    v_to_regs(c, sm.b.v, vpk);
     load_state_tile(st[2], 2, slab, c.col, c.h);
-    lds_barrier();
+    // v is needed only by the solve: its rows are requested behind the
+    // state and wait in registers, so the tree matrices need not wait for
+    // them (the V tile passes through LDS after the contraction)
+    load_rows(c, s, v, rv);
     const bool tree_ok = !sm.tp.bad;
     // wave 3: the previous path's validity (and the fault flags)
     auto validate = [&]() -> bool {
@@ -245,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
         if (commit) pc::apply_known_u(sm.b.kt.kc, sm.cx, U0, st, ident, c.m, c.h);
         if (tree_ok) inverse_split(c, sm.b.s);   // starts with a barrier: the chunk is read
         lds_barrier();                           // the inverse scratch is free from here on
-        if (commit) {
+        if (kLong && commit) {
             for (int c0 = 32; c0 < mlen; c0 += 32) {
                 const int mc = min(32, mlen - c0);
                 const f32x16 Uc =
@@ -263,28 +280,35 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             }
         }
     } else {
-        if (tree_ok) {
-            if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
-            load_state_tile(st[3], 3, slab, c.col, c.h);
-            lds_barrier();
-            inverse(c, sm.b.s);
-        } else {
-            load_state_tile(st[3], 3, slab, c.col, c.h);
-        }
-        lds_barrier();   // the inverse scratch is free from here on
-
-        // ---- 3. commit: wave 3 validates the path and prepares the first
-        //         chunk, every wave applies it
+        // ---- 3. the first 16-slot chunk (over the T rows): wave 3 validates
+        //         the path and builds the chunk's keys and X while the others
+        //         mask, wave 0 its T while wave 3 substitutes the tree's
+        //         diagonal blocks; every wave applies it, its values from
+        //         registers, between the inverse's Z / L steps and its last step
         if (c.w == 3) {
             if (validate() && mlen > 0)
-                pc::build16(sm.b.ch, sm.cx, r16, min(pc::kC16, mlen), c.l);
+                pc::build16_x(sm.b.kt16.ch, sm.cx, r16.k, r16.la, r16.bt, min(pc::kC16, mlen),
+                              c.l);
+        } else if (tree_ok) {
+            mask(c, sm.tp, gc, ga, sm.b.s);
         }
+        load_state_tile(st[3], 3, slab, c.col, c.h);
         lds_barrier();
         commit = sm.commit_ok && mlen > 0;
-        if (commit) {
-            pc::apply16(sm.b.ch, sm.cx, st, ident, c.m, c.h, c.col);
+        if (commit && c.w == 0) pc::build16_t(sm.b.kt16.ch, c.l);
+        if (tree_ok) {
+            inverse_subst(c, sm.b.s);
+            inverse_zl(c, sm.b.s);   // starts with a barrier: T is in place
+        } else {
+            lds_barrier();
+        }
+        if (commit) pc::apply16_early(sm.b.kt16.ch, sm.cx, U0, st, ident, c.m, c.h);
+        if (tree_ok) inverse_split(c, sm.b.s);   // starts with a barrier: the chunk is read
+        lds_barrier();                           // the inverse scratch is free from here on
+        if (kLong && commit) {
+            // later chunks: wave 3 loads and prepares each over the inverse
+            // scratch, every wave applies it
             for (int c0 = pc::kC16; c0 < mlen; c0 += pc::kC16) {
-                lds_barrier();   // every wave is done with the previous chunk
                 if (c.w == 3) {
                     const int mc = min(pc::kC16, mlen - c0);
                     const int rj = c.l >> 2;
@@ -296,6 +320,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
                 }
                 lds_barrier();
                 pc::apply16(sm.b.ch, sm.cx, st, ident, c.m, c.h, c.col);
+                lds_barrier();   // every wave is done with this chunk
             }
         }
     }
@@ -315,7 +340,16 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     // stores issued there.  One explicit wait here settles it.
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     contract(c, sm.a.t, st, P, R, commit ? slab : nullptr);
+    // the V tile through the K tile's place (free once every wave has
+    // finished the contraction) into this lane's columns
     lds_barrier();
+    store_rows(c, rv, sm.a.t.k);
+    lds_barrier();
+    uint32_t vpk[2][8];
+    v_to_regs(c, sm.a.t.k, vpk);
+    // the first block's staging rows overlap the K tile only when the
+    // pseudo-values are staged beside the outputs
+    if constexpr (kUout) lds_barrier();
     // the first block's rows leave while the second block is solved
     SolveCarry cy;
     f32x16 u0, o0, u1, o1;
@@ -335,10 +369,15 @@ bool commit_verify_mfma_supports(const CommitVerifyArgs &a) {
 }
 
 hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s) {
-    auto kern = a.u_prev ? (a.u_out ? commit_verify_mfma_kernel<true, true>
-                                    : commit_verify_mfma_kernel<true, false>)
-                         : (a.u_out ? commit_verify_mfma_kernel<false, true>
-                                    : commit_verify_mfma_kernel<false, false>);
+    const bool lng = a.c.max_path > (a.u_prev ? 32 : pc::kC16);
+    auto kern = a.u_prev ? (a.u_out ? (lng ? commit_verify_mfma_kernel<true, true, true>
+                                           : commit_verify_mfma_kernel<true, true, false>)
+                                    : (lng ? commit_verify_mfma_kernel<true, false, true>
+                                           : commit_verify_mfma_kernel<true, false, false>))
+                         : (a.u_out ? (lng ? commit_verify_mfma_kernel<false, true, true>
+                                           : commit_verify_mfma_kernel<false, true, false>)
+                                    : (lng ? commit_verify_mfma_kernel<false, false, true>
+                                           : commit_verify_mfma_kernel<false, false, false>));
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.v.batch * a.v.H)), dim3(kThreads), 0, s, a.c.S,
                        a.c.path, a.c.path_len, a.c.max_path, (const uint16_t *)a.c.k,
                        (const uint16_t *)a.c.v, a.c.alpha, a.c.beta, a.c.parent, a.u_prev,

@@ -323,13 +323,17 @@ __device__ __forceinline__ void apply_update(const ChunkView &cv, const f32x16 &
 }
 
 // Apply a prepared chunk of NR (16 or 32) path slots to this wave's state
-// slab (no barrier inside).
-template <int NR>
-__device__ __forceinline__ void apply_rows(const ChunkView &cv, f32x16 (&st)[4],
-                                           const bf16x8 (&ident)[2], int h, int col) {
+// slab, the chunk's values given in registers: vv[r] = v of path slot
+// crow(r, h) in this lane's column, zero past the chunk (no barrier inside).
+// NA (1 or 2) accumulators for R: two halve its MFMA chain at the cost of
+// 16 registers.
+template <int NR, int NA = 1>
+__device__ __forceinline__ void apply_rows_v(const ChunkView &cv, const f32x16 &vv,
+                                             f32x16 (&st)[4], const bf16x8 (&ident)[2], int h) {
     constexpr int KS = NR / 16;   // k-steps over path slots that can be nonzero
-    // ---- R = K_p S: B operands straight from the state tiles
-    f32x16 R = {};
+    // ---- R = K_p S: B operands straight from the state tiles (with two
+    //      accumulators, even and odd state tiles apart)
+    f32x16 Rp[NA] = {};
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -340,17 +344,18 @@ __device__ __forceinline__ void apply_rows(const ChunkView &cv, f32x16 (&st)[4],
             bf16x8 sh, sl;
             split8(sv, sh, sl);
             const bf16x8 a = lds8(cv.kp_row + 32 * q + 16 * kk + 8 * h);
-            R = mfma(a, sh, R);
-            R = mfma(a, sl, R);
+            Rp[q % NA] = mfma(a, sh, Rp[q % NA]);
+            Rp[q % NA] = mfma(a, sl, Rp[q % NA]);
         }
+    f32x16 R = Rp[0];
+    if constexpr (NA == 2) R += Rp[1];
 
     // ---- right-hand side and U = T RHS, scaled by the decay to the chunk end
     f32x16 rhs;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int j = crow(r, h);
-        rhs[r] = j < NR ? cv.beta[j] * (to_f32(cv.vp[j * cv.vp_stride + col]) - cv.eg[j] * R[r])
-                        : 0.f;
+        rhs[r] = j < NR ? cv.beta[j] * (vv[r] - cv.eg[j] * R[r]) : 0.f;
     }
     f32x16 U = {};
 #pragma unroll
@@ -367,6 +372,19 @@ __device__ __forceinline__ void apply_rows(const ChunkView &cv, f32x16 (&st)[4],
         U = mfma(al, bhh, U);
     }
     apply_update<NR>(cv, U, st, ident, h);
+}
+
+// the same with the chunk's values read from the LDS value tile
+template <int NR>
+__device__ __forceinline__ void apply_rows(const ChunkView &cv, f32x16 (&st)[4],
+                                           const bf16x8 (&ident)[2], int h, int col) {
+    f32x16 vv;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int j = crow(r, h);
+        vv[r] = j < NR ? to_f32(cv.vp[j * cv.vp_stride + col]) : 0.f;
+    }
+    apply_rows_v<NR>(cv, vv, st, ident, h);
 }
 
 __device__ __forceinline__ void apply_chunk(const ChunkTiles &sm, f32x16 (&st)[4],
@@ -430,24 +448,23 @@ __device__ __forceinline__ Rows16 load_rows16(int row_id, bool row_live, int gat
     return r;
 }
 
-// One wave: rows into the chunk tiles, decay prefix, Gram, X, and
-// T = (I + X)^{-1} by forward substitution (lane = column of T).  LDS
-// accesses of one wave complete in order, so no barrier is needed inside.
-__device__ __forceinline__ void build16(Chunk16 &ch, Chunk16Aux &ax, const Rows16 &r, int mc,
-                                        int l) {
+// One wave: keys into a chunk's key tile, decay prefix, Gram and X; Ch has
+// the kp, x, th and tl members of Chunk16.  k holds the lane's part of the
+// key rows as loaded by load_rows16 / load_keys16, la and bt its slot's raw
+// gates (lanes < 16).  LDS accesses of one wave complete in order, so no
+// barrier is needed inside.
+template <class Ch>
+__device__ __forceinline__ void build16_x(Ch &ch, Chunk16Aux &ax, const uint4 (&k)[4], float la,
+                                             float bt, int mc, int l) {
     const int m = l & 31, h = l >> 5;
     {
         const int j = l >> 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c8 = 32 * (l & 3) + 8 * i;
-            store_row8_permuted(ch.kp[j], c8, r.k[i]);
-            *reinterpret_cast<uint4 *>(&ch.vp[j][c8]) = r.v[i];
-        }
+        for (int i = 0; i < 4; ++i) store_row8_permuted(ch.kp[j], 32 * (l & 3) + 8 * i, k[i]);
     }
     // inclusive prefix of the log2 decays over the chunk (slots past mc: 0)
     {
-        float gs = (l < mc) ? log2f(r.la) : 0.f;
+        float gs = (l < mc) ? log2f(la) : 0.f;
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) {
             const float t = __shfl_up(gs, o, 32);
@@ -458,7 +475,7 @@ __device__ __forceinline__ void build16(Chunk16 &ch, Chunk16Aux &ax, const Rows1
             ax.g[l] = gs;
             ax.eg[l] = l < mc ? exp2f(gs) : 0.f;
             ax.wdec[l] = l < mc ? exp2f(gl - gs) : 0.f;
-            ax.beta[l] = l < mc ? r.bt : 0.f;
+            ax.beta[l] = l < mc ? bt : 0.f;
         }
         if (l == 0) ax.glast = exp2f(gl);
     }
@@ -487,23 +504,39 @@ __device__ __forceinline__ void build16(Chunk16 &ch, Chunk16Aux &ax, const Rows1
                 make_float4(x4[0], x4[1], x4[2], x4[3]);
         }
     }
-    // T column l (lanes 0..15) by forward substitution; lanes 16..31 write
-    // the zero columns 16..31
+}
+
+// One wave (any; the chunk's X written and visible): T = (I + X)^{-1} by
+// forward substitution, lane = column of T (lanes 0..15); lanes 16..31
+// write the zero columns 16..31.  Row r's entries are requested two rows
+// ahead of their use, so the chain of rows waits on arithmetic rather than
+// on LDS latency.
+template <class Ch>
+__device__ __forceinline__ void build16_t(Ch &ch, int l) {
     if (l < 16) {
         const int col = l;
         float t[16];
+        float4 xr[16][4];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            float acc = (rr == col) ? 1.f : 0.f;
+        for (int r = 0; r < 16 + 2; ++r) {
+            if (r < 16) {
 #pragma unroll
-            for (int s4 = 0; s4 < rr; s4 += 4) {
-                const float4 xr = *reinterpret_cast<const float4 *>(&ch.x[rr][s4]);
-                acc = fmaf(-xr.x, t[s4], acc);
-                if (s4 + 1 < rr) acc = fmaf(-xr.y, t[s4 + 1], acc);
-                if (s4 + 2 < rr) acc = fmaf(-xr.z, t[s4 + 2], acc);
-                if (s4 + 3 < rr) acc = fmaf(-xr.w, t[s4 + 3], acc);
+                for (int s4 = 0; s4 < r; s4 += 4)
+                    xr[r][s4 / 4] = *reinterpret_cast<const float4 *>(&ch.x[r][s4]);
             }
-            t[rr] = acc;
+            const int rr = r - 2;
+            if (rr >= 0) {
+                float acc = (rr == col) ? 1.f : 0.f;
+#pragma unroll
+                for (int s4 = 0; s4 < rr; s4 += 4) {
+                    const float4 x4 = xr[rr][s4 / 4];
+                    acc = fmaf(-x4.x, t[s4], acc);
+                    if (s4 + 1 < rr) acc = fmaf(-x4.y, t[s4 + 1], acc);
+                    if (s4 + 2 < rr) acc = fmaf(-x4.z, t[s4 + 2], acc);
+                    if (s4 + 3 < rr) acc = fmaf(-x4.w, t[s4 + 3], acc);
+                }
+                t[rr] = acc;
+            }
         }
         const int pc = perm(col);
 #pragma unroll
@@ -523,6 +556,19 @@ __device__ __forceinline__ void build16(Chunk16 &ch, Chunk16Aux &ax, const Rows1
     }
 }
 
+// One wave: rows into the chunk tiles (values too), X, then T.
+__device__ __forceinline__ void build16(Chunk16 &ch, Chunk16Aux &ax, const Rows16 &r, int mc,
+                                        int l) {
+    {
+        const int j = l >> 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4 *>(&ch.vp[j][32 * (l & 3) + 8 * i]) = r.v[i];
+    }
+    build16_x(ch, ax, r.k, r.la, r.bt, mc, l);
+    build16_t(ch, l);
+}
+
 __device__ __forceinline__ void apply16(const Chunk16 &ch, const Chunk16Aux &ax, f32x16 (&st)[4],
                                         const bf16x8 (&ident)[2], int m, int h, int col) {
     const bool live = m < kC16;
@@ -531,6 +577,70 @@ __device__ __forceinline__ void apply16(const Chunk16 &ch, const Chunk16Aux &ax,
                        ax.eg,                  ax.wdec,
                        ax.beta,                ax.glast};
     apply_rows<kC16>(cv, st, ident, h, col);
+}
+
+// ---- the first 16-slot chunk of a solving commit, prepared while the
+// verify's tree matrices are built: it holds no values (every wave keeps its
+// own columns of the chunk's value rows in registers), so it fits in the
+// T rows of the verify's solve blocks.
+struct EarlyChunk16 {
+    uint16_t kp[kC16][kKP];                  // path keys, d_k permuted within 16-blocks
+    float x[kC16][kC16];                     // X of the chunk (strictly lower)
+    uint16_t th[kC16][kBL], tl[kC16][kBL];   // T hi / lo; permuted columns, 16..31 zero
+};
+
+// key rows and raw gates of a chunk in the preparing wave: lane l holds
+// bytes [64 (l & 3), 64 (l & 3) + 64) of slot l >> 2's key row, lanes < 16
+// slot l's alpha and beta (arguments as for load_rows16)
+struct KeyRows16 {
+    uint4 k[4];
+    float la, bt;
+};
+
+__device__ __forceinline__ KeyRows16 load_keys16(int row_id, bool row_live, int gate_id,
+                                                 bool gate_live, const uint16_t *k,
+                                                 const float *alpha, const float *beta, int rs,
+                                                 int gs, uint32_t bytes, int l) {
+    KeyRows16 r;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k, bytes);
+    const uint32_t base = row_live ? (uint32_t)(row_id * rs + 32 * (l & 3)) * 2 : bytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.k[i] = load16(kr, row_live ? base + 16 * i : bytes);
+    const int gi = gate_live ? gate_id : 0;
+    r.la = alpha[(size_t)gi * gs];
+    r.bt = beta[(size_t)gi * gs];
+    return r;
+}
+
+// this lane's values of the first 16 slots crow(r, h), r < 8, of the chunk
+// at path slot c0, widened from bf16 (zero past the chunk): v_head points at
+// node 0 of this (sequence, head) of a [batch][n][H][128] bf16 tensor,
+// rs = H * 128, bytes = n * rs * 2
+__device__ __forceinline__ f32x16 load_v_chunk16(const uint16_t *v_head, uint32_t bytes,
+                                                 const int *pid, int c0, int mc, int rs, int col,
+                                                 int h) {
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_head, bytes);
+    f32x16 V = {};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int j = crow(r, h);
+        const uint32_t off =
+            j < mc ? (uint32_t)(pid[min(c0 + j, kMaxPath - 1)] * rs + col) * 2 : bytes;
+        const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(vr, (int)off, 0, kNT);
+        V[r] = __uint_as_float((uint32_t)x << 16);
+    }
+    return V;
+}
+
+__device__ __forceinline__ void apply16_early(const EarlyChunk16 &ch, const Chunk16Aux &ax,
+                                              const f32x16 &vv, f32x16 (&st)[4],
+                                              const bf16x8 (&ident)[2], int m, int h) {
+    const bool live = m < kC16;
+    const ChunkView cv{live ? ch.kp[m] : ax.zk, live ? ch.th[m] : ax.zt, live ? ch.tl[m] : ax.zt,
+                       nullptr,                0,
+                       ax.eg,                  ax.wdec,
+                       ax.beta,                ax.glast};
+    apply_rows_v<kC16, 2>(cv, vv, st, ident, h);
 }
 
 // ---- commit from known pseudo-values (u_s written by the verify that ran on

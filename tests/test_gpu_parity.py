@@ -392,17 +392,18 @@ def test_commit_verify_matches_separate_calls(gpu_lib):
     assert oracle.rel_err(out, oref) <= BF16_GATE
 
 
-@pytest.mark.parametrize("n_prev,n,dk,dv,dtype", [
-    (128, 64, 128, 128, "bf16"),    # fused kernel, four commit chunks
-    (20, 1, 128, 128, "bf16"),      # fused kernel, one-node tree
-    (64, 100, 128, 128, "bf16"),    # MFMA commit + generic verify
-    (8, 65, 128, 128, "bf16"),
-    (37, 37, 64, 64, "fp32"),       # generic commit + generic verify
-    (50, 30, 32, 48, "bf16"),
+@pytest.mark.parametrize("n_prev,n,dk,dv,dtype,max_path", [
+    (128, 64, 128, 128, "bf16", None),   # fused kernel, four commit chunks
+    (20, 1, 128, 128, "bf16", None),     # fused kernel, one-node tree
+    (64, 64, 128, 128, "bf16", 13),      # fused kernel, paths within the first chunk
+    (64, 100, 128, 128, "bf16", None),   # MFMA commit + generic verify
+    (8, 65, 128, 128, "bf16", None),
+    (37, 37, 64, 64, "fp32", None),      # generic commit + generic verify
+    (50, 30, 32, 48, "bf16", None),
 ])
-def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype):
+def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype, max_path):
     """sequence 0 clean, 1 bad previous path, 2 bad new tree, 3 both, 4 empty path"""
-    say("commit-verify", n_prev, n, dk, dv, dtype)
+    say("commit-verify", n_prev, n, dk, dv, dtype, max_path)
     rng = np.random.default_rng(n_prev * 7 + n)
     pp = np.stack([gs.chain_tree(n_prev) if n_prev == 128 else
                    gs.random_recursive_tree(rng, n_prev, max_depth=12) for _ in range(5)])
@@ -412,7 +413,7 @@ def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype):
         acc[:] = 127
     prev = gs.make_set(pp, 2, dk, dv, dtype, seed=n_prev, accepted=acc)
     cur = gs.make_set(pc, 2, dk, dv, dtype, seed=n_prev + 1)
-    path, plen = prev.paths(max_path=n_prev)
+    path, plen = prev.paths(max_path=n_prev if max_path is None else max_path)
     path[1, plen[1] - 1] = n_prev       # id out of range
     path[3, 0] = n_prev + 3
     plen[4] = 0
@@ -504,6 +505,43 @@ def test_commit_verify_pseudo_values_long_path_and_faults(gpu_lib):
     assert np.isnan(oh[2]).all() and np.isnan(uh[2]).all()
     UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
     assert oracle.rel_err(uh[[0, 1]], UB[[0, 1]]) <= BF16_GATE
+
+
+def test_commit_verify_pseudo_values_short_paths_and_faults(gpu_lib):
+    """max_path 13 (the first 32-slot chunk holds every path): a clean
+    sequence, an out-of-range id, a path longer than max_path, an empty path;
+    faulted and empty paths leave the state bit-unchanged"""
+    rng = np.random.default_rng(41)
+    pprev = np.stack([gs.random_recursive_tree(rng, 64, max_depth=12) for _ in range(4)])
+    pcur = np.stack([gs.random_recursive_tree(rng, 64, max_depth=12) for _ in range(4)])
+    acc = np.array([gs.pick_leaf(rng, pprev[i]) for i in range(4)], np.int32)
+    A = gs.make_set(pprev, 2, 128, 128, "bf16", seed=41, accepted=acc)
+    B = gs.make_set(pcur, 2, 128, 128, "bf16", seed=42)
+    dA, dB = upload(A), upload(B)
+    S = dA["S0"].clone()
+    prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
+    uA = torch.empty(dA["v"].shape, dtype=torch.float32, device="cuda")
+    uB = torch.empty(dB["v"].shape, dtype=torch.float32, device="cuda")
+    path, plen = A.paths(max_path=13)
+    gpu_lib.commit_verify(S, dev(path), dev(np.zeros(4, np.int32)), prevA, dA["q"], dA["k"],
+                          dA["v"], dA["alpha"], dA["beta"], dA["parent"], u_out=uA)
+    path[1, 0] = 70                     # sequence 1: id out of range
+    plen[2] = 14                        # sequence 2: longer than max_path
+    plen[3] = 0                         # sequence 3: nothing to commit
+    st = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    outB = gpu_lib.commit_verify(S, dev(path), dev(plen), prevA, dB["q"], dB["k"], dB["v"],
+                                 dB["alpha"], dB["beta"], dB["parent"], u_prev=uA, u_out=uB,
+                                 status=st)
+    torch.cuda.synchronize()
+    oref, Sref, rst = oracle_commit_verify(A, B, path, plen)
+    assert host(st).tolist() == rst.tolist() == [0, 2, 2, 0]
+    Sh, oh, uh = host(S), host(outB), host(uB)
+    for b in (1, 2, 3):
+        assert np.array_equal(Sh[b], A.S0[b]), b
+    assert oracle.rel_err(Sh[0], Sref[0]) <= BF16_GATE
+    assert oracle.rel_err(oh, oref) <= BF16_GATE
+    UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert oracle.rel_err(uh, UB) <= BF16_GATE
 
 
 # ---------------------------------------------------------------------------
