@@ -3,14 +3,16 @@
 // One workgroup per (sequence, head); the stages (topology, transposed Gram
 // tiles, mask and decay, tiled block inverse, Q S0 / K S0, solve, output)
 // are in tree_verify.hpp, where the method is described.  This kernel adds
-// the load schedule: Q/K/V tiles first (16-byte row chunks into LDS), then
-// the S0 slab.  A wave that issues the 64 KiB slab stalls until the memory
-// system has accepted it, so the two workgroups resident on a CU (dispatch
-// rounds r and r + 1) take opposite orders: one streams its state first and
-// builds the tree matrices afterwards, the other builds them while its
-// neighbour streams, then streams its own.  LDS: 79 KB, two workgroups per
-// CU; the V tile and the solve blocks share bytes, and the output rows are
-// staged over the dead Q/K tiles.
+// the load schedule: Q/K tiles first (16-byte row chunks into LDS), then
+// the S0 slab, then the v rows, which only the solve needs: they wait in
+// registers and pass through the K tile's place once the contraction has
+// read it, so the tree matrices never wait for them.  A wave that issues
+// the 64 KiB slab stalls until the memory system has accepted it, so the
+// two workgroups resident on a CU (dispatch rounds r and r + 1) take
+// opposite orders: one streams its state first and builds the tree
+// matrices afterwards, the other builds them while its neighbour streams,
+// then streams its own.  LDS: 79 KB, two workgroups per CU; the output rows
+// are staged over the dead Q/K tiles.
 #include "internal.hpp"
 #include "tree_verify.hpp"
 
@@ -25,7 +27,6 @@ struct Smem {
         float o[kN][kD + 4];
     } a;
     union {
-        uint16_t v[kN][kQK];
         SolveBlocks s;
     } b;
     Topo tp;
@@ -40,29 +41,28 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     const Lane c = lane_coords();
     const Seq s = seq_coords(blockIdx.x, n, H);
 
-    // ---- 1. gates first (wave 3), then the Q, K, V tiles; topology while
+    // ---- 1. gates first (wave 3), then the Q and K tiles; topology while
     //         the tiles are in flight
     const Gates gt = load_gates(c, s, parent, alpha, beta);
     uint4 rq[4], rk[4], rv[4];
     load_rows(c, s, q, rq);
     load_rows(c, s, k, rk);
-    load_rows(c, s, v, rv);
     if (c.w == 3) topology(c, s, gt, sm.tp, status, true);
     store_rows_permuted(c, rq, sm.a.t.q);
     store_rows_permuted(c, rk, sm.a.t.k);
-    store_rows(c, rv, sm.b.v);
     lds_barrier();
 
     const bool state_first = ((blockIdx.x / ncu) & 1) == 0;
     const float *slab = S0 + (size_t)blockIdx.x * kD * kD;
     f32x16 st[4];
-    if (state_first) load_state(st, slab, c.col, c.h);
+    if (state_first) {
+        load_state(st, slab, c.col, c.h);
+        load_rows(c, s, v, rv);
+    }
 
-    // ---- 2. transposed Gram tiles (waves 0-2), V -> registers
+    // ---- 2. transposed Gram tiles (waves 0-2)
     f32x16 gc, ga;
     if (c.w < 3) gram(c, sm.a.t, gc, ga);
-    uint32_t vpk[2][8];
-    v_to_regs(c, sm.b.v, vpk);
     lds_barrier();
     if (sm.tp.bad) {
         store_nan(c, s, out);
@@ -75,10 +75,19 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     inverse(c, sm.b.s);
 
     // ---- 5. P = Q S0, R = K S0
-    if (!state_first) load_state(st, slab, c.col, c.h);
+    if (!state_first) {
+        load_state(st, slab, c.col, c.h);
+        load_rows(c, s, v, rv);
+    }
     f32x16 P[2], R[2];
     contract(c, sm.a.t, st, P, R);
+    // the V tile through the K tile's place into this lane's columns (the
+    // first block's staging rows lie in the Q tile's place)
     lds_barrier();
+    store_rows(c, rv, sm.a.t.k);
+    lds_barrier();
+    uint32_t vpk[2][8];
+    v_to_regs(c, sm.a.t.k, vpk);
 
     // ---- 6. solve and output, 7. whole-row stores
     // the first block's rows leave while the second block is solved
