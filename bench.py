@@ -9,20 +9,20 @@ iteration).  Workload: one GDN layer, batch 16, 32 heads, d_k = d_v = 128,
 q/k/v, fp32 gates and state; seeded synthetic inputs (gdn_synth), no model
 weights.
 
-R independent input sets (default 16, ~1.2 GB in total plus two 16 MiB
-pseudo-value buffers per set) are resident in HBM before timing and are used
-round-robin, so the 256 MiB Infinity Cache cannot serve repeated reads.
-Step i works on set i mod R: its state is advanced along the accepted path
-of its own tree, from the pseudo-values its previous step wrote from that
-same state (the commit then needs no solve), and its tree is verified again,
-writing fresh pseudo-values; a first call per set (no commit) seeds them.
+R independent input sets (default 16, ~1.2 GB in total plus pseudo-value
+buffers) are resident in HBM before timing and are used round-robin, so the
+256 MiB Infinity Cache cannot serve repeated reads.  Step i works on set
+i mod R: its state is advanced along the accepted path of its own tree,
+from the pseudo-values its previous step wrote from that same state (the
+commit then needs no solve), and its tree is verified again, writing fresh
+pseudo-values; a first call per set (no commit) seeds them.
 
 Timed regions (HIP events on the launch stream, start and end only, so no
 event fence sits between kernels), K launches each after 2R untimed ones:
-the fused step (the headline value), the fused step with the commit solving
-for the pseudo-values itself (set i - 1's path), the same step as two
-launches (gdn_tree_verify then gdn_tree_commit), verify alone and commit
-alone.  Launches are prepared
+the fused step (the headline value), the same with fp16 pseudo-values, the
+fused step with the commit solving for the pseudo-values itself (set i - 1's
+path), the same step as two launches (gdn_tree_verify then gdn_tree_commit),
+verify alone and commit alone.  Launches are prepared
 once (binding Launch objects), so the host enqueues faster than the GPU
 drains and the events time the GPU.
 
@@ -217,11 +217,11 @@ def main():
     # pseudo-values (two buffers per set, alternating).  fused_solve,
     # reported beside it: set i's state is advanced along set i - 1's path
     # with the commit solving for the pseudo-values itself.
-    fused_u, fused_solve, ver, com = [], [], [], []
+    fused_u, fused_u16, seed_u16, fused_solve, ver, com = [], [], [], [], [], []
     for i, d in enumerate(sets):
-        d["u"] = [torch.empty((batch, n, H, dv), dtype=torch.float32, device="cuda")
-                  for _ in range(2)]
         own = (d["k"], d["v"], d["alpha"], d["beta"], d["parent"])
+        for key, udt in (("u", torch.float32), ("u16", torch.float16)):
+            d[key] = [torch.empty((batch, n, H, dv), dtype=udt, device="cuda") for _ in range(2)]
         # first call on this state: no commit, pseudo-values into u[0]
         g.commit_verify(d["S"], d["path"], torch.zeros_like(d["plen"]), own, d["q"], d["k"],
                         d["v"], d["alpha"], d["beta"], d["parent"], out=d["out"],
@@ -231,6 +231,15 @@ def main():
                                         out=d["out"], u_prev=d["u"][par],
                                         u_out=d["u"][1 - par], stream=stream, prepare=True)
                         for par in range(2)])
+        seed_u16.append(g.commit_verify(d["S"], d["path"], torch.zeros_like(d["plen"]), own,
+                                        d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                        d["parent"], out=d["out"], u_out=d["u16"][0],
+                                        stream=stream, prepare=True))
+        fused_u16.append([g.commit_verify(d["S"], d["path"], d["plen"], own, d["q"], d["k"],
+                                          d["v"], d["alpha"], d["beta"], d["parent"],
+                                          out=d["out"], u_prev=d["u16"][par],
+                                          u_out=d["u16"][1 - par], stream=stream, prepare=True)
+                          for par in range(2)])
         p = sets[(i - 1) % R]
         fused_solve.append(g.commit_verify(d["S"], p["path"], p["plen"],
                                            (p["k"], p["v"], p["alpha"], p["beta"], p["parent"]),
@@ -286,13 +295,31 @@ def main():
         ver[i]()
         com[i]()
 
+    visits16 = [0] * R
+
+    def fused_step_u16(i):
+        fused_u16[i][visits16[i] & 1]()
+        visits16[i] += 1
+
     ms_step = timed("fused", fused_step)
+    # the fp16 pseudo-value chain starts from a first call on each set's
+    # current state
+    for i in range(R):
+        seed_u16[i]()
+    u16_ms = timed("fused_u16", fused_step_u16)
+    # back on the fp32 chain: reseed it from the current states
+    for i, d in enumerate(sets):
+        g.commit_verify(d["S"], d["path"], torch.zeros_like(d["plen"]),
+                        (d["k"], d["v"], d["alpha"], d["beta"], d["parent"]), d["q"], d["k"],
+                        d["v"], d["alpha"], d["beta"], d["parent"], out=d["out"],
+                        u_out=d["u"][visits[i] & 1], stream=stream)
     solve_ms = timed("fused_solve", lambda i: fused_solve[i]())
     sep_ms = timed("separate", separate)
     ver_ms = timed("verify", lambda i: ver[i]())
     com_ms = timed("commit", lambda i: com[i]())
     recheck_ms = timed("fused_recheck", fused_step)
-    log(f"fused {ms_step * 1e3:.2f} us (again at the end: {recheck_ms * 1e3:.2f} us; commit "
+    log(f"fused {ms_step * 1e3:.2f} us (again at the end: {recheck_ms * 1e3:.2f} us; fp16 "
+        f"pseudo-values: {u16_ms * 1e3:.2f} us; commit "
         f"solving for its pseudo-values: {solve_ms * 1e3:.2f} us), "
         f"separate {sep_ms * 1e3:.2f} us, verify {ver_ms * 1e3:.2f} "
         f"us, commit {com_ms * 1e3:.2f} us per launch (host enqueue "
@@ -341,7 +368,7 @@ def main():
     # inputs, 8 rotating sets of width-8 best-first trees of 126 nodes
     cmp126 = None
     if not args.no_compare:
-        sets = fused_u = fused_solve = ver = com = None
+        sets = fused_u = fused_u16 = seed_u16 = fused_solve = ver = com = None
         torch.cuda.empty_cache()
         c_sets = []
         for s_ in range(8):
@@ -431,6 +458,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "gdn_tree_commit_verify", "algorithmic_bytes_per_launch": fbytes,
                      "mean_launch_us": step_s * 1e6},
+        "fused_u16_us": u16_ms * 1e3,
         "fused_commit_solving_us": solve_ms * 1e3,
         "separate_step_us": sep_ms * 1e3,
         "separate_step_nodes_per_s": nodes / (sep_ms * 1e-3),

@@ -34,6 +34,7 @@ FAULT_BAD_PARENT = 1
 FAULT_BAD_PATH = 2
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2     # pseudo-values of commit_verify only
 MAX_NODES = 128
 MAX_DIM = 128
 MAX_CANDIDATES = 32
@@ -78,7 +79,7 @@ def load() -> ctypes.CDLL:
         lib.gdn_tree_commit.argtypes = [P, P, P, I, P, P, I, P, P, P, I, I, I, I, I, P, P]
         lib.gdn_tree_commit.restype = I
         lib.gdn_tree_commit_verify.argtypes = [P, P, P, I, P, P, P, P, P, P, I, P, P, P, I, P, P,
-                                               P, P, P, I, I, I, I, I, P, P]
+                                               P, P, P, I, I, I, I, I, I, P, P]
         lib.gdn_tree_commit_verify.restype = I
         lib.gdn_tree_build.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
         lib.gdn_tree_build.restype = I
@@ -248,10 +249,11 @@ def commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent, out=Non
     (in place), then verify the new tree from the committed S.
 
     prev = (k_prev, v_prev, alpha_prev, beta_prev, parent_prev): the tensors
-    of the tree the path was accepted from.  u_out (fp32 [batch][n][H][d_v])
-    receives the new tree's pseudo-values; u_prev, the previous call's
-    u_out on this same S, lets the commit skip its solve.  Returns out
-    [batch][n][H][d_v] (prepare=True: a Launch instead of launching).
+    of the tree the path was accepted from.  u_out ([batch][n][H][d_v], fp32
+    or fp16) receives the new tree's pseudo-values; u_prev, the previous
+    call's u_out on this same S (same dtype), lets the commit skip its
+    solve.  Returns out [batch][n][H][d_v] (prepare=True: a Launch instead
+    of launching).
     """
     torch = _torch()
     lib = load()
@@ -275,8 +277,9 @@ def commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent, out=Non
     _need(alpha_prev, "alpha_prev", (torch.float32,), (batch, n_prev, H))
     _need(beta_prev, "beta_prev", (torch.float32,), (batch, n_prev, H))
     _need(parent_prev, "parent_prev", (torch.int32,), (batch, n_prev))
+    udt = (torch.float32, torch.float16)
     if u_prev is not None:
-        _need(u_prev, "u_prev", (torch.float32,), (batch, n_prev, H, dv))
+        _need(u_prev, "u_prev", udt, (batch, n_prev, H, dv))
     _need(S, "S", (torch.float32,), (batch, H, dk, dv))
     _need(path, "path", (torch.int32,))
     if path.dim() != 2 or path.shape[0] != batch:
@@ -286,13 +289,17 @@ def commit_verify(S, path, path_len, prev, q, k, v, alpha, beta, parent, out=Non
         out = torch.empty((batch, n, H, dv), dtype=torch.float32, device=q.device)
     _need(out, "out", (torch.float32,), (batch, n, H, dv))
     if u_out is not None:
-        _need(u_out, "u_out", (torch.float32,), (batch, n, H, dv))
+        _need(u_out, "u_out", udt, (batch, n, H, dv))
+    if u_prev is not None and u_out is not None and u_prev.dtype != u_out.dtype:
+        raise ValueError("u_prev and u_out must share a dtype")
+    u_given = u_out if u_out is not None else u_prev
+    u_dtype = DTYPE_F16 if (u_given is not None and u_given.dtype == torch.float16) else 0
     if status is not None:
         _need(status, "status", (torch.int32,), (batch,))
     args = (_ptr(S), _ptr(path), _ptr(path_len), int(path.shape[1]), _ptr(k_prev),
             _ptr(v_prev), _ptr(alpha_prev), _ptr(beta_prev), _ptr(parent_prev), _ptr(u_prev),
             n_prev, _ptr(q), _ptr(k), _ptr(v), _qkv_dtype(q), _ptr(alpha), _ptr(beta),
-            _ptr(parent), _ptr(out), _ptr(u_out), batch, n, H, dk, dv, _ptr(status),
+            _ptr(parent), _ptr(out), _ptr(u_out), u_dtype, batch, n, H, dk, dv, _ptr(status),
             _stream(stream))
     return _issue("gdn_tree_commit_verify", lib.gdn_tree_commit_verify, args,
                   (S, path, path_len, *prev, u_prev, q, k, v, alpha, beta, parent, out, u_out,

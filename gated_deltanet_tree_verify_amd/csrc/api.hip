@@ -104,17 +104,19 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path, const int32_t *path_le
 gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *path_len,
                                   int max_path, const void *k_prev, const void *v_prev,
                                   const float *alpha_prev, const float *beta_prev,
-                                  const int32_t *parent_prev, const float *u_prev, int n_prev,
+                                  const int32_t *parent_prev, const void *u_prev, int n_prev,
                                   const void *q, const void *k, const void *v,
                                   gdn_dtype qkv_dtype, const float *alpha, const float *beta,
-                                  const int32_t *parent, float *out, float *u_out, int batch,
-                                  int n, int H, int d_k, int d_v, int32_t *status,
-                                  void *stream) {
+                                  const int32_t *parent, float *out, void *u_out,
+                                  gdn_dtype u_dtype, int batch, int n, int H, int d_k, int d_v,
+                                  int32_t *status, void *stream) {
     if (!S || !path || !path_len || !k_prev || !v_prev || !alpha_prev || !beta_prev ||
         !parent_prev || !q || !k || !v || !alpha || !beta || !parent || !out)
         return GDN_ERR_INVALID_ARG;
     if (qkv_dtype != GDN_DTYPE_F32 && qkv_dtype != GDN_DTYPE_BF16) return GDN_ERR_INVALID_ARG;
     if (max_path < 1) return GDN_ERR_INVALID_ARG;
+    if ((u_prev || u_out) && u_dtype != GDN_DTYPE_F32 && u_dtype != GDN_DTYPE_F16)
+        return GDN_ERR_INVALID_ARG;
     const void *ptrs[] = {S,    path, path_len, k_prev, v_prev, alpha_prev, beta_prev, parent_prev,
                           u_prev, q,  k,        v,      alpha,  beta,       parent,    out,
                           u_out, status};
@@ -128,7 +130,8 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
          parent_prev, batch, n_prev, H, d_k, d_v, status},
         {q, k, v, qkv_dtype, alpha, beta, parent, S, out, batch, n, H, d_k, d_v, status, true},
         u_prev,
-        u_out};
+        u_out,
+        u_dtype == GDN_DTYPE_F16};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::commit_verify_mfma_supports(a)) return from_hip(gdn::launch_commit_verify_mfma(a, s));
     if (u_out) return GDN_ERR_UNSUPPORTED;

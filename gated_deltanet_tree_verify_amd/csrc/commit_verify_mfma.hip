@@ -125,17 +125,18 @@ __device__ __forceinline__ bool path_valid(const PathLanes &p, int m, int max_pa
 // than the first chunk (32 slots with pseudo-values given, else 16), so the
 // later chunks are applied too; without it a longer path is never read
 // (the host takes the kLong instance whenever max_path exceeds the first
-// chunk), and the kernel carries no code and no registers for them.
-template <bool kU, bool kUout, bool kLong>
+// chunk), and the kernel carries no code and no registers for them.  kUh:
+// u_prev and u_out hold fp16 values (fp32 otherwise).
+template <bool kU, bool kUout, bool kLong, bool kUh>
 __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     float *__restrict__ S, const int32_t *__restrict__ path, const int32_t *__restrict__ path_len,
     int max_path, const uint16_t *__restrict__ k_prev, const uint16_t *__restrict__ v_prev,
     const float *__restrict__ alpha_prev, const float *__restrict__ beta_prev,
-    const int32_t *__restrict__ parent_prev, const float *__restrict__ u_prev, int n_prev,
+    const int32_t *__restrict__ parent_prev, const void *__restrict__ u_prev, int n_prev,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ alpha,
     const float *__restrict__ beta, const int32_t *__restrict__ parent,
-    float *__restrict__ out, float *__restrict__ u_out, int n, int H, int ncu,
+    float *__restrict__ out, void *__restrict__ u_out, int n, int H, int ncu,
     int32_t *__restrict__ status) {
     __shared__ Smem sm;
     const Lane c = lane_coords();
@@ -209,12 +210,14 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
 
     // the first chunk's pseudo-values (this wave's columns), in flight
     // during the tree matrices
-    const float *u_head = u_prev + prow0;
-    const uint32_t ubytes = (uint32_t)((size_t)n_prev * H * kD * 4);
+    constexpr size_t ues = kUh ? 2 : 4;   // bytes per pseudo-value
+    const void *u_head = static_cast<const char *>(u_prev) + prow0 * ues;
+    const uint32_t ubytes = (uint32_t)((size_t)n_prev * H * kD * ues);
     f32x16 U0 = {};
     if (mlen > 0 && mlen <= kMaxPathIds) {
         if constexpr (kU)
-            U0 = pc::load_u_chunk(u_head, ubytes, sm.pid, 0, min(32, mlen), H * kD, c.col, c.h);
+            U0 = pc::load_u_chunk<kUh>(u_head, ubytes, sm.pid, 0, min(32, mlen), H * kD, c.col,
+                                       c.h);
         else   // the first chunk's values, in this wave's columns
             U0 = pc::load_v_chunk16(v_prev + prow0, pbytes, sm.pid, 0, min(pc::kC16, mlen),
                                     H * kD, c.col, c.h);
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             for (int c0 = 32; c0 < mlen; c0 += 32) {
                 const int mc = min(32, mlen - c0);
                 const f32x16 Uc =
-                    pc::load_u_chunk(u_head, ubytes, sm.pid, c0, mc, H * kD, c.col, c.h);
+                    pc::load_u_chunk<kUh>(u_head, ubytes, sm.pid, c0, mc, H * kD, c.col, c.h);
                 if (c.w == 3) {
                     const int rj = c.l >> 1;
                     const pc::KeyRows32 kr = pc::load_keys32(
@@ -330,7 +333,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     if (!tree_ok) {
         if (commit) store_state(st, slab, c.col, c.h);
         store_nan(c, s, out);
-        if constexpr (kUout) store_nan(c, s, u_out);
+        if constexpr (kUout) {
+            if constexpr (kUh) store_nan_f16(c, s, static_cast<uint16_t *>(u_out));
+            else store_nan(c, s, static_cast<float *>(u_out));
+        }
         return;
     }
     f32x16 P[2], R[2];
@@ -354,10 +360,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     SolveCarry cy;
     f32x16 u0, o0, u1, o1;
     solve_block0(c, sm.tp, sm.b.s, P, R, vpk, u0, o0, cy);
-    store_block<kUout>(c, s, sm.a.o, o0, out, u0, u_out, 0);
+    store_block<kUout, kUh>(c, s, sm.a.o, o0, out, u0, u_out, 0);
     solve_block1(c, sm.b.s, P, cy, u1, o1);
     lds_barrier();   // every thread has read the first block from the staging area
-    store_block<kUout>(c, s, sm.a.o, o1, out, u1, u_out, 32);
+    store_block<kUout, kUh>(c, s, sm.a.o, o1, out, u1, u_out, 32);
 }
 
 }  // namespace
@@ -368,23 +374,40 @@ bool commit_verify_mfma_supports(const CommitVerifyArgs &a) {
            a.v.H <= 4096;
 }
 
-hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s) {
-    const bool lng = a.c.max_path > (a.u_prev ? 32 : pc::kC16);
-    auto kern = a.u_prev ? (a.u_out ? (lng ? commit_verify_mfma_kernel<true, true, true>
-                                           : commit_verify_mfma_kernel<true, true, false>)
-                                    : (lng ? commit_verify_mfma_kernel<true, false, true>
-                                           : commit_verify_mfma_kernel<true, false, false>))
-                         : (a.u_out ? (lng ? commit_verify_mfma_kernel<false, true, true>
-                                           : commit_verify_mfma_kernel<false, true, false>)
-                                    : (lng ? commit_verify_mfma_kernel<false, false, true>
-                                           : commit_verify_mfma_kernel<false, false, false>));
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.v.batch * a.v.H)), dim3(kThreads), 0, s, a.c.S,
+namespace {
+
+template <bool kU, bool kUout, bool kLong, bool kUh>
+hipError_t launch_cv(const CommitVerifyArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((commit_verify_mfma_kernel<kU, kUout, kLong, kUh>),
+                       dim3((unsigned)(a.v.batch * a.v.H)), dim3(kThreads), 0, s, a.c.S,
                        a.c.path, a.c.path_len, a.c.max_path, (const uint16_t *)a.c.k,
                        (const uint16_t *)a.c.v, a.c.alpha, a.c.beta, a.c.parent, a.u_prev,
                        a.c.n, (const uint16_t *)a.v.q, (const uint16_t *)a.v.k,
                        (const uint16_t *)a.v.v, a.v.alpha, a.v.beta, a.v.parent, a.v.out,
                        a.u_out, a.v.n, a.v.H, device_cu_count(), a.v.status);
     return hipGetLastError();
+}
+
+template <bool kU, bool kUout, bool kLong>
+hipError_t launch_cv_u(const CommitVerifyArgs &a, hipStream_t s) {
+    if constexpr (kU || kUout) {
+        if (a.u_half) return launch_cv<kU, kUout, kLong, true>(a, s);
+    }
+    return launch_cv<kU, kUout, kLong, false>(a, s);
+}
+
+template <bool kU, bool kUout>
+hipError_t launch_cv_len(const CommitVerifyArgs &a, hipStream_t s) {
+    // paths longer than the first chunk need the chunk loop
+    if (a.c.max_path > (kU ? 32 : pc::kC16)) return launch_cv_u<kU, kUout, true>(a, s);
+    return launch_cv_u<kU, kUout, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s) {
+    if (a.u_prev) return a.u_out ? launch_cv_len<true, true>(a, s) : launch_cv_len<true, false>(a, s);
+    return a.u_out ? launch_cv_len<false, true>(a, s) : launch_cv_len<false, false>(a, s);
 }
 
 }  // namespace gdn

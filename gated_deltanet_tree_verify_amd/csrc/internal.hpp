@@ -38,8 +38,9 @@ struct CommitArgs {
 struct CommitVerifyArgs {
     CommitArgs c;
     VerifyArgs v;
-    const float *u_prev;   // previous tree's pseudo-values, or null (solve for them)
-    float *u_out;          // this tree's pseudo-values, or null
+    const void *u_prev;    // previous tree's pseudo-values, or null (solve for them)
+    void *u_out;           // this tree's pseudo-values, or null
+    bool u_half;           // u_prev / u_out hold fp16 (else fp32)
 };
 
 // number of compute units of the current device (cached per device); only

@@ -158,6 +158,17 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNT));
 }
 
+// 16-byte store of 8 fp16 values (raw bits), non-temporal
+__device__ __forceinline__ void store16h(uint16_t *p, const uint4 &x) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
 // 16-byte store of an output row segment, non-temporal
 __device__ __forceinline__ void store16(float *p, const float4 &x) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -693,17 +693,25 @@ __device__ __forceinline__ void build_keys32(KeyChunk32 &kc, Chunk16Aux &ax, con
 
 // this lane's u entries of the chunk's slots crow(r, h) (zero past the chunk):
 // u_head points at node 0 of this (sequence, head) of a [batch][n][H][128]
-// fp32 tensor, rs = H * 128, bytes = n * rs * 4
-__device__ __forceinline__ f32x16 load_u_chunk(const float *u_head, uint32_t bytes, const int *pid,
+// tensor of fp32 (or, with kHalf, fp16) values, rs = H * 128, bytes = n * rs
+// times the element size
+template <bool kHalf>
+__device__ __forceinline__ f32x16 load_u_chunk(const void *u_head, uint32_t bytes, const int *pid,
                                                int c0, int mc, int rs, int col, int h) {
     const __amdgpu_buffer_rsrc_t ur = make_rsrc(u_head, bytes);
+    constexpr uint32_t es = kHalf ? 2 : 4;
     f32x16 U;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int j = crow(r, h);
         const uint32_t off =
-            j < mc ? (uint32_t)(pid[min(c0 + j, kMaxPath - 1)] * rs + col) * 4 : bytes;
-        U[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ur, (int)off, 0, kNT));
+            j < mc ? (uint32_t)(pid[min(c0 + j, kMaxPath - 1)] * rs + col) * es : bytes;
+        if constexpr (kHalf) {
+            const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(ur, (int)off, 0, kNT);
+            U[r] = static_cast<float>(__builtin_bit_cast(_Float16, x));
+        } else {
+            U[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ur, (int)off, 0, kNT));
+        }
     }
     return U;
 }

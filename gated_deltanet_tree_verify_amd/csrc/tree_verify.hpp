@@ -468,29 +468,59 @@ __device__ __forceinline__ void solve_block1(const Lane &c, const SolveBlocks &s
     o1 = mm3<kBL>(sb.yh[2], sb.yl[2], split_tile(u1), o1, c.m, c.h);
 }
 
-// Rows row0 .. row0 + 31 of one or two [batch][n][H][128] fp32 outputs, from
-// a 32-row result tile each, through LDS as whole 512-byte rows: tile a goes
-// to dst_a through staging rows 0..31, tile b (when kPair) to dst_b through
-// rows 32..63.  Contains one barrier; the staging area must be free.
-template <bool kPair>
+// Rows row0 .. row0 + 31 of one or two [batch][n][H][128] outputs, from a
+// 32-row result tile each, through LDS as whole rows: tile a goes to the fp32
+// dst_a through staging rows 0..31, tile b (when kPair) to dst_b through rows
+// 32..63, as fp32 or, with kHalfB, as fp16 rounded to nearest (256-byte
+// rows).  Contains one barrier; the staging area must be free.
+template <bool kPair, bool kHalfB = false>
 __device__ __forceinline__ void store_block(const Lane &c, const Seq &s, float (*ostage)[kD + 4],
                                             const f32x16 &a, float *dst_a, const f32x16 &b,
-                                            float *dst_b, int row0) {
+                                            void *dst_b, int row0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         ostage[crow(r, c.h)][c.col] = a[r];
         if constexpr (kPair) ostage[32 + crow(r, c.h)][c.col] = b[r];
     }
     lds_barrier();
+    constexpr int kFullRows = (kPair && !kHalfB) ? 64 : 32;   // rows stored as fp32
 #pragma unroll
-    for (int it = 0; it < (kPair ? 8 : 4); ++it) {
+    for (int it = 0; it < kFullRows / 8; ++it) {
         const int e = c.tid + kThreads * it, row = e >> 5, c4 = (e & 31) * 4;
         const int node = row0 + (row & 31);
-        float *dst = (kPair && row >= 32) ? dst_b : dst_a;
+        float *dst = (kPair && row >= 32) ? static_cast<float *>(dst_b) : dst_a;
         if (node < s.n)
             store16(dst + s.base + node * s.rstride + c4,
                     *reinterpret_cast<const float4 *>(&ostage[row][c4]));
     }
+    if constexpr (kPair && kHalfB) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
+            const int node = row0 + row;
+            const float4 x0 = *reinterpret_cast<const float4 *>(&ostage[32 + row][c8]);
+            const float4 x1 = *reinterpret_cast<const float4 *>(&ostage[32 + row][c8 + 4]);
+            const uint4 h = make_uint4(
+                (uint32_t)f16_bits(x0.x) | ((uint32_t)f16_bits(x0.y) << 16),
+                (uint32_t)f16_bits(x0.z) | ((uint32_t)f16_bits(x0.w) << 16),
+                (uint32_t)f16_bits(x1.x) | ((uint32_t)f16_bits(x1.y) << 16),
+                (uint32_t)f16_bits(x1.z) | ((uint32_t)f16_bits(x1.w) << 16));
+            if (node < s.n)
+                store16h(static_cast<uint16_t *>(dst_b) + s.base + node * s.rstride + c8, h);
+        }
+    }
+}
+
+// NaN rows of an fp16 [batch][n][H][128] tensor (this lane's entries)
+__device__ __forceinline__ void store_nan_f16(const Lane &c, const Seq &s, uint16_t *out) {
+    uint16_t *orow = out + s.base + c.col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 32 * t + crow(r, c.h);
+            if (i < s.n) orow[(size_t)i * s.rstride] = 0x7e00;   // quiet NaN
+        }
 }
 
 // NaN rows for a sequence whose tree is malformed (this lane's entries)

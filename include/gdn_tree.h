@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 6
+#define GDN_TREE_ABI_VERSION 7
 #define GDN_MAX_NODES 128
 #define GDN_MAX_DIM 128
 #define GDN_MAX_CANDIDATES 32   /* child candidates per node, gdn_tree_build */
@@ -65,7 +65,9 @@ typedef enum {
     GDN_ERR_HIP = -3          /* the HIP runtime refused a launch           */
 } gdn_status;
 
-typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
+/* element types: q/k/v take F32 or BF16; the pseudo-values of
+   gdn_tree_commit_verify take F32 or F16 */
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1, GDN_DTYPE_F16 = 2 } gdn_dtype;
 
 /* device-detected fault flags (status[b]) */
 #define GDN_FAULT_BAD_PARENT 1 /* some parent[i] outside [-1, i)             */
@@ -146,14 +148,21 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path,
  * Pseudo-values (optional).  The verify solves for u_i = beta_i (v_i -
  * alpha_i S_p^T k_i) of every node (S_p: the state at i's parent), and the
  * state after a path is e^{g} S + sum_s e^{g - g_s} k_s u_s^T.  u_out
- * [batch][n][H][d_v] fp32, when not NULL, receives the new tree's u (NaN
- * rows for a malformed tree).  u_prev [batch][n_prev][H][d_v], when not
- * NULL, must be the u_out that the call verifying the previous tree wrote
- * from this same S: the commit then applies that sum directly instead of
+ * [batch][n][H][d_v], when not NULL, receives the new tree's u (NaN rows
+ * for a malformed tree).  u_prev [batch][n_prev][H][d_v], when not NULL,
+ * must be the u_out that the call verifying the previous tree wrote from
+ * this same S: the commit then applies that sum directly instead of
  * solving again (faster; same result up to rounding).  Other u_prev values
  * give that sum, not the commit.  The first call of a decode loop passes
- * path_len = 0 and u_prev = NULL.  u_out needs bf16, d_k = d_v = 128 and
- * n <= 64 (else GDN_ERR_UNSUPPORTED); u_prev is ignored on other shapes.
+ * path_len = 0 and u_prev = NULL.  u_dtype (read only when u_prev or u_out
+ * is given) is the element type of both: GDN_DTYPE_F32, or GDN_DTYPE_F16
+ * for half the bytes, u rounded to the nearest fp16 when written (relative
+ * error at most 2^-11 for |u| in [2^-14, 65504]; larger |u| overflows, so
+ * F16 is for pseudo-values in that range).  The committed state then
+ * differs from the solving commit by at most 2^-11 sum_s e^{g - g_s}
+ * |k_s| |u_s|^T elementwise (plus rounding).  u_out needs bf16,
+ * d_k = d_v = 128 and n <= 64 (else GDN_ERR_UNSUPPORTED); u_prev is ignored
+ * on other shapes.
  *
  * out and u_out must not alias any input, S must not alias any other
  * argument; the previous-tree tensors may be the same tensors as the new
@@ -165,13 +174,13 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path,
                                   const float *alpha_prev,
                                   const float *beta_prev,
                                   const int32_t *parent_prev,
-                                  const float *u_prev, int n_prev,
+                                  const void *u_prev, int n_prev,
                                   const void *q, const void *k, const void *v,
                                   gdn_dtype qkv_dtype, const float *alpha,
                                   const float *beta, const int32_t *parent,
-                                  float *out, float *u_out, int batch, int n,
-                                  int H, int d_k, int d_v, int32_t *status,
-                                  void *stream);
+                                  float *out, void *u_out, gdn_dtype u_dtype,
+                                  int batch, int n, int H, int d_k, int d_v,
+                                  int32_t *status, void *stream);
 
 /*
  * Width-w best-first draft-tree construction (the DFlash-TfM page's tree

@@ -88,13 +88,14 @@ def test_commit_rejects(lib):
 
 
 def _commit_verify(lib, null=None, ptr=FAKE, max_path=4, n_prev=8, batch=1, n=8, H=1, dk=16,
-                   dv=16, dtype=1, status=None, u_prev=None, u_out=None):
+                   dv=16, dtype=1, status=None, u_prev=None, u_out=None, u_dtype=0):
     p = [ptr] * 15    # S path path_len k_prev v_prev a_prev b_prev par_prev q k v a b par out
     if null is not None:
         p[null] = None
     return lib.gdn_tree_commit_verify(p[0], p[1], p[2], max_path, p[3], p[4], p[5], p[6], p[7],
                                       u_prev, n_prev, p[8], p[9], p[10], dtype, p[11], p[12],
-                                      p[13], p[14], u_out, batch, n, H, dk, dv, status, None)
+                                      p[13], p[14], u_out, u_dtype, batch, n, H, dk, dv, status,
+                                      None)
 
 
 @pytest.mark.parametrize("null", range(15))
@@ -108,6 +109,9 @@ def test_commit_verify_null_pointer(lib, null):
     (dict(dtype=2), -1), (dict(ptr=MISALIGNED), -1), (dict(status=MISALIGNED), -1),
     (dict(u_prev=MISALIGNED), -1), (dict(u_out=MISALIGNED), -1),
     (dict(u_out=FAKE), -2),        # pseudo-values out need the bf16, d = 128, n <= 64 kernel
+    (dict(u_out=FAKE, u_dtype=2), -2),
+    (dict(u_out=FAKE, u_dtype=1), -1),   # pseudo-values are fp32 or fp16
+    (dict(u_prev=FAKE, u_dtype=3), -1),
 ])
 def test_commit_verify_rejects(lib, kw, code):
     assert _commit_verify(lib, **kw) == code

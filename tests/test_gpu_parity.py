@@ -435,17 +435,22 @@ def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype, max_
 # ---------------------------------------------------------------------------
 # fused step with pseudo-values carried from one call to the next
 # ---------------------------------------------------------------------------
-def test_commit_verify_pseudo_values_decode_loop(gpu_lib):
+U_DTYPES = {"fp32": torch.float32, "fp16": torch.float16}
+
+
+@pytest.mark.parametrize("udt", ["fp32", "fp16"])
+def test_commit_verify_pseudo_values_decode_loop(gpu_lib, udt):
     """call 1 verifies tree A (no commit) and writes its u; call 2 commits
     A's accepted path from that u (no solve) and verifies tree B; every
-    output against the oracle"""
-    say("commit-verify with pseudo-values")
+    output against the oracle.  fp16 pseudo-values are the fp32 ones
+    rounded to nearest, bit for bit."""
+    say("commit-verify with pseudo-values", udt)
     A, B = gs.make_config(2, s=5), gs.make_config(2, s=6)
     dA, dB = upload(A), upload(B)
     S = dA["S0"].clone()
     prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
-    uA = torch.full(dA["v"].shape, 7.0, dtype=torch.float32, device="cuda")
-    uB = torch.full(dB["v"].shape, 7.0, dtype=torch.float32, device="cuda")
+    uA = torch.full(dA["v"].shape, 7.0, dtype=U_DTYPES[udt], device="cuda")
+    uB = torch.full(dB["v"].shape, 7.0, dtype=U_DTYPES[udt], device="cuda")
     st = torch.full((16,), -7, dtype=torch.int32, device="cuda")
     zero = dev(np.zeros(16, np.int32))
     pathA, plenA = A.paths(max_path=13)
@@ -459,6 +464,13 @@ def test_commit_verify_pseudo_values_decode_loop(gpu_lib):
     eu = oracle.rel_err(host(uA), UA)
     say("u rel err", eu)
     assert eu <= BF16_GATE
+    if udt == "fp16":
+        u32 = torch.empty(dA["v"].shape, dtype=torch.float32, device="cuda")
+        S2 = dA["S0"].clone()
+        gpu_lib.commit_verify(S2, dev(pathA), zero, prevA, dA["q"], dA["k"], dA["v"],
+                              dA["alpha"], dA["beta"], dA["parent"], u_out=u32)
+        torch.cuda.synchronize()
+        assert torch.equal(uA.view(torch.int16), u32.half().view(torch.int16))
     outB = gpu_lib.commit_verify(S, dev(pathA), dev(plenA), prevA, dB["q"], dB["k"], dB["v"],
                                  dB["alpha"], dB["beta"], dB["parent"], u_prev=uA, u_out=uB,
                                  status=st)
@@ -472,7 +484,8 @@ def test_commit_verify_pseudo_values_decode_loop(gpu_lib):
     assert es <= BF16_GATE and eo <= BF16_GATE and eu <= BF16_GATE
 
 
-def test_commit_verify_pseudo_values_long_path_and_faults(gpu_lib):
+@pytest.mark.parametrize("udt", ["fp32", "fp16"])
+def test_commit_verify_pseudo_values_long_path_and_faults(gpu_lib, udt):
     """a 64-node chain (two 32-slot chunks of known u), a bad path (state
     untouched) and a malformed new tree (NaN outputs and u)"""
     chain = gs.chain_tree(64)
@@ -485,8 +498,8 @@ def test_commit_verify_pseudo_values_long_path_and_faults(gpu_lib):
     dA, dB = upload(A), upload(B)
     S = dA["S0"].clone()
     prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
-    uA = torch.empty(dA["v"].shape, dtype=torch.float32, device="cuda")
-    uB = torch.empty(dB["v"].shape, dtype=torch.float32, device="cuda")
+    uA = torch.empty(dA["v"].shape, dtype=U_DTYPES[udt], device="cuda")
+    uB = torch.empty(dB["v"].shape, dtype=U_DTYPES[udt], device="cuda")
     path, plen = A.paths(max_path=64)
     gpu_lib.commit_verify(S, dev(path), dev(np.zeros(3, np.int32)), prevA, dA["q"], dA["k"],
                           dA["v"], dA["alpha"], dA["beta"], dA["parent"], u_out=uA)
@@ -507,7 +520,8 @@ def test_commit_verify_pseudo_values_long_path_and_faults(gpu_lib):
     assert oracle.rel_err(uh[[0, 1]], UB[[0, 1]]) <= BF16_GATE
 
 
-def test_commit_verify_pseudo_values_short_paths_and_faults(gpu_lib):
+@pytest.mark.parametrize("udt", ["fp32", "fp16"])
+def test_commit_verify_pseudo_values_short_paths_and_faults(gpu_lib, udt):
     """max_path 13 (the first 32-slot chunk holds every path): a clean
     sequence, an out-of-range id, a path longer than max_path, an empty path;
     faulted and empty paths leave the state bit-unchanged"""
@@ -520,8 +534,8 @@ def test_commit_verify_pseudo_values_short_paths_and_faults(gpu_lib):
     dA, dB = upload(A), upload(B)
     S = dA["S0"].clone()
     prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
-    uA = torch.empty(dA["v"].shape, dtype=torch.float32, device="cuda")
-    uB = torch.empty(dB["v"].shape, dtype=torch.float32, device="cuda")
+    uA = torch.empty(dA["v"].shape, dtype=U_DTYPES[udt], device="cuda")
+    uB = torch.empty(dB["v"].shape, dtype=U_DTYPES[udt], device="cuda")
     path, plen = A.paths(max_path=13)
     gpu_lib.commit_verify(S, dev(path), dev(np.zeros(4, np.int32)), prevA, dA["q"], dA["k"],
                           dA["v"], dA["alpha"], dA["beta"], dA["parent"], u_out=uA)
