@@ -11,11 +11,12 @@
 //
 // Schedule.  The only verify work that needs the state is Q S, K S and what
 // follows; the Gram matrices, masks and block inverses of the new tree need
-// only q, k and the parents.  So every wave requests its q and k rows
-// first, its first state tiles once q and k are in, then the rest of its
-// slab (one tile per tree-matrix phase) and its v rows; the tree matrices
-// are built while the state streams in.  Wave 3 also reads the previous path (ids,
-// then the parents that validate it and the first chunk's rows and gates).
+// only q, k and the parents.  So waves 0-2 request the q and k rows first
+// (wave 3 meanwhile reads the gates and the previous path: ids, then the
+// parents that validate it and the first chunk's rows and gates, and builds
+// the topology), every wave its first state tiles once q and k are in, then
+// the rest of its slab (one tile per tree-matrix phase) and last its v rows;
+// the tree matrices are built while the state streams in.
 //   * Pseudo-values carried (u_prev): while waves 0-2 compute the masks,
 //     wave 3 validates the path and lays out the first 32-slot key chunk
 //     over the T rows of the solve blocks, which the inverse writes only in
@@ -118,6 +119,29 @@ __device__ __forceinline__ bool path_valid(const PathLanes &p, int m, int max_pa
     return __ballot(bad) == 0ull;
 }
 
+// 64 node rows of a bf16 [batch][n][H][128] tensor loaded by waves 0-2 alone
+// (192 threads, 16-byte chunks e = tid + 192 it, six per thread, the last
+// partly empty); rows past n read as zero
+__device__ __forceinline__ void load_rows3(const Lane &c, const Seq &s, const uint16_t *src,
+                                           uint4 (&x)[6]) {
+    const uint32_t bytes = (uint32_t)(s.n * s.rstride * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + s.base, bytes);
+#pragma unroll
+    for (int it = 0; it < 6; ++it) {
+        const int e = c.tid + 192 * it, row = e >> 4, c8 = (e & 15) * 8;
+        x[it] = load16(rs, e < 1024 ? (uint32_t)((row * s.rstride + c8) * 2) : bytes);
+    }
+}
+
+__device__ __forceinline__ void store_rows3_permuted(const Lane &c, const uint4 (&x)[6],
+                                                     uint16_t (*dst)[kQK]) {
+#pragma unroll
+    for (int it = 0; it < 6; ++it) {
+        const int e = c.tid + 192 * it, row = e >> 4, c8 = (e & 15) * 8;
+        if (e < 1024) store_row8_permuted(dst[row], c8, x[it]);
+    }
+}
+
 // kU: the previous tree's pseudo-values u_prev are given, so the commit is
 // the rank-m update S <- e^{g_a} S + sum_s e^{g_a - g_s} k_s u_s^T with no
 // solve; otherwise the commit solves for them chunk by chunk.  kUout: the
@@ -161,9 +185,11 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
         if (c.l < lim) pl.id0 = prow[c.l];
         if (64 + c.l < lim) pl.id1 = prow[64 + c.l];
     }
-    uint4 rq[4], rk[4], rv[4];
-    load_rows(c, s, q, rq);
-    load_rows(c, s, k, rk);
+    uint4 rq[6], rk[6], rv[4];
+    if (c.w < 3) {
+        load_rows3(c, s, q, rq);
+        load_rows3(c, s, k, rk);
+    }
     // the state slab is requested one 32-row tile at a time, between the
     // tree-matrix phases: a wave that issues a whole 64 KiB slab stalls
     // until the memory system has accepted all of it
@@ -200,8 +226,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
         for (int i = c.l; i < pc::kKP; i += 64) sm.cx.zk[i] = 0;
         if (c.l < pc::kBL) sm.cx.zt[c.l] = 0;
     }
-    store_rows_permuted(c, rq, sm.a.t.q);
-    store_rows_permuted(c, rk, sm.a.t.k);
+    if (c.w < 3) {
+        store_rows3_permuted(c, rq, sm.a.t.q);
+        store_rows3_permuted(c, rk, sm.a.t.k);
+    }
     // the state once q and k are in: every workgroup's Gram operands are
     // fetched before any of the bulk behind them
     load_state_tile(st[0], 0, slab, c.col, c.h);
@@ -227,10 +255,6 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     f32x16 gc, ga;
     if (c.w < 3) gram(c, sm.a.t, gc, ga);
     load_state_tile(st[2], 2, slab, c.col, c.h);
-    // v is needed only by the solve: its rows are requested behind the
-    // state and wait in registers, so the tree matrices need not wait for
-    // them (the V tile passes through LDS after the contraction)
-    load_rows(c, s, v, rv);
     const bool tree_ok = !sm.tp.bad;
     // wave 3: the previous path's validity (and the fault flags)
     auto validate = [&]() -> bool {
@@ -256,6 +280,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             mask(c, sm.tp, gc, ga, sm.b.s);
         }
         load_state_tile(st[3], 3, slab, c.col, c.h);
+        // v is needed only by the solve: its rows are requested behind the
+        // last state tile and wait in registers (the V tile passes through
+        // LDS after the contraction)
+        load_rows(c, s, v, rv);
         lds_barrier();
         commit = sm.commit_ok && mlen > 0;
         if (tree_ok) {
@@ -296,6 +324,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             mask(c, sm.tp, gc, ga, sm.b.s);
         }
         load_state_tile(st[3], 3, slab, c.col, c.h);
+        // v is needed only by the solve: its rows are requested behind the
+        // last state tile and wait in registers (the V tile passes through
+        // LDS after the contraction)
+        load_rows(c, s, v, rv);
         lds_barrier();
         commit = sm.commit_ok && mlen > 0;
         if (commit && c.w == 0) pc::build16_t(sm.b.kt16.ch, c.l);
