@@ -26,6 +26,11 @@ verify alone and commit alone.  Launches are prepared
 once (binding Launch objects), so the host enqueues faster than the GPU
 drains and the events time the GPU.
 
+Side measurements (not the headline): the integer kernels of the step
+(acceptance walk, path extraction, tree construction); the tree-size-126
+comparison of the tree verify against single-branch recurrent
+verification; verify and commit on the batch-64, 128-node workload.
+
 Prints one JSON line.  `roofline` is for the fused kernel: algorithmic bytes
 per launch / its mean launch time.  `traffic` is read from the committed
 rocprofv3 counter summary when it was taken on the current kernel source,
@@ -163,7 +168,8 @@ def main():
     ap.add_argument("--sets", type=int, default=16, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
-                    help="skip the tree-size-126 tree vs single-branch comparison")
+                    help="skip the tree-size-126 tree vs single-branch comparison and the "
+                         "batch-64 / 128-node side measurement")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -366,7 +372,7 @@ def main():
     # tree-size-126 comparison: the tree verify against single-branch
     # recurrent verification (one chain per root-to-leaf branch) on the same
     # inputs, 8 rotating sets of width-8 best-first trees of 126 nodes
-    cmp126 = None
+    cmp126 = b64 = None
     if not args.no_compare:
         sets = fused_u = fused_u16 = seed_u16 = fused_solve = ver = com = None
         torch.cuda.empty_cache()
@@ -424,6 +430,42 @@ def main():
             f"TFLOP/s; its fp32 floor {floor_us:.0f} us, {floor_us / t_tree:.2f}x the tree)")
         c_sets = tv126 = bv126 = None
 
+        # the batch-64, 128-node workload (a quarter chains, a quarter stars
+        # and 16-ary bushes, half random recursive trees): verify and the
+        # commit of each sequence's accepted branch, 2 rotating sets of
+        # ~0.6 GB each
+        torch.cuda.empty_cache()
+        w3 = gs.CONFIGS[3]
+        b_sets = []
+        for s_ in range(2):
+            ts = gs.make_config(3, s=s_)
+            pth, pl = ts.paths(max_path=w3.n)
+            b_sets.append(dict(q=dev(ts.q_bits.view(np.int16)).view(torch.bfloat16),
+                               k=dev(ts.k_bits.view(np.int16)).view(torch.bfloat16),
+                               v=dev(ts.v_bits.view(np.int16)).view(torch.bfloat16),
+                               alpha=dev(ts.alpha), beta=dev(ts.beta), parent=dev(ts.parent),
+                               S=dev(ts.S0), path=dev(pth), plen=dev(pl),
+                               m=float(np.sum(pl))))
+            b_sets[-1]["out"] = torch.empty((w3.batch, w3.n, w3.H, w3.d_v), dtype=torch.float32,
+                                            device="cuda")
+        vb = [g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"],
+                       out=d["out"], stream=stream, prepare=True) for d in b_sets]
+        cb = [g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"],
+                       d["parent"], stream=stream, prepare=True) for d in b_sets]
+        t_vb = timed_list(vb, 20)
+        t_cb = timed_list(cb, 20)
+        vb_bytes = verify_bytes(w3.batch, w3.n, w3.H, w3.d_k, w3.d_v)
+        cb_bytes = commit_bytes(w3.batch, w3.H, w3.d_k, w3.d_v,
+                                [float(np.mean([d["m"] for d in b_sets]))])
+        b64 = {"workload": w3.name, "verify_us": t_vb, "commit_us": t_cb,
+               "verify_nodes_per_s": w3.batch * w3.n / (t_vb * 1e-6),
+               "verify_hbm_gbps": vb_bytes / (t_vb * 1e-6) / 1e9,
+               "commit_hbm_gbps": cb_bytes / (t_cb * 1e-6) / 1e9,
+               "verify_algorithmic_bytes": vb_bytes, "commit_algorithmic_bytes": cb_bytes}
+        log(f"b64/n128: verify {t_vb:.1f} us ({b64['verify_hbm_gbps']:.0f} GB/s), commit "
+            f"{t_cb:.1f} us ({b64['commit_hbm_gbps']:.0f} GB/s)")
+        b_sets = vb = cb = None
+
     # achievable-bandwidth line: a plain 1 GiB device copy
     src = torch.empty(2**28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -473,6 +515,7 @@ def main():
         "accept_us": accept_us,
         "path_us": path_us,
         "tree126_vs_branch": cmp126,
+        "b64_n128": b64,
     }
     if not args.no_cpu_baseline:
         ts, path, plen = host0
