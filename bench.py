@@ -189,7 +189,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     g.load()
-    w = gs.CONFIGS[WORKLOAD_INDEX]
+    w = gs.WORKLOADS[WORKLOAD_INDEX]
     batch, n, H, dk, dv = w.batch, w.n, w.H, w.d_k, w.d_v
     stream = torch.cuda.current_stream()
 
@@ -435,7 +435,7 @@ def main():
         # commit of each sequence's accepted branch, 2 rotating sets of
         # ~0.6 GB each
         torch.cuda.empty_cache()
-        w3 = gs.CONFIGS[3]
+        w3 = gs.WORKLOADS[3]
         b_sets = []
         for s_ in range(2):
             ts = gs.make_config(3, s=s_)

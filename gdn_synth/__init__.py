@@ -37,7 +37,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "Workload", "TensorSet", "CONFIGS", "make_set", "make_config",
+    "Workload", "TensorSet", "WORKLOADS", "make_set", "make_config",
     "random_recursive_tree", "chain_tree", "star_tree", "kary_bfs_tree",
     "best_first_tree", "mixed_tree_batch", "pick_leaf", "leaves",
     "to_bf16_bits", "bf16_bits_to_f32", "path_to", "select", "slice_set",
@@ -302,7 +302,7 @@ class Workload:
     description: str = ""
 
 
-CONFIGS = [
+WORKLOADS = [
     Workload("tiny-fp32-b1-h1-d16-n8", 1, 8, 1, 16, 16, "fp32",
              description="8-node random recursive tree (plus the 8-node chain), fp32"),
     Workload("gdn-layer-b1-h32-d128-n32", 1, 32, 32, 128, 128, "bf16",
@@ -317,7 +317,7 @@ CONFIGS = [
 
 
 def make_trees(i: int, rng: np.random.Generator) -> np.ndarray:
-    w = CONFIGS[i]
+    w = WORKLOADS[i]
     if i == 0:
         return random_recursive_tree(rng, w.n)[None, :]
     if i == 1:
@@ -338,7 +338,7 @@ def make_config(i: int, s: int = 0, layer: int = 0, chain: bool = False,
     `chain` replaces workload 0's tree by the 8-node chain.  `batch`/`heads`
     take a leading slice of the drawn set (used for bounded samples).
     """
-    w = CONFIGS[i]
+    w = WORKLOADS[i]
     seed = 1000 * i + s
     rng = np.random.Generator(np.random.PCG64(seed))
     parent = make_trees(i, rng)
