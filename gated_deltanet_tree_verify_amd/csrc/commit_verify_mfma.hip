@@ -86,39 +86,6 @@ static_assert(offsetof(SolveBlocks, th) + sizeof(pc::KeyChunk32) <= offsetof(Sol
               "the first commit chunk must stay inside the T rows, clear of what the mask writes");
 static_assert(sizeof(Smem) <= 81920, "two workgroups per CU");
 
-// Previous path as seen by wave 3: lane l holds the ids of slots l and
-// 64 + l (-1 past the path) and, after the second round of loads, the
-// parents that validate them.
-struct PathLanes {
-    int id0, id1;
-    int par0, par1;
-};
-
-// node id of path slot j (j < 128)
-__device__ __forceinline__ int slot_id(const PathLanes &p, int j) {
-    const int a = __shfl(p.id0, j & 63), b = __shfl(p.id1, j & 63);
-    return j < 64 ? a : b;
-}
-
-// a path is valid when 0 <= m <= max_path, its ids lie in [0, n_prev) and
-// increase, the first is a root and each later id's parent is the previous id
-__device__ __forceinline__ bool path_valid(const PathLanes &p, int m, int max_path, int n_prev,
-                                           int l) {
-    if (m < 0 || m > max_path || m > kMaxPathIds) return false;
-    const int last0 = __shfl(p.id0, 63);
-    bool bad = false;
-#pragma unroll
-    for (int rnd = 0; rnd < 2; ++rnd) {
-        const int j = 64 * rnd + l;
-        const int id = rnd == 0 ? p.id0 : p.id1;
-        const int par = rnd == 0 ? p.par0 : p.par1;
-        int prev = __shfl(id, (l + 63) & 63);
-        if (l == 0) prev = rnd == 0 ? -1 : last0;
-        if (j < m && (id < 0 || id >= n_prev || (j > 0 && prev >= id) || par != prev)) bad = true;
-    }
-    return __ballot(bad) == 0ull;
-}
-
 // 64 node rows of a bf16 [batch][n][H][128] tensor loaded by waves 0-2 alone
 // (192 threads, 16-byte chunks e = tid + 192 it, six per thread, the last
 // partly empty); rows past n read as zero
@@ -177,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     //         ids, every wave its q/k/v rows, then its state slab; wave 3
     //         requests the path parents and first chunk rows in between
     Gates gt{-1, 1.f, 0.f, false};
-    PathLanes pl{-1, -1, -2, -2};
+    pc::PathLanes pl{-1, -1, -2, -2};
     if (c.w == 3) {
         gt = load_gates(c, s, parent, alpha, beta);
         const int32_t *prow = path + (size_t)s.b * max_path;
@@ -208,14 +175,14 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             // the first chunk's keys and gates
             const int mc0 = min(32, mlen);
             const int rj = c.l >> 1;
-            const int rid = slot_id(pl, rj);
+            const int rid = pc::slot_id(pl, rj);
             k32 = pc::load_keys32(rid, rj < mc0 && rid >= 0 && rid < n_prev, pl.id0,
                                   c.l < mc0 && pl.id0 >= 0 && pl.id0 < n_prev, k_prev + prow0,
                                   alpha_prev + pgate0, H * kD, H, pbytes, c.l);
         } else {
             const int mc0 = min(pc::kC16, mlen);
             const int rj = c.l >> 2;
-            const int rid = slot_id(pl, rj);
+            const int rid = pc::slot_id(pl, rj);
             r16 = pc::load_keys16(rid, rj < mc0 && rid >= 0 && rid < n_prev, pl.id0,
                                   c.l < mc0 && pl.id0 >= 0 && pl.id0 < n_prev, k_prev + prow0,
                                   alpha_prev + pgate0, beta_prev + pgate0, H * kD, H, pbytes,
@@ -258,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     const bool tree_ok = !sm.tp.bad;
     // wave 3: the previous path's validity (and the fault flags)
     auto validate = [&]() -> bool {
-        const bool ok = path_valid(pl, mlen, max_path, n_prev, c.l);
+        const bool ok = pc::path_valid(pl, mlen, max_path, n_prev, c.l);
         if (c.l == 0) {
             sm.commit_ok = ok;
             if (s.hd == 0 && status)
@@ -301,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
                 if (c.w == 3) {
                     const int rj = c.l >> 1;
                     const pc::KeyRows32 kr = pc::load_keys32(
-                        slot_id(pl, c0 + rj), rj < mc, slot_id(pl, c0 + (c.l & 31)), c.l < mc,
+                        pc::slot_id(pl, c0 + rj), rj < mc, pc::slot_id(pl, c0 + (c.l & 31)), c.l < mc,
                         k_prev + prow0, alpha_prev + pgate0, H * kD, H, pbytes, c.l);
                     pc::build_keys32(sm.b.kc, sm.cx, kr, mc, c.l);
                 }
@@ -348,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
                     const int mc = min(pc::kC16, mlen - c0);
                     const int rj = c.l >> 2;
                     const pc::Rows16 rr = pc::load_rows16(
-                        slot_id(pl, c0 + rj), rj < mc, slot_id(pl, c0 + (c.l & 15)), c.l < mc,
+                        pc::slot_id(pl, c0 + rj), rj < mc, pc::slot_id(pl, c0 + (c.l & 15)), c.l < mc,
                         k_prev + prow0, v_prev + prow0, alpha_prev + pgate0, beta_prev + pgate0,
                         H * kD, H, pbytes, c.l);
                     pc::build16(sm.b.ch, sm.cx, rr, mc, c.l);

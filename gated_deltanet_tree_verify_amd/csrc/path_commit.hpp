@@ -79,6 +79,39 @@ __device__ __forceinline__ bool validate_and_keep(PathIds &pi, const int32_t *pa
     return ok;
 }
 
+// A path as seen by the one wave that reads it: lane l holds the ids of slots l and
+// 64 + l (-1 past the path) and, after the second round of loads, the
+// parents that validate them.
+struct PathLanes {
+    int id0, id1;
+    int par0, par1;
+};
+
+// node id of path slot j (j < 128)
+__device__ __forceinline__ int slot_id(const PathLanes &p, int j) {
+    const int a = __shfl(p.id0, j & 63), b = __shfl(p.id1, j & 63);
+    return j < 64 ? a : b;
+}
+
+// a path is valid when 0 <= m <= max_path, its ids lie in [0, n) and
+// increase, the first is a root and each later id's parent is the previous id
+__device__ __forceinline__ bool path_valid(const PathLanes &p, int m, int max_path, int n,
+                                           int l) {
+    if (m < 0 || m > max_path || m > kMaxPath) return false;
+    const int last0 = __shfl(p.id0, 63);
+    bool bad = false;
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd) {
+        const int j = 64 * rnd + l;
+        const int id = rnd == 0 ? p.id0 : p.id1;
+        const int par = rnd == 0 ? p.par0 : p.par1;
+        int prev = __shfl(id, (l + 63) & 63);
+        if (l == 0) prev = rnd == 0 ? -1 : last0;
+        if (j < m && (id < 0 || id >= n || (j > 0 && prev >= id) || par != prev)) bad = true;
+    }
+    return __ballot(bad) == 0ull;
+}
+
 // Gates and key / value rows of the chunk starting at path slot c0, in
 // registers (one round of loads; threads < 32 also take a gate pair).
 struct ChunkRows {

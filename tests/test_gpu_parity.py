@@ -156,12 +156,14 @@ def test_verify_fp32_gate_at_d128(gpu_lib):
 # ---------------------------------------------------------------------------
 # commit parity, commit-then-verify, invariants
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", [0, 1, 2])
-def test_commit_parity(gpu_lib, cfg):
-    say("commit cfg", cfg)
+@pytest.mark.parametrize("cfg,max_path", [(0, None), (1, None), (2, None), (1, 9), (2, 13)])
+def test_commit_parity(gpu_lib, cfg, max_path):
+    """max_path None: the tree size (32-slot chunks); 9 and 13 (the deepest
+    path of those trees): the one-chunk kernel for paths of at most 16 nodes"""
+    say("commit cfg", cfg, "max_path", max_path)
     ts = gs.make_config(cfg)
     d = upload(ts)
-    path, plen = ts.paths(max_path=ts.parent.shape[1])
+    path, plen = ts.paths(max_path=ts.parent.shape[1] if max_path is None else max_path)
     S = d["S0"].clone()
     st = torch.full((ts.parent.shape[0],), -7, dtype=torch.int32, device="cuda")
     gpu_lib.commit(S, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
