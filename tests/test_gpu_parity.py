@@ -487,6 +487,45 @@ def test_commit_verify_pseudo_values_decode_loop(gpu_lib, udt):
 
 
 @pytest.mark.parametrize("udt", ["fp32", "fp16"])
+def test_commit_verify_decode_chain(gpu_lib, udt):
+    """six decode steps on one state, 8 sequences x 8 heads of the b16/n64
+    workload's trees: step t commits tree t-1's accepted path from the
+    pseudo-values step t-1 wrote, then verifies tree t.  The committed state
+    and every step's outputs track the oracle run along the same chain
+    (commit then verify, fp64), within the gate at every step: the rounding
+    of carried fp16 pseudo-values does not build up."""
+    say("decode chain", udt)
+    trees = [gs.make_config(2, s=20 + t, batch=8, heads=8) for t in range(6)]
+    dev_sets = [upload(ts) for ts in trees]
+    S = dev_sets[0]["S0"].clone()
+    Sref = trees[0].S0.astype(np.float64)
+    u = [torch.empty(dev_sets[0]["v"].shape, dtype=U_DTYPES[udt], device="cuda") for _ in range(2)]
+    st = torch.full((8,), -7, dtype=torch.int32, device="cuda")
+    worst_s = worst_o = 0.0
+    for t, (ts, d) in enumerate(zip(trees, dev_sets)):
+        prev_ts, prev_d = (trees[t - 1], dev_sets[t - 1]) if t else (ts, d)
+        path, plen = prev_ts.paths(max_path=13)
+        if t == 0:
+            plen = np.zeros_like(plen)
+        prev = (prev_d["k"], prev_d["v"], prev_d["alpha"], prev_d["beta"], prev_d["parent"])
+        out = gpu_lib.commit_verify(S, dev(path), dev(plen), prev, d["q"], d["k"], d["v"],
+                                    d["alpha"], d["beta"], d["parent"],
+                                    u_prev=u[(t - 1) % 2] if t else None, u_out=u[t % 2],
+                                    status=st)
+        torch.cuda.synchronize()
+        if t:
+            Sref, cst = oracle.commit(Sref, path, plen, prev_ts.k, prev_ts.v, prev_ts.alpha,
+                                      prev_ts.beta, prev_ts.parent)
+            assert cst.tolist() == [0] * 8
+        oref, vst = oracle.verify(ts.q, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, Sref)
+        assert host(st).tolist() == vst.tolist() == [0] * 8
+        es, eo = oracle.rel_err(host(S), Sref), oracle.rel_err(host(out), oref)
+        worst_s, worst_o = max(worst_s, es), max(worst_o, eo)
+        assert es <= BF16_GATE and eo <= BF16_GATE, (t, es, eo)
+    say("worst rel err over the chain: S", worst_s, "out", worst_o)
+
+
+@pytest.mark.parametrize("udt", ["fp32", "fp16"])
 def test_commit_verify_pseudo_values_long_path_and_faults(gpu_lib, udt):
     """a 64-node chain (two 32-slot chunks of known u), a bad path (state
     untouched) and a malformed new tree (NaN outputs and u)"""
