@@ -218,6 +218,88 @@ def test_verify_leaves_state_untouched_and_is_deterministic(gpu_lib):
     assert torch.equal(o1, o2)
 
 
+def _verify_with(g, d, **over):
+    x = dict(d)
+    x.update(over)
+    out = g.verify(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["parent"], x["S0"])
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def test_homogeneity_bitwise_on_gpu(gpu_lib):
+    """the outputs are linear in (V, S0) jointly; doubling both is exact in
+    floating point (and in the hi / lo splits), so the outputs double bit
+    for bit (MFMA kernel, bf16)"""
+    ts = gs.make_config(2, batch=4, heads=8)
+    d = upload(ts)
+    o1 = _verify_with(gpu_lib, d)
+    o2 = _verify_with(gpu_lib, d, v=(d["v"].float() * 2).to(torch.bfloat16), S0=d["S0"] * 2)
+    assert np.array_equal(o2, 2 * o1)
+
+
+def test_additivity_on_gpu(gpu_lib):
+    """out(V1 + V2, S1 + S2) = out(V1, S1) + out(V2, S2) for one tree (fp32
+    path: the sums are formed in fp32, so to within their rounding)"""
+    A = gs.make_config(1, heads=8)
+    a, b = gs.make_set(A.parent, 8, 128, 128, "fp32", seed=3), gs.make_set(A.parent, 8, 128, 128,
+                                                                           "fp32", seed=4)
+    da, db = upload(a), upload(b)
+    o_a = _verify_with(gpu_lib, da)
+    o_b = _verify_with(gpu_lib, da, v=db["v"], S0=db["S0"])
+    o_ab = _verify_with(gpu_lib, da, v=da["v"] + db["v"], S0=da["S0"] + db["S0"])
+    assert oracle.rel_err(o_ab, o_a + o_b) <= 1e-5
+
+
+def test_non_descendants_unchanged_on_gpu(gpu_lib):
+    """new inputs at one node change the outputs of that node's subtree only;
+    every other node's output is bit-identical (its X and Y entries for the
+    node are masked to exact zeros)"""
+    ts = gs.make_config(2, batch=4, heads=8)
+    d = upload(ts)
+    o1 = _verify_with(gpu_lib, d)
+    j = 10
+    rng = np.random.default_rng(5)
+    d2 = {key: t.clone() for key, t in d.items()}
+    for key in ("q", "k", "v"):
+        x = torch.from_numpy(rng.standard_normal(d2[key][:, j].shape).astype(np.float32))
+        if key != "v":
+            x = x / x.norm(dim=-1, keepdim=True)
+        d2[key][:, j] = x.to(d2[key].dtype).cuda()
+    d2["alpha"][:, j] = 0.5
+    d2["beta"][:, j] = 0.9
+    o2 = _verify_with(gpu_lib, d2)
+    for b in range(ts.parent.shape[0]):
+        par = ts.parent[b]
+        sub = np.zeros(len(par), bool)
+        sub[j] = True
+        for i in range(j + 1, len(par)):
+            sub[i] = par[i] >= 0 and sub[par[i]]
+        assert np.array_equal(o1[b, ~sub], o2[b, ~sub]), b
+        assert not np.array_equal(o1[b, sub], o2[b, sub]), b
+
+
+def test_closed_forms_on_gpu(gpu_lib):
+    """beta = 0: o_i = e^{g_i} S0^T q_i (a plain product times the path decay;
+    MFMA kernel, bf16); q = k, beta = 1 with unit keys: o = v for any alpha
+    and S0 (fp32 path)"""
+    ts = gs.make_config(2, batch=4, heads=8)
+    d = upload(ts)
+    o = _verify_with(gpu_lib, d, beta=torch.zeros_like(d["beta"]))
+    la = np.log(ts.alpha.astype(np.float64))
+    ref = np.empty(o.shape)
+    for b in range(ts.parent.shape[0]):
+        g = np.zeros((ts.parent.shape[1], ts.alpha.shape[2]))
+        for i, p in enumerate(ts.parent[b]):
+            g[i] = la[b, i] + (g[p] if p >= 0 else 0.0)
+        qs = np.einsum("nhk,hkv->nhv", ts.q[b].astype(np.float64), ts.S0[b].astype(np.float64))
+        ref[b] = np.exp(g)[:, :, None] * qs
+    assert oracle.rel_err(o, ref) <= 2e-5
+    f = gs.make_set(ts.parent, 8, 128, 128, "fp32", seed=6)
+    df = upload(f)
+    o = _verify_with(gpu_lib, df, q=df["k"], beta=torch.ones_like(df["beta"]))
+    assert oracle.rel_err(o, f.v) <= 1e-5
+
+
 def test_relabeling_on_gpu(gpu_lib):
     ts = gs.make_config(1)
     out, _, d = run_verify(gpu_lib, ts)
