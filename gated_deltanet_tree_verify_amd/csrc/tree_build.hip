@@ -17,8 +17,9 @@
 // of its sorted row: the heap becomes "best head over the live nodes", one
 // wave-wide maximum per popped candidate.  Lane l owns nodes l and 64 + l
 // and keeps their heads, and the entries after them, in registers; a
-// candidate is one 64-bit word whose unsigned order is the pop order, so the
-// maximum is one compare per DPP step.
+// candidate is one 64-bit word whose unsigned order is the pop order, and
+// its maximum takes a 32-bit pass over the scores plus, on a tie, one over
+// the keys.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -45,31 +46,40 @@ __device__ __forceinline__ float unpack_score(unsigned long long w) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// one DPP step of the wave-wide maximum of a 64-bit word (lanes with no
-// source see 0, the identity)
+// one DPP step of a wave-wide maximum of a 32-bit unsigned value (lanes
+// with no source see 0, the identity); wave_max32: row_shr 1, 2, 4, 8 leave
+// each 16-lane row's maximum in its lane 15, row_bcast 15 and 31 carry
+// those into lane 63, which is read out (uniform)
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ unsigned long long dpp_max(unsigned long long x) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROW_MASK,
-                                                              0xf, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL,
-                                                              ROW_MASK, 0xf, false);
-    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_max32(uint32_t x) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
     return o > x ? o : x;
 }
 
-// maximum over the wave, returned uniform: row_shr 1, 2, 4, 8 leave each
-// 16-lane row's maximum in its lane 15; row_bcast 15 and 31 carry those
-// into lane 63, which is read out
-__device__ __forceinline__ unsigned long long wave_max(unsigned long long x) {
-    x = dpp_max<0x111, 0xf>(x);
-    x = dpp_max<0x112, 0xf>(x);
-    x = dpp_max<0x114, 0xf>(x);
-    x = dpp_max<0x118, 0xf>(x);
-    x = dpp_max<0x142, 0xa>(x);
-    x = dpp_max<0x143, 0xc>(x);
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
-    return ((unsigned long long)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max32(uint32_t x) {
+    x = dpp_max32<0x111, 0xf>(x);
+    x = dpp_max32<0x112, 0xf>(x);
+    x = dpp_max32<0x114, 0xf>(x);
+    x = dpp_max32<0x118, 0xf>(x);
+    x = dpp_max32<0x142, 0xa>(x);
+    x = dpp_max32<0x143, 0xc>(x);
+    return __builtin_amdgcn_readlane((int)x, 63);
+}
+
+// The wave maximum of a 64-bit candidate word in two 32-bit passes: the
+// high halves (the scores) first; the low halves only among the lanes that
+// hold that score, and when one lane alone holds it (the usual case) its
+// word is read directly.  Same word as a 64-bit maximum.
+__device__ __forceinline__ unsigned long long wave_max_2level(unsigned long long x) {
+    const uint32_t hi = (uint32_t)(x >> 32), lo = (uint32_t)x;
+    const uint32_t mhi = wave_max32(hi);
+    const unsigned long long tied = __ballot(hi == mhi);
+    uint32_t mlo;
+    if (__popcll(tied) == 1)
+        mlo = __builtin_amdgcn_readlane((int)lo, __ffsll((long long)tied) - 1);
+    else
+        mlo = wave_max32(hi == mhi ? lo : 0u);
+    return ((unsigned long long)mhi << 32) | mlo;
 }
 
 // One tree node owned by a lane.  x / j: log-probability and original slot
@@ -182,7 +192,7 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
         const int cnt = min(width, n - nn);
         int popped = 0;
         for (; popped < cnt; ++popped) {
-            const unsigned long long best = wave_max(c0 > c1 ? c0 : c1);
+            const unsigned long long best = wave_max_2level(c0 > c1 ? c0 : c1);
             if (best == 0ull) break;   // nothing left this round
             const int key = 8191 - (int)(((uint32_t)best >> 8) & 0xffffffu);
             const int pnode = key >> 6, pslot = key & 63;
