@@ -44,7 +44,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     // state slab: four result tiles of this lane's column
     float *slab = S + (size_t)bh * kD * kD;
     f32x16 st[4];
-    load_state(st, slab, col, h);
+    // 4-byte accesses, one tile at a time (measured faster here than the
+    // whole-slab 8-byte ones)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_state_tile(st[q], q, slab, col, h);
     bf16x8 ident[2];
     key_identity(ident, m, h);
     for (int c0 = 0; c0 < mlen; c0 += kC) {
@@ -52,7 +55,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
         apply_chunk(sm.ct, st, ident, m, h, col);
         lds_barrier();   // the chunk tiles are restaged next
     }
-    store_state(st, slab, col, h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_state_tile(st[q], q, slab, col, h);
 }
 
 // Paths of at most 16 nodes (max_path <= 16, the usual case: a tree of

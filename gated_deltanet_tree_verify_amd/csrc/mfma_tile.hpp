@@ -180,12 +180,16 @@ __device__ __forceinline__ void store16(float *p, const float4 &x) {
 // tiles, tile q holding rows 32 q + crow(r, h).  The 128 x 128 fp32 state of
 // one (sequence, head) is addressed through a buffer resource: the lane's
 // column and half go into one 32-bit lane offset and every row offset is a
-// scalar constant, so the 64 loads or stores of a lane carry no per-element
+// scalar constant, so the loads or stores of a lane carry no per-element
 // address arithmetic and nothing address-like stays live between the load
 // and the store of the slab.  The resource's size bounds every access to
-// the 64 KiB of that state.  slab must be wave-uniform.  The b32 buffer
-// builtins move 32-bit integers: the floats pass through them as bit
-// patterns.
+// the 64 KiB of that state.  slab must be wave-uniform.  The buffer
+// builtins move integers: the floats pass through them as bit patterns.
+// Tiles go one at a time with 4-byte accesses (load_state_tile,
+// store_state_tile: the fused kernel and the long-path commit, measured
+// faster there) or whole slabs with 8-byte accesses (load_state,
+// store_state: the verify, short-path commit and branch kernels, half the
+// memory instructions).
 constexpr int kStateDim = 128;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float *slab) {
@@ -194,17 +198,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float *slab) 
 
 __device__ __forceinline__ int state_lane_offset(int col, int h) {
     return 4 * (col + 4 * h * kStateDim);
-}
-
-__device__ __forceinline__ void load_state(f32x16 (&st)[4], const float *slab, int col, int h) {
-    const __amdgpu_buffer_rsrc_t rs = state_rsrc(slab);
-    const int vo = state_lane_offset(col, h);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            st[q][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                rs, vo, 4 * kStateDim * (32 * q + crow(r, 0)), kNT));
 }
 
 // one tile (rows 32 q .. 32 q + 31) of the slab
@@ -230,19 +223,64 @@ __device__ __forceinline__ void store_state_tile(const f32x16 &t, int q, float *
     }
 }
 
-__device__ __forceinline__ void store_state(const f32x16 (&st)[4], float *slab, int col, int h) {
+// Lane pairs (columns 2a, 2a + 1) move 2 x 2 blocks with 8-byte accesses:
+// for registers 2j, 2j + 1 (rows R = crow(2j, h) and R + 1) the even lane
+// accesses row R and the odd lane row R + 1, both at columns 2a, 2a + 1, and
+// one swap between the pair (DPP quad_perm 1 0 3 2) gives each lane its own
+// column of both rows.  Half the memory instructions of 4-byte accesses.
+constexpr int kSwapPairs = 0xB1;   // quad_perm [1, 0, 3, 2]
+
+__device__ __forceinline__ uint32_t pair_swap(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kSwapPairs, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ int state_pair_offset(int col, int h) {
+    return 4 * ((col & ~1) + kStateDim * (4 * h + (col & 1)));
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void load_state_tile_x2(f32x16 &t, int q, const float *slab, int col,
+                                                   int h) {
     const __amdgpu_buffer_rsrc_t rs = state_rsrc(slab);
-    const int vo = state_lane_offset(col, h);
+    const int vo = state_pair_offset(col, h);
+    const bool odd = col & 1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int j = 0; j < 8; ++j) {
+        const u32x2 x = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                       rs, vo, 4 * kStateDim * (32 * q + crow(2 * j, 0)), kNT));
+        const uint32_t recv = pair_swap(odd ? x.x : x.y);
+        t[2 * j] = __uint_as_float(odd ? recv : x.x);
+        t[2 * j + 1] = __uint_as_float(odd ? x.y : recv);
+    }
+}
+
+__device__ __forceinline__ void store_state_tile_x2(const f32x16 &t, int q, float *slab, int col,
+                                                    int h) {
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc(slab);
+    const int vo = state_pair_offset(col, h);
+    const bool odd = col & 1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            // through a scalar temporary: a bit cast applied to the vector
-            // element itself reads element 0 with this compiler
-            const float x = st[q][r];
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, vo,
-                                                  4 * kStateDim * (32 * q + crow(r, 0)), kNT);
-        }
+    for (int j = 0; j < 8; ++j) {
+        const float a = t[2 * j], b = t[2 * j + 1];   // scalar temporaries
+        const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+        const uint32_t recv = pair_swap(odd ? ua : ub);
+        const u32x2 x = odd ? u32x2{recv, ub} : u32x2{ua, recv};
+        __builtin_amdgcn_raw_buffer_store_b64(x, rs, vo,
+                                              4 * kStateDim * (32 * q + crow(2 * j, 0)), kNT);
+    }
+}
+
+// the whole slab, 8-byte accesses
+__device__ __forceinline__ void load_state(f32x16 (&st)[4], const float *slab, int col, int h) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_state_tile_x2(st[q], q, slab, col, h);
+}
+
+__device__ __forceinline__ void store_state(const f32x16 (&st)[4], float *slab, int col, int h) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_state_tile_x2(st[q], q, slab, col, h);
 }
 
 }  // namespace tile
