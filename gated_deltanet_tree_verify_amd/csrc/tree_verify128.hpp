@@ -151,6 +151,28 @@ __device__ __forceinline__ void store_rows_permuted(const Lane &c, const uint4 (
     }
 }
 
+// the same rows loaded by waves 0-2 alone (192 threads, e = tid + 192 it,
+// eleven chunks per thread, the last round partly empty)
+__device__ __forceinline__ void load_rows3(const Lane &c, const Seq &s, const uint16_t *src,
+                                           uint4 (&x)[11]) {
+    const uint32_t bytes = (uint32_t)(s.n * s.rstride * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + s.base, bytes);
+#pragma unroll
+    for (int it = 0; it < 11; ++it) {
+        const int e = c.tid + 192 * it, row = e >> 4, c8 = (e & 15) * 8;
+        x[it] = load16(rs, e < kN * 16 ? (uint32_t)((row * s.rstride + c8) * 2) : bytes);
+    }
+}
+
+__device__ __forceinline__ void store_rows3_permuted(const Lane &c, const uint4 (&x)[11],
+                                                     uint16_t (*dst)[kQK]) {
+#pragma unroll
+    for (int it = 0; it < 11; ++it) {
+        const int e = c.tid + 192 * it, row = e >> 4, c8 = (e & 15) * 8;
+        if (e < kN * 16) store_row8_permuted(dst[row], c8, x[it]);
+    }
+}
+
 __device__ __forceinline__ void store_rows(const Lane &c, const uint4 (&x)[8],
                                            uint16_t (*dst)[kQK]) {
 #pragma unroll

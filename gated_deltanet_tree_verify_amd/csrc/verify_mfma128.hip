@@ -40,16 +40,21 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
     const Seq s = tv::seq_coords(blockIdx.x, n, H);
     const float *slab = S0 + (size_t)blockIdx.x * kD * kD;
 
-    // ---- 1. topology (wave 3), then the Q, K, V tiles
-    if (c.w == 3)
-        tv128::topology(c, s, parent, alpha, beta, sm.tp, status, s.hd == 0, status_or);
+    // ---- 1. the Q and K tiles (waves 0-2) while wave 3 builds the topology
+    //         under its share of the V rows; then the V tile
     {
         uint4 x[8];
-        tv128::load_rows(c, s, q, x);
-        tv128::store_rows_permuted(c, x, sm.t.q);
-        tv128::load_rows(c, s, k, x);
-        tv128::store_rows_permuted(c, x, sm.t.k);
-        tv128::load_rows(c, s, v, x);
+        if (c.w < 3) {
+            uint4 y[11];
+            tv128::load_rows3(c, s, q, y);
+            tv128::store_rows3_permuted(c, y, sm.t.q);
+            tv128::load_rows3(c, s, k, y);
+            tv128::store_rows3_permuted(c, y, sm.t.k);
+            tv128::load_rows(c, s, v, x);
+        } else {
+            tv128::load_rows(c, s, v, x);
+            tv128::topology(c, s, parent, alpha, beta, sm.tp, status, s.hd == 0, status_or);
+        }
         tv128::store_rows(c, x, sm.b.v);
     }
     f32x16 st[4];
