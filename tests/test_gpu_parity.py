@@ -335,6 +335,23 @@ def test_verify_bad_parent(gpu_lib):
     assert oracle.rel_err(out[0], ref[0]) <= BF16_GATE
 
 
+@pytest.mark.parametrize("n", [65, 128])
+def test_verify_bad_parent_n128(gpu_lib, n):
+    """the 65..128-node kernel: a node that is its own parent, a parent
+    after its node; the healthy sequence is unaffected"""
+    say("verify bad parent n", n)
+    rng = np.random.default_rng(n + 77)
+    par = np.stack([gs.random_recursive_tree(rng, n, max_depth=16) for _ in range(3)])
+    par[1, n - 1] = n - 1
+    par[2, 40] = n - 1
+    ts = gs.make_set(par, 4, 128, 128, "bf16", seed=n)
+    out, st, _ = run_verify(gpu_lib, ts)
+    ref, rst = oracle.verify_set(ts)
+    assert st.tolist() == rst.tolist() == [0, 1, 1]
+    assert np.isnan(out[1:]).all() and np.isfinite(out[0]).all()
+    assert oracle.rel_err(out[0], ref[0]) <= BF16_GATE
+
+
 def test_commit_bad_paths_leave_state(gpu_lib):
     ts = gs.make_config(2, batch=4)
     d = upload(ts)
