@@ -242,15 +242,20 @@ __device__ __forceinline__ void store_split(const Lane &c, const float (&v)[16],
     }
 }
 
-// the three blocks of half hf (row / key blocks 2 hf, 2 hf + 1) into the
-// 64-node solve blocks, wave w < 3 taking block (0,0), (1,0), (1,1)
-__device__ __forceinline__ void half_blocks(const Lane &c, const QKTiles &t, const Topo &tp,
-                                            int hf, SolveBlocks &sb) {
+// the three blocks of half hf (row / key blocks 2 hf, 2 hf + 1), wave w < 3
+// taking block (0,0), (1,0), (1,1): masked Gram values into registers, then
+// into the 64-node solve blocks
+__device__ __forceinline__ void half_values(const Lane &c, const QKTiles &t, const Topo &tp,
+                                            int hf, float (&y)[16], float (&x)[16]) {
     const int la = c.w == 0 ? 0 : 1, lb = c.w == 2 ? 1 : 0;
     f32x16 gc, ga;
     gram(c, t, 2 * hf + la, 2 * hf + lb, gc, ga);
-    float y[16], x[16];
     mask(c, tp, 2 * hf + la, 2 * hf + lb, gc, ga, y, x);
+}
+
+__device__ __forceinline__ void half_store(const Lane &c, float (&y)[16], float (&x)[16],
+                                           SolveBlocks &sb) {
+    const int la = c.w == 0 ? 0 : 1;
     store_split(c, y, sb.yh[c.w], sb.yl[c.w]);
     if (c.w == 1) {
 #pragma unroll

@@ -5,7 +5,11 @@
 // region that holds the V tile and then the 64-node solve blocks of each
 // half in turn plus the four cross blocks (82 KB), and the topology (5.5 KB):
 // one workgroup per CU.  The state slab is requested one 32-row tile at a
-// time between the phases that do not need it.
+// time between the phases that do not need it.  With one wave per SIMD
+// nothing hides a stage's latency, so independent work is paired: each wave
+// forms its first- and second-half block values together (the second half's
+// wait in registers until its solve blocks are free), and both halves' P / R
+// contractions run back to back once the last state tile lands.
 #include "internal.hpp"
 #include "tree_verify128.hpp"
 
@@ -72,17 +76,25 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
         return;
     }
 
-    // ---- 3. half 0: blocks, inverse, P / R, solve, outputs
-    if (c.w < 3) tv128::half_blocks(c, sm.t, sm.tp, 0, sm.b.sx.s);
+    // ---- 3. half 0: blocks, inverse, P / R, solve, outputs; half 1's
+    //         block values wait in registers until its solve blocks are free
+    float y1[16], x1[16];
+    if (c.w < 3) {
+        float y0[16], x0[16];
+        tv128::half_values(c, sm.t, sm.tp, 0, y0, x0);
+        tv128::half_values(c, sm.t, sm.tp, 1, y1, x1);
+        tv128::half_store(c, y0, x0, sm.b.sx.s);
+    }
     load_state_tile(st[2], 2, slab, c.col, c.h);
     lds_barrier();
     tv::inverse(c, sm.b.sx.s);
     load_state_tile(st[3], 3, slab, c.col, c.h);
     lds_barrier();
-    f32x16 u01[2];
+    f32x16 u01[2], P1[2], R1[2];
     {
         f32x16 P[2], R[2], rhs[2], o[2];
         tv128::contract(c, sm.t, 0, st, P, R);
+        tv128::contract(c, sm.t, 1, st, P1, R1);   // the state dies here
         tv128::rhs_and_decay(c, sm.tp, 0, P, R, vpk, rhs);
         tv128::solve_half(c, sm.b.sx.s, rhs, P, u01, o);
         tv128::store_out(c, s, 0, o, out);
@@ -90,14 +102,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
     lds_barrier();   // every wave is done with half 0's solve blocks
 
     // ---- 4. half 1, with the cross terms of half 0's pseudo-values
-    if (c.w < 3) tv128::half_blocks(c, sm.t, sm.tp, 1, sm.b.sx.s);
+    if (c.w < 3) tv128::half_store(c, y1, x1, sm.b.sx.s);
     lds_barrier();
     tv::inverse(c, sm.b.sx.s);
     lds_barrier();
     {
-        f32x16 P[2], R[2], rhs[2], u[2], o[2];
-        tv128::contract(c, sm.t, 1, st, P, R);
-        tv128::rhs_and_decay(c, sm.tp, 1, P, R, vpk, rhs);
+        f32x16 rhs[2], u[2], o[2];
+        f32x16 (&P)[2] = P1;
+        tv128::rhs_and_decay(c, sm.tp, 1, P, R1, vpk, rhs);
         const Cross &cr = sm.b.sx.x;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
