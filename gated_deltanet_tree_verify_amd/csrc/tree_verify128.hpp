@@ -283,30 +283,35 @@ __device__ __forceinline__ void cross_block(const Lane &c, const QKTiles &t, con
     store_split(c, x, cr.xh[a][b], cr.xl[a][b]);
 }
 
-// P = Q S0, R = K S0 over rows 64 hf .. 64 hf + 63 for this wave's columns
-__device__ __forceinline__ void contract(const Lane &c, const QKTiles &t, int hf,
-                                         const f32x16 (&st)[4], f32x16 (&P)[2], f32x16 (&R)[2]) {
-    P[0] = P[1] = R[0] = R[1] = f32x16{};
+// state tile q's share of P = Q S0 and R = K S0 for this wave's columns over
+// both halves (rows 64 hf + 32 tt + crow), the state split into bf16 hi + lo;
+// the caller takes q = 0, 1, 2, 3 in turn, each as its tile lands
+__device__ __forceinline__ void contract_tile(const Lane &c, const QKTiles &t, int q,
+                                              const f32x16 &sq, f32x16 (&P0)[2],
+                                              f32x16 (&R0)[2], f32x16 (&P1)[2],
+                                              f32x16 (&R1)[2]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int kk = 0; kk < 2; ++kk) {
+        float sv[8];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float sv[8];
+        for (int j = 0; j < 8; ++j) sv[j] = sq[8 * kk + j];
+        bf16x8 sh, sl;
+        split8(sv, sh, sl);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sv[j] = st[q][8 * kk + j];
-            bf16x8 sh, sl;
-            split8(sv, sh, sl);
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
+                f32x16 &p = hf ? P1[tt] : P0[tt];
+                f32x16 &r = hf ? R1[tt] : R0[tt];
                 const int row = 64 * hf + 32 * tt + c.m;
                 const bf16x8 aq = lds8(&t.q[row][32 * q + 16 * kk + 8 * c.h]);
                 const bf16x8 ak = lds8(&t.k[row][32 * q + 16 * kk + 8 * c.h]);
-                P[tt] = mfma(aq, sh, P[tt]);
-                P[tt] = mfma(aq, sl, P[tt]);
-                R[tt] = mfma(ak, sh, R[tt]);
-                R[tt] = mfma(ak, sl, R[tt]);
+                p = mfma(aq, sh, p);
+                p = mfma(aq, sl, p);
+                r = mfma(ak, sh, r);
+                r = mfma(ak, sl, r);
             }
-        }
+    }
 }
 
 // right-hand side beta (v - e^g R) and e^g P for rows 64 hf + 32 t + crow

@@ -8,8 +8,9 @@
 // time between the phases that do not need it.  With one wave per SIMD
 // nothing hides a stage's latency, so independent work is paired: each wave
 // forms its first- and second-half block values together (the second half's
-// wait in registers until its solve blocks are free), and both halves' P / R
-// contractions run back to back once the last state tile lands.
+// wait in registers until its solve blocks are free), and each state tile is
+// contracted into both halves' P / R as soon as it has landed, ahead of the
+// stage that follows, so only the last tile's share waits for the last tile.
 #include "internal.hpp"
 #include "tree_verify128.hpp"
 
@@ -76,8 +77,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
         return;
     }
 
-    // ---- 3. half 0: blocks, inverse, P / R, solve, outputs; half 1's
-    //         block values wait in registers until its solve blocks are free
+    // ---- 3. half 0: blocks, inverse, solve, outputs; half 1's block values
+    //         wait in registers until its solve blocks are free, and each
+    //         state tile goes into both halves' P / R once it has landed
+    f32x16 P0[2] = {}, R0[2] = {}, P1[2] = {}, R1[2] = {};
+    tv128::contract_tile(c, sm.t, 0, st[0], P0, R0, P1, R1);
     float y1[16], x1[16];
     if (c.w < 3) {
         float y0[16], x0[16];
@@ -87,16 +91,17 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
     }
     load_state_tile(st[2], 2, slab, c.col, c.h);
     lds_barrier();
+    tv128::contract_tile(c, sm.t, 1, st[1], P0, R0, P1, R1);
     tv::inverse(c, sm.b.sx.s);
     load_state_tile(st[3], 3, slab, c.col, c.h);
+    tv128::contract_tile(c, sm.t, 2, st[2], P0, R0, P1, R1);
     lds_barrier();
-    f32x16 u01[2], P1[2], R1[2];
+    tv128::contract_tile(c, sm.t, 3, st[3], P0, R0, P1, R1);
+    f32x16 u01[2];
     {
-        f32x16 P[2], R[2], rhs[2], o[2];
-        tv128::contract(c, sm.t, 0, st, P, R);
-        tv128::contract(c, sm.t, 1, st, P1, R1);   // the state dies here
-        tv128::rhs_and_decay(c, sm.tp, 0, P, R, vpk, rhs);
-        tv128::solve_half(c, sm.b.sx.s, rhs, P, u01, o);
+        f32x16 rhs[2], o[2];
+        tv128::rhs_and_decay(c, sm.tp, 0, P0, R0, vpk, rhs);
+        tv128::solve_half(c, sm.b.sx.s, rhs, P0, u01, o);
         tv128::store_out(c, s, 0, o, out);
     }
     lds_barrier();   // every wave is done with half 0's solve blocks
@@ -108,8 +113,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
     lds_barrier();
     {
         f32x16 rhs[2], u[2], o[2];
-        f32x16 (&P)[2] = P1;
-        tv128::rhs_and_decay(c, sm.tp, 1, P, R1, vpk, rhs);
+        tv128::rhs_and_decay(c, sm.tp, 1, P1, R1, vpk, rhs);
         const Cross &cr = sm.b.sx.x;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -117,10 +121,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 rhs[t] = mm3<kBL>(cr.xh[t][b], cr.xl[t][b], ub, rhs[t], c.m, c.h);
-                P[t] = mm3<kBL>(cr.yh[t][b], cr.yl[t][b], ub, P[t], c.m, c.h);
+                P1[t] = mm3<kBL>(cr.yh[t][b], cr.yl[t][b], ub, P1[t], c.m, c.h);
             }
         }
-        tv128::solve_half(c, sm.b.sx.s, rhs, P, u, o);
+        tv128::solve_half(c, sm.b.sx.s, rhs, P1, u, o);
         tv128::store_out(c, s, 1, o, out);
     }
 }
