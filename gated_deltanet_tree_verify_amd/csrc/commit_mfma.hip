@@ -44,14 +44,19 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
     // state slab: four result tiles of this lane's column
     float *slab = S + (size_t)bh * kD * kD;
     f32x16 st[4];
-    // 4-byte accesses, one tile at a time (measured faster here than the
-    // whole-slab 8-byte ones)
+    // the first chunk's rows are requested ahead of the state, which only its
+    // application needs; each later chunk's rows while the one before it is
+    // applied.  State: 4-byte accesses, one tile at a time (measured faster
+    // here than the whole-slab 8-byte ones).
+    ChunkRows rows = load_chunk(sm.pi.pid, 0, mlen, b, hd, n, H, k, v, alpha, beta, tid);
 #pragma unroll
     for (int q = 0; q < 4; ++q) load_state_tile(st[q], q, slab, col, h);
     bf16x8 ident[2];
     key_identity(ident, m, h);
     for (int c0 = 0; c0 < mlen; c0 += kC) {
-        prepare_chunk(sm.ct, sm.pi.pid, c0, mlen, b, hd, n, H, k, v, alpha, beta, tid, w, l);
+        build_chunk(sm.ct, rows, c0, mlen, tid, w, l);
+        if (c0 + kC < mlen)
+            rows = load_chunk(sm.pi.pid, c0 + kC, mlen, b, hd, n, H, k, v, alpha, beta, tid);
         apply_chunk(sm.ct, st, ident, m, h, col);
         lds_barrier();   // the chunk tiles are restaged next
     }
