@@ -68,9 +68,9 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_kernel(
 // depth d gives paths of at most d + 1 nodes): one 16-slot chunk, prepared by
 // wave 0 alone while the other waves stream the state.  Wave 0 reads the
 // path ids, then in one round the parents that validate them and the
-// chunk's key / value rows and gates, builds the chunk (Gram, X,
-// T = (I + X)^{-1}) and only then requests its own state tiles; waves 1-3
-// request theirs at once.  Every wave then applies the chunk (R = K_p S,
+// chunk's key / value rows and gates, then its own state tiles, which land
+// while it builds the chunk (Gram, X, T = (I + X)^{-1}); waves 1-3 request
+// theirs at once.  Every wave then applies the chunk (R = K_p S,
 // U = T RHS, the update) and writes its slab back.
 struct SmemShort {
     Chunk16 ch;
@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_short_kernel(
         const Rows16 r16 = load_rows16(rid, rj < mc && rid >= 0 && rid < n, pl.id0,
                                        l < mc && pl.id0 >= 0 && pl.id0 < n, k + row0, v + row0,
                                        alpha + gate0, beta + gate0, H * kD, H, bytes, l);
+        load_state(st, slab, col, h);
         for (int i = l; i < kKP; i += 64) sm.cx.zk[i] = 0;
         if (l < kBL) sm.cx.zt[l] = 0;
         const bool ok = path_valid(pl, mlen, max_path, n, l) && mlen <= kC16;
@@ -117,7 +118,6 @@ __global__ __launch_bounds__(kThreads, 2) void commit_mfma_short_kernel(
             if (hd == 0 && status) status[b] = ok ? 0 : kFaultBadPath;
         }
         if (ok && mlen > 0) build16(sm.ch, sm.cx, r16, mc, l);
-        load_state(st, slab, col, h);
     } else {
         load_state(st, slab, col, h);
     }
