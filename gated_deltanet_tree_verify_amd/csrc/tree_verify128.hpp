@@ -352,18 +352,27 @@ __device__ __forceinline__ void solve_half(const Lane &c, const SolveBlocks &sb,
     o[1] = mm3<kBL>(sb.yh[2], sb.yl[2], split_tile(u[1]), o[1], c.m, c.h);
 }
 
-// this lane's entries of output rows 64 hf + 32 t + crow(r, h), rows < n
-__device__ __forceinline__ void store_out(const Lane &c, const Seq &s, int hf,
-                                          const f32x16 (&o)[2], float *out) {
-    float *orow = out + s.base + c.col;
+// output rows 64 hf .. 64 hf + 63 (rows < n): this wave's result tiles into
+// the LDS staging rows (row stride kD + 4 floats), then whole rows as 16-byte
+// chunks, eight per thread (four times fewer store instructions than the
+// tiles' own 4-byte entries); a barrier of the caller must separate the
+// staging area's previous readers from this call
+__device__ __forceinline__ void store_out_staged(const Lane &c, const Seq &s, int hf,
+                                                 const f32x16 (&o)[2], float (*stage)[kD + 4],
+                                                 float *out) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 64 * hf + 32 * t + crow(r, c.h);
-            const float x = o[t][r];
-            if (i < s.n) __builtin_nontemporal_store(x, orow + (size_t)i * s.rstride);
-        }
+        for (int r = 0; r < 16; ++r) stage[32 * t + crow(r, c.h)][c.col] = o[t][r];
+    tv::lds_barrier();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int e = c.tid + kThreads * it, row = e >> 5, c4 = (e & 31) * 4;
+        const int i = 64 * hf + row;
+        if (i < s.n)
+            store16(out + s.base + (size_t)i * s.rstride + c4,
+                    *reinterpret_cast<const float4 *>(&stage[row][c4]));
+    }
 }
 
 __device__ __forceinline__ void store_nan(const Lane &c, const Seq &s, float *out) {

@@ -4,7 +4,8 @@
 // solve are in tree_verify128.hpp.  LDS: the 128-row Q/K tiles (68 KB), one
 // region that holds the V tile and then the 64-node solve blocks of each
 // half in turn plus the four cross blocks (82 KB), and the topology (5.5 KB):
-// one workgroup per CU.  The state slab is requested one 32-row tile at a
+// one workgroup per CU.  Each half's output rows are staged over the Q/K
+// tiles once the last contraction has read them.  The state slab is requested one 32-row tile at a
 // time between the phases that do not need it.  With one wave per SIMD
 // nothing hides a stage's latency, so independent work is paired: each wave
 // forms its first- and second-half block values together (the second half's
@@ -20,7 +21,10 @@ namespace {
 using namespace tv128;
 
 struct Smem {
-    QKTiles t;
+    union {
+        QKTiles t;
+        float o[64][kD + 4];   // one half's output rows, once Q and K are dead
+    } a;
     union {
         uint16_t v[kN][kQK];
         struct {
@@ -52,9 +56,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
         if (c.w < 3) {
             uint4 y[11];
             tv128::load_rows3(c, s, q, y);
-            tv128::store_rows3_permuted(c, y, sm.t.q);
+            tv128::store_rows3_permuted(c, y, sm.a.t.q);
             tv128::load_rows3(c, s, k, y);
-            tv128::store_rows3_permuted(c, y, sm.t.k);
+            tv128::store_rows3_permuted(c, y, sm.a.t.k);
             tv128::load_rows(c, s, v, x);
         } else {
             tv128::load_rows(c, s, v, x);
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
     lds_barrier();
 
     // ---- 2. cross blocks (one per wave), V -> registers
-    tv128::cross_block(c, sm.t, sm.tp, sm.b.sx.x);
+    tv128::cross_block(c, sm.a.t, sm.tp, sm.b.sx.x);
     uint32_t vpk[4][8];
     tv128::v_to_regs(c, sm.b.v, vpk);
     load_state_tile(st[1], 1, slab, c.col, c.h);
@@ -81,28 +85,29 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
     //         wait in registers until its solve blocks are free, and each
     //         state tile goes into both halves' P / R once it has landed
     f32x16 P0[2] = {}, R0[2] = {}, P1[2] = {}, R1[2] = {};
-    tv128::contract_tile(c, sm.t, 0, st[0], P0, R0, P1, R1);
+    tv128::contract_tile(c, sm.a.t, 0, st[0], P0, R0, P1, R1);
     float y1[16], x1[16];
     if (c.w < 3) {
         float y0[16], x0[16];
-        tv128::half_values(c, sm.t, sm.tp, 0, y0, x0);
-        tv128::half_values(c, sm.t, sm.tp, 1, y1, x1);
+        tv128::half_values(c, sm.a.t, sm.tp, 0, y0, x0);
+        tv128::half_values(c, sm.a.t, sm.tp, 1, y1, x1);
         tv128::half_store(c, y0, x0, sm.b.sx.s);
     }
     load_state_tile(st[2], 2, slab, c.col, c.h);
     lds_barrier();
-    tv128::contract_tile(c, sm.t, 1, st[1], P0, R0, P1, R1);
+    tv128::contract_tile(c, sm.a.t, 1, st[1], P0, R0, P1, R1);
     tv::inverse(c, sm.b.sx.s);
     load_state_tile(st[3], 3, slab, c.col, c.h);
-    tv128::contract_tile(c, sm.t, 2, st[2], P0, R0, P1, R1);
+    tv128::contract_tile(c, sm.a.t, 2, st[2], P0, R0, P1, R1);
     lds_barrier();
-    tv128::contract_tile(c, sm.t, 3, st[3], P0, R0, P1, R1);
+    tv128::contract_tile(c, sm.a.t, 3, st[3], P0, R0, P1, R1);
     f32x16 u01[2];
     {
         f32x16 rhs[2], o[2];
         tv128::rhs_and_decay(c, sm.tp, 0, P0, R0, vpk, rhs);
         tv128::solve_half(c, sm.b.sx.s, rhs, P0, u01, o);
-        tv128::store_out(c, s, 0, o, out);
+        lds_barrier();   // every wave has read its last Q / K rows
+        tv128::store_out_staged(c, s, 0, o, sm.a.o, out);
     }
     lds_barrier();   // every wave is done with half 0's solve blocks
 
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_n128_kernel(
             }
         }
         tv128::solve_half(c, sm.b.sx.s, rhs, P1, u, o);
-        tv128::store_out(c, s, 1, o, out);
+        tv128::store_out_staged(c, s, 1, o, sm.a.o, out);
     }
 }
 
