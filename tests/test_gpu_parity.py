@@ -185,6 +185,24 @@ def test_commit_deep_chain_n128(gpu_lib):
     assert oracle.rel_err(host(S), Sref) <= BF16_GATE
 
 
+def test_commit_chunk_edges_n128(gpu_lib):
+    """the 32-slot chunked commit at path lengths on and next to the chunk
+    edges (1, 32, 33, 64, 96, 97 nodes), the next chunk's rows prefetched"""
+    ts = gs.make_set(np.stack([gs.chain_tree(128)] * 6), 2, 128, 128, "bf16", seed=12,
+                     accepted=np.array([0, 31, 32, 63, 95, 96], np.int32))
+    d = upload(ts)
+    path, plen = ts.paths(max_path=128)
+    assert plen.tolist() == [1, 32, 33, 64, 96, 97]
+    S = d["S0"].clone()
+    st = torch.full((6,), -7, dtype=torch.int32, device="cuda")
+    gpu_lib.commit(S, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                   status=st)
+    torch.cuda.synchronize()
+    Sref, rst = oracle.commit_set(ts, path_arr=path, path_len=plen)
+    assert host(st).tolist() == rst.tolist() == [0] * 6
+    assert oracle.rel_err(host(S), Sref) <= BF16_GATE
+
+
 def test_commit_then_verify_subtree(gpu_lib):
     """the committed state, verified over the re-rooted subtree below the
     accepted node, reproduces the original verify outputs of that subtree"""
