@@ -229,8 +229,11 @@ gdn_status gdn_tree_accept(const int32_t *parent, const int32_t *draft_tok,
                            int n, int32_t *status, void *stream);
 
 /*
- * Accepted path: path[b][0..m) = root .. accepted[b] (root first), the rest
- * of the row -1, path_len[b] = m.  The walk goes up from accepted[b]; a
+ * Accepted path (the section above commits the state along the accepted
+ * branch only, once that branch is known; this call turns the accepted node
+ * into that branch, the input of gdn_tree_commit and of the commit half of
+ * gdn_tree_commit_verify): path[b][0..m) = root .. accepted[b] (root
+ * first), the rest of the row -1, path_len[b] = m.  The walk goes up from accepted[b]; a
  * parent outside [-1, node) stops it with GDN_FAULT_BAD_PARENT; an accepted
  * id outside [0, n) or m > max_path gives GDN_FAULT_BAD_PATH.  A faulted row
  * is all -1 with path_len 0.  Integer work, bit-exact.  1 <= max_path.
@@ -240,7 +243,11 @@ gdn_status gdn_tree_path(const int32_t *parent, const int32_t *accepted,
                          int max_path, int32_t *status, void *stream);
 
 /*
- * Tree indexing: depth[b][i] (root = 0) and the ancestor-or-self bitmask
+ * Tree indexing (the section above takes the draft tree topologically sorted
+ * and builds X and Y from the ancestor relations between its nodes: X over
+ * strict ancestors, Y over ancestors and the node itself; this call exposes
+ * the indexing that the verify kernels compute on chip, for inspection and
+ * tests): depth[b][i] (root = 0) and the ancestor-or-self bitmask
  * anc[b][i][ceil(n/32)] (bit s%32 of word s/32 is set iff s == i or s is an
  * ancestor of i).  A malformed tree gives GDN_FAULT_BAD_PARENT, depth -1
  * and anc 0 for every node of that batch element.  Bit-exact.

@@ -748,6 +748,30 @@ def test_tree_build_ties_and_dry(gpu_lib):
     assert np.array_equal(host(sc).view(np.uint32), rs.view(np.uint32))
 
 
+def test_tree_build_hand_worked_ties(gpu_lib):
+    """the hand-derived tie cases (tests/golden/tree_build_ties.json), each
+    case its own launch: every ordering decision is a tie"""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "tree_build_ties.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        say("tie case", c["name"])
+        lp = np.array([[-np.inf if x is None else x for x in row] for row in c["cand_logp"]],
+                      np.float32)[None]
+        ii, jj = np.meshgrid(np.arange(lp.shape[1]), np.arange(lp.shape[2]), indexing="ij")
+        tok = np.where(np.isfinite(lp[0]), 100 + 10 * ii + jj, -1).astype(np.int32)[None]
+        root = np.array([c["root_tok"]], np.int32)
+        par, tk, sc, nb = gpu_lib.build_tree(dev(lp), dev(tok), dev(root), c["width"],
+                                             c["max_depth"])
+        torch.cuda.synchronize()
+        want = np.array([-np.inf if x is None else x for x in c["score"]], np.float32)
+        assert host(nb).tolist() == [c["n_built"]]
+        assert host(par)[0].tolist() == c["parent"]
+        assert host(tk)[0].tolist() == c["token"]
+        assert np.array_equal(host(sc)[0].view(np.uint32), want.view(np.uint32))
+
+
 def test_tree_build_overflowing_scores(gpu_lib):
     # scores that overflow to -inf are still candidates (popped last, by push
     # order), and a +inf score is popped first

@@ -619,6 +619,50 @@ def test_tree_build_rounds_take_the_best_available(w):
         start += len(grp)
 
 
+def _tie_golden():
+    """the hand-worked tie cases: tables, tokens and expected arrays (null =
+    -inf / absent slot)"""
+    with open(os.path.join(GOLDEN, "tree_build_ties.json")) as f:
+        g = json.load(f)
+    out = []
+    for c in g["cases"]:
+        lp = np.array([[-np.inf if x is None else x for x in row] for row in c["cand_logp"]],
+                      np.float32)
+        ii, jj = np.meshgrid(np.arange(lp.shape[0]), np.arange(lp.shape[1]), indexing="ij")
+        tok = np.where(np.isfinite(lp), 100 + 10 * ii + jj, -1).astype(np.int32)
+        sc = np.array([-np.inf if x is None else x for x in c["score"]], np.float32)
+        out.append((c, lp, tok, sc))
+    return out
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_tree_build_tie_order_hand_worked(case):
+    """ties between equal scores go to the lower node id, then the lower slot
+    (hand-derived fixture; a reversed tie order changes every case)"""
+    c, lp, tok, sc = _tie_golden()[case]
+    par, tk, s, nb = oracle.build_tree(lp, tok, c["root_tok"], c["n"], c["width"],
+                                       c["max_depth"])
+    assert nb == c["n_built"]
+    assert par.tolist() == c["parent"]
+    assert tk.tolist() == c["token"]
+    assert np.array_equal(s, sc)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tree_build_width_one_ties_are_strict_best_first(seed):
+    """w = 1 on tables of small integer log-probs (most scores tie): the heap
+    matches the brute-force scan, whose ties go to the first (node, slot)"""
+    rng = np.random.default_rng(100 + seed)
+    lp = rng.choice(np.array([-1, -2, -3, -np.inf], np.float32), size=(24, 4))
+    lp[0, 0] = -1                              # the root proposes something
+    tok = np.arange(lp.size, dtype=np.int32).reshape(lp.shape)
+    for md in (2, 24):
+        par, _, _, nb = oracle.build_tree(lp, tok, 0, 24, 1, md)
+        ref = _strict_best_first(lp, 24, md)
+        assert nb == len(ref)
+        assert np.array_equal(par[:nb], ref)
+
+
 def test_tree_build_runs_dry_and_depth_cap():
     lp = np.full((10, 3), -np.inf, np.float32)
     lp[0, :2] = [-0.1, -0.5]
