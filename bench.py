@@ -12,30 +12,39 @@ weights.
 R independent input sets (default 16, ~1.2 GB in total plus pseudo-value
 buffers) are resident in HBM before timing and are used round-robin, so the
 256 MiB Infinity Cache cannot serve repeated reads.  Step i works on set
-i mod R: its state is advanced along the accepted path of its own tree,
-from the pseudo-values its previous step wrote from that same state (the
-commit then needs no solve), and its tree is verified again, writing fresh
-pseudo-values; a first call per set (no commit) seeds them.
+i mod R.  Two forms of the step are timed:
+  * commit solving (HEADLINE_STEP "solving"): set i's state is advanced
+    along the accepted path of set i - 1's tree (its tensors), the commit
+    solving for the pseudo-values itself, then set i's tree is verified;
+  * pseudo-values carried ("carried", fp32; "carried16", fp16): set i's
+    state is advanced along its own tree's accepted path from the
+    pseudo-values its previous step wrote from that same state (no solve),
+    then its tree is verified again, writing fresh pseudo-values.
 
-Timed regions (HIP events on the launch stream, start and end only, so no
-event fence sits between kernels), K launches each after 2R untimed ones:
-the fused step (the headline value), the same with fp16 pseudo-values, the
-fused step with the commit solving for the pseudo-values itself (set i - 1's
-path), the same step as two launches (gdn_tree_verify then gdn_tree_commit),
-verify alone and commit alone.  Launches are prepared
-once (binding Launch objects), so the host enqueues faster than the GPU
-drains and the events time the GPU.
+Timing: W untimed warmup steps, a clock-settle phase (≥ 30 ms of GPU work on
+the verify kernel, so the headline kernel's own dispatches are essentially
+its timed ones), then for each form `--regions` (default 5) timed regions of
+exactly K steps each, every region bracketed by a device synchronisation and
+timed by HIP events on the launch stream (the GPU is kept busy by R untimed
+launches queued ahead of the start event, so no launch latency enters).
+The reported time is the median region's mean launch time.  Launches are
+prepared once (binding Launch objects), so the host enqueues faster than the
+GPU drains.
 
-Side measurements (not the headline): the integer kernels of the step
-(acceptance walk, path extraction, tree construction); the tree-size-126
-comparison of the tree verify against single-branch recurrent
-verification; verify and commit on the batch-64, 128-node workload.
+Also timed, each as its own median of regions: the same step as two
+launches (gdn_tree_verify then gdn_tree_commit), verify alone and commit
+alone; the batch-1 / 32-node layer (latency, each launch replayed from a
+captured HIP graph so no host time enters); the 48-layer stack (batch 32,
+one fused launch per layer per step); the integer kernels (acceptance walk,
+path extraction, tree construction); the tree-size-126 comparison of the
+tree verify against single-branch recurrent verification; verify and commit
+on the batch-64, 128-node workload.
 
-Prints one JSON line.  `roofline` is for the fused kernel: algorithmic bytes
-per launch / its mean launch time.  `traffic` is read from the committed
-rocprofv3 counter summary when it was taken on the current kernel source,
-else null.  `cpu_baseline` times the fp64 oracle (test infrastructure) on
-the host cores on the same workload.
+Prints one JSON line.  `roofline` is for the headline kernel: algorithmic
+bytes per launch / its median launch time.  `traffic` is read from the
+committed rocprofv3 counter summary when it was taken on the current kernel
+source, else null.  `cpu_baseline` times the fp64 oracle (test
+infrastructure) on the host cores on the same workload.
 """
 from __future__ import annotations
 
@@ -43,6 +52,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -52,12 +62,20 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN tree-verify nodes/sec (B=64 tree, batch 16, 32 heads); achieved HBM GB/s"
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD_INDEX = 2
+# the form of the step reported as the headline value (see the docstring)
+HEADLINE_STEP = "carried"
 # arithmetic of the verify path: bf16 operands feed the MFMA contractions with
 # fp32 accumulation; everything else is fp32
 KERNEL_DTYPE = "bf16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "commit_verify_b16_n64_h32_d128_traffic.txt")
+TRAFFIC_FILES = {
+    "carried": os.path.join(ROOT, "profiles", "commit_verify_b16_n64_h32_d128_traffic.txt"),
+    "solving": os.path.join(ROOT, "profiles",
+                            "commit_verify_solving_b16_n64_h32_d128_traffic.txt"),
+}
 TRAFFIC_SOURCES = ("commit_verify_mfma.hip", "path_commit.hpp", "tree_verify.hpp",
                    "mfma_tile.hpp", "device_common.hpp")
+MAX_PATH = 13            # deepest path of the depth <= 12 trees, plus one
+GEN_WORKERS = 16         # host processes drawing the synthetic inputs
 
 
 def verify_bytes(batch, n, H, dk, dv, elem=2):
@@ -67,10 +85,10 @@ def verify_bytes(batch, n, H, dk, dv, elem=2):
     return batch * H * per_bh + batch * n * 4
 
 
-def commit_bytes(batch, H, dk, dv, path_lens, elem=2, max_path=None):
+def commit_bytes(batch, H, dk, dv, path_lens, elem=2):
     """state read + written once, plus k, v, alpha, beta of every path node and
     the path itself"""
-    m = int(sum(path_lens))
+    m = float(sum(path_lens))
     return (batch * H * 2 * 4 * dk * dv + m * H * ((dk + dv) * elem + 8)
             + m * 4 + batch * 4)
 
@@ -113,13 +131,15 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """per-launch HBM bytes from the committed counter summary, or None when
-    the fused kernel's source changed since the counters were taken"""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(step):
+    """per-launch HBM bytes of the headline kernel from the committed counter
+    summary, or None when the fused kernel's source changed since the
+    counters were taken"""
+    path = TRAFFIC_FILES.get(step)
+    if path is None or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.lstrip().startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
@@ -160,16 +180,51 @@ def cpu_baseline(ts, path, plen, budget_s=10.0):
             "verify_s_per_step": tv / steps, "commit_s_per_step": tc / steps}
 
 
+# ---------------------------------------------------------------------------
+# input generation (host processes, before the GPU is touched)
+# ---------------------------------------------------------------------------
+def _draw(job):
+    """One seeded input set of a workload; keeps the fp32 copies of q/k/v only
+    when asked (the oracle's CPU baseline needs them)."""
+    import gdn_synth as gs
+    kind, a, keep = job
+    if kind == "cfg":
+        wi, s = a
+        ts = gs.make_config(wi, s=s)
+    elif kind == "layer":
+        ts = gs.make_config(4, layer=a)
+    else:
+        ts = gs.make_tree126(a)
+    if not keep:
+        ts.q = ts.k = ts.v = None
+    return ts
+
+
+def draw_all(jobs, workers):
+    """every job drawn by a pool of fresh interpreter processes (a worker
+    that dies raises here instead of being replaced)"""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    nw = max(1, min(workers, len(os.sched_getaffinity(0)), len(jobs)))
+    if nw == 1:
+        return [_draw(j) for j in jobs]
+    with ProcessPoolExecutor(nw, mp_context=mp.get_context("spawn")) as pool:
+        return list(pool.map(_draw, jobs))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--regions", type=int, default=5, help="timed regions per measurement")
     ap.add_argument("--sets", type=int, default=16, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the tree-size-126 tree vs single-branch comparison and the "
                          "batch-64 / 128-node side measurement")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack")
+    ap.add_argument("--no-latency", action="store_true", help="skip the batch-1 latency leg")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -178,305 +233,366 @@ def main():
               "sequences or heads with no exchange step, but none is launched here.",
               file=sys.stderr)
         sys.exit(2)
+    K, NREG = args.steps, max(1, args.regions)
+    log = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
 
     import numpy as np
-    import torch
-
-    import gated_deltanet_tree_verify_amd as g
     import gdn_synth as gs
 
-    log = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
+    # ---- every input set, drawn on the host before the GPU is touched
+    t0 = time.time()
+    jobs = [("cfg", (WORKLOAD_INDEX, s), s == 0) for s in range(args.sets)]
+    if not args.no_latency:
+        jobs.append(("cfg", (1, 0), False))
+    if not args.no_stack:
+        jobs += [("layer", l, False) for l in range(gs.WORKLOADS[4].layers)]
+    if not args.no_compare:
+        jobs += [("t126", s, False) for s in range(8)]
+        jobs += [("cfg", (3, s), False) for s in range(2)]
+    drawn = draw_all(jobs, GEN_WORKERS)
+    pick = lambda kind, a: [ts for (k_, a_, _), ts in zip(jobs, drawn) if k_ == kind and
+                            (a is None or a_ == a or (isinstance(a_, tuple) and a_[0] == a))]
+    main_host = pick("cfg", WORKLOAD_INDEX)
+    log(f"drew {len(jobs)} input sets on {min(GEN_WORKERS, len(os.sched_getaffinity(0)))} "
+        f"host processes in {time.time() - t0:.1f}s")
+
+    import torch
+    import gated_deltanet_tree_verify_amd as g
+
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     g.load()
     w = gs.WORKLOADS[WORKLOAD_INDEX]
     batch, n, H, dk, dv = w.batch, w.n, w.H, w.d_k, w.d_v
     stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def dev(x):
         return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
-    sets, host0 = [], None
-    max_path = 13
-    t0 = time.time()
-    for s in range(args.sets):
-        ts = gs.make_config(WORKLOAD_INDEX, s=s)
+    def upload(ts, max_path):
         path, plen = ts.paths(max_path=max_path)
-        if s == 0:
-            host0 = (ts, path, plen)
-        d = dict(q=dev(ts.q_bits.view(np.int16)).view(torch.bfloat16),
-                 k=dev(ts.k_bits.view(np.int16)).view(torch.bfloat16),
-                 v=dev(ts.v_bits.view(np.int16)).view(torch.bfloat16),
-                 alpha=dev(ts.alpha), beta=dev(ts.beta), parent=dev(ts.parent), S=dev(ts.S0),
-                 path=dev(path), plen=dev(plen), plen_host=plen)
+        return dict(q=dev(ts.q_bits.view(np.int16)).view(torch.bfloat16),
+                    k=dev(ts.k_bits.view(np.int16)).view(torch.bfloat16),
+                    v=dev(ts.v_bits.view(np.int16)).view(torch.bfloat16),
+                    alpha=dev(ts.alpha), beta=dev(ts.beta), parent=dev(ts.parent),
+                    S=dev(ts.S0), path=dev(path), plen=dev(plen), plen_host=plen)
+
+    def regions(body, nsteps, preroll, nreg=NREG):
+        """median over nreg regions of the mean time (ms) of nsteps calls of
+        body(i); preroll untimed calls keep the GPU busy ahead of the start"""
+        per, host = [], []
+        i = 0
+        for _ in range(nreg):
+            torch.cuda.synchronize()
+            for _ in range(preroll):
+                body(i)
+                i += 1
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            h0 = time.perf_counter()
+            for _ in range(nsteps):
+                body(i)
+                i += 1
+            host.append((time.perf_counter() - h0) / nsteps)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / nsteps)
+        return statistics.median(per), per, statistics.median(host)
+
+    # ---- the batch-16 / 64-node layer, R rotating sets
+    sets = [upload(ts, MAX_PATH) for ts in main_host]
+    for d in sets:
         d["out"] = torch.empty((batch, n, H, dv), dtype=torch.float32, device="cuda")
-        sets.append(d)
     torch.cuda.synchronize()
     resident = sum(t.numel() * t.element_size() for d in sets for t in d.values()
                    if isinstance(t, torch.Tensor))
-    log(f"generated {args.sets} sets ({resident / 2**30:.2f} GiB resident) in {time.time() - t0:.1f}s")
-
+    log(f"{len(sets)} sets of {w.name} resident ({resident / 2**30:.2f} GiB)")
     R = len(sets)
-    # The step (fused_u): set i's state is advanced along its own tree's
-    # accepted path from the pseudo-values its previous verify wrote from that
-    # same state, then the tree is verified again and writes fresh
-    # pseudo-values (two buffers per set, alternating).  fused_solve,
-    # reported beside it: set i's state is advanced along set i - 1's path
-    # with the commit solving for the pseudo-values itself.
-    fused_u, fused_u16, seed_u16, fused_solve, ver, com = [], [], [], [], [], []
+    own = lambda d: (d["k"], d["v"], d["alpha"], d["beta"], d["parent"])
+    zero_plen = torch.zeros(batch, dtype=torch.int32, device="cuda")
+    carried, carried16, seed16, solving, ver, com = [], [], [], [], [], []
     for i, d in enumerate(sets):
-        own = (d["k"], d["v"], d["alpha"], d["beta"], d["parent"])
         for key, udt in (("u", torch.float32), ("u16", torch.float16)):
             d[key] = [torch.empty((batch, n, H, dv), dtype=udt, device="cuda") for _ in range(2)]
         # first call on this state: no commit, pseudo-values into u[0]
-        g.commit_verify(d["S"], d["path"], torch.zeros_like(d["plen"]), own, d["q"], d["k"],
-                        d["v"], d["alpha"], d["beta"], d["parent"], out=d["out"],
-                        u_out=d["u"][0], stream=stream)
-        fused_u.append([g.commit_verify(d["S"], d["path"], d["plen"], own, d["q"], d["k"],
-                                        d["v"], d["alpha"], d["beta"], d["parent"],
-                                        out=d["out"], u_prev=d["u"][par],
-                                        u_out=d["u"][1 - par], stream=stream, prepare=True)
-                        for par in range(2)])
-        seed_u16.append(g.commit_verify(d["S"], d["path"], torch.zeros_like(d["plen"]), own,
-                                        d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                        d["parent"], out=d["out"], u_out=d["u16"][0],
-                                        stream=stream, prepare=True))
-        fused_u16.append([g.commit_verify(d["S"], d["path"], d["plen"], own, d["q"], d["k"],
-                                          d["v"], d["alpha"], d["beta"], d["parent"],
-                                          out=d["out"], u_prev=d["u16"][par],
-                                          u_out=d["u16"][1 - par], stream=stream, prepare=True)
-                          for par in range(2)])
+        g.commit_verify(d["S"], d["path"], zero_plen, own(d), d["q"], d["k"], d["v"],
+                        d["alpha"], d["beta"], d["parent"], out=d["out"], u_out=d["u"][0],
+                        stream=stream)
+        fv = lambda d, key, par, up=True: g.commit_verify(
+            d["S"], d["path"], d["plen"], own(d), d["q"], d["k"], d["v"], d["alpha"],
+            d["beta"], d["parent"], out=d["out"], u_prev=d[key][par] if up else None,
+            u_out=d[key][1 - par], stream=stream, prepare=True)
+        carried.append([fv(d, "u", par) for par in range(2)])
+        carried16.append([fv(d, "u16", par) for par in range(2)])
+        seed16.append(g.commit_verify(d["S"], d["path"], zero_plen, own(d), d["q"], d["k"],
+                                      d["v"], d["alpha"], d["beta"], d["parent"], out=d["out"],
+                                      u_out=d["u16"][0], stream=stream, prepare=True))
         p = sets[(i - 1) % R]
-        fused_solve.append(g.commit_verify(d["S"], p["path"], p["plen"],
-                                           (p["k"], p["v"], p["alpha"], p["beta"], p["parent"]),
-                                           d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                           d["parent"], out=d["out"], stream=stream,
-                                           prepare=True))
+        solving.append(g.commit_verify(d["S"], p["path"], p["plen"], own(p), d["q"], d["k"],
+                                       d["v"], d["alpha"], d["beta"], d["parent"], out=d["out"],
+                                       stream=stream, prepare=True))
         ver.append(g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"],
                             out=d["out"], stream=stream, prepare=True))
         com.append(g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"],
                             d["parent"], stream=stream, prepare=True))
-    visits = [0] * R
+    visits = {"u": [0] * R, "u16": [0] * R}
 
-    def fused_step(i):
-        fused_u[i][visits[i] & 1]()
-        visits[i] += 1
+    def carried_step(i, key="u", calls=None):
+        j = i % R
+        (calls or carried)[j][visits[key][j] & 1]()
+        visits[key][j] += 1
 
+    steps = {
+        "carried": carried_step,
+        "carried16": lambda i: carried_step(i, "u16", carried16),
+        "solving": lambda i: solving[i % R](),
+    }
+    head = steps[HEADLINE_STEP]
     for i in range(args.warmup):
-        fused_step(i % R)
+        head(i)
     torch.cuda.synchronize()
-    # Clocks settle only after some milliseconds of sustained load: without
-    # this the first timed region runs ~10% slow whatever it holds.  Keep
-    # stepping (untimed) until 30 ms of GPU time have passed.
-    settle0, settle1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    settle0.record(stream)
+    # Clocks settle only after some milliseconds of sustained load; the
+    # settle phase runs the verify kernel, so that the headline kernel's
+    # dispatches are its warmup, its prerolls and its timed ones.
+    e0, e1 = ev(), ev()
+    e0.record(stream)
     settled = 0
     while True:
         for i in range(100):
-            fused_step(i % R)
-        settle1.record(stream)
-        settle1.synchronize()
+            ver[i % R]()
+        e1.record(stream)
+        e1.synchronize()
         settled += 100
-        if settle0.elapsed_time(settle1) >= 30.0 or settled >= 20000:
+        if e0.elapsed_time(e1) >= 30.0 or settled >= 20000:
             break
 
-    K = args.steps
-    host_s = {}
-
-    def timed(name, body):
-        for i in range(2 * R):   # settle this launch shape before its timed region
-            body(i % R)
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        h0 = time.perf_counter()
-        for i in range(K):
-            body(i % R)
-        host_s[name] = (time.perf_counter() - h0) / K
-        end.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / K
-
-    def separate(i):
-        ver[i]()
-        com[i]()
-
-    visits16 = [0] * R
-
-    def fused_step_u16(i):
-        fused_u16[i][visits16[i] & 1]()
-        visits16[i] += 1
-
-    ms_step = timed("fused", fused_step)
-    # the fp16 pseudo-value chain starts from a first call on each set's
-    # current state
+    res = {}
+    res[HEADLINE_STEP] = regions(head, K, R)
+    # the fp16 chain starts from a first call on each set's current state
     for i in range(R):
-        seed_u16[i]()
-    u16_ms = timed("fused_u16", fused_step_u16)
-    # back on the fp32 chain: reseed it from the current states
-    for i, d in enumerate(sets):
-        g.commit_verify(d["S"], d["path"], torch.zeros_like(d["plen"]),
-                        (d["k"], d["v"], d["alpha"], d["beta"], d["parent"]), d["q"], d["k"],
-                        d["v"], d["alpha"], d["beta"], d["parent"], out=d["out"],
-                        u_out=d["u"][visits[i] & 1], stream=stream)
-    solve_ms = timed("fused_solve", lambda i: fused_solve[i]())
-    sep_ms = timed("separate", separate)
-    ver_ms = timed("verify", lambda i: ver[i]())
-    com_ms = timed("commit", lambda i: com[i]())
-    recheck_ms = timed("fused_recheck", fused_step)
-    log(f"fused {ms_step * 1e3:.2f} us (again at the end: {recheck_ms * 1e3:.2f} us; fp16 "
-        f"pseudo-values: {u16_ms * 1e3:.2f} us; commit "
-        f"solving for its pseudo-values: {solve_ms * 1e3:.2f} us), "
-        f"separate {sep_ms * 1e3:.2f} us, verify {ver_ms * 1e3:.2f} "
-        f"us, commit {com_ms * 1e3:.2f} us per launch (host enqueue "
-        f"{host_s['fused'] * 1e6:.1f} us per fused launch)")
+        seed16[i]()
+    visits["u16"] = [0] * R
+    for name in ("carried", "carried16", "solving"):
+        if name not in res:
+            if name == "carried":
+                # reseed the fp32 chain from the current states
+                for j, d in enumerate(sets):
+                    g.commit_verify(d["S"], d["path"], zero_plen, own(d), d["q"], d["k"],
+                                    d["v"], d["alpha"], d["beta"], d["parent"], out=d["out"],
+                                    u_out=d["u"][visits["u"][j] & 1], stream=stream)
+            res[name] = regions(steps[name], K, R)
+    res["separate"] = regions(lambda i: (ver[i % R](), com[i % R]()), K, R)
+    res["verify"] = regions(lambda i: ver[i % R](), K, R)
+    res["commit"] = regions(lambda i: com[i % R](), K, R)
+    us = {k_: v_[0] * 1e3 for k_, v_ in res.items()}
+    log("batch-16 layer, median of %d regions of %d launches: " % (NREG, K) +
+        ", ".join(f"{k_} {v_:.2f} us" for k_, v_ in us.items()) +
+        f" (host enqueue {res[HEADLINE_STEP][2] * 1e6:.1f} us per launch)")
+    log(f"  {HEADLINE_STEP} regions: " + " ".join(f"{x * 1e3:.2f}" for x in res[HEADLINE_STEP][1]))
+
     nodes = batch * n
     mean_plen = float(np.mean([float(np.sum(d["plen_host"])) for d in sets]))
     vbytes = verify_bytes(batch, n, H, dk, dv)
     cbytes = commit_bytes(batch, H, dk, dv, [mean_plen])
     fbytes = fused_bytes(batch, n, H, dk, dv, [mean_plen])
+    ms_step = res[HEADLINE_STEP][0]
     step_s = ms_step * 1e-3
     achieved = fbytes / step_s / 1e9
-    traffic = read_traffic()
 
-    # the acceptance walk and path extraction that produce the next step's
-    # commit input (integer kernels, launch-latency bound), same trees
-    ts0 = host0[0]
+    # ---- the step's integer kernels on the same trees
+    ts0 = main_host[0]
     draft, vtok = gs.make_accept_tokens(np.random.default_rng(0), ts0.parent, p_match=0.8)
     dpar, ddraft, dvtok = dev(ts0.parent), dev(draft), dev(vtok)
     acc_call = g.accept(dpar, ddraft, dvtok, stream=stream, prepare=True)
     acc_t, _, _ = acc_call()
-    path_call = g.path(dpar, acc_t, max_path, stream=stream, prepare=True)
-
-    def timed_call(call, reps=200):
-        for _ in range(5):
-            call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
-
-    accept_us = timed_call(acc_call)
-    path_us = timed_call(path_call)
-    # the step before verify: width-8 best-first construction of the same
-    # batch's 64-node trees from a synthetic candidate table (K = 8)
+    path_call = g.path(dpar, acc_t, MAX_PATH, stream=stream, prepare=True)
     clp, ctok, croot = gs.candidate_table(np.random.default_rng(1), batch, n, 8)
     build_call = g.build_tree(dev(clp), dev(ctok), dev(croot), 8, 12, stream=stream,
                               prepare=True)
-    build_us = timed_call(build_call)
+    small = lambda call: regions(lambda i: call(), 100, 5, 3)[0] * 1e3
+    accept_us, path_us, build_us = small(acc_call), small(path_call), small(build_call)
+    sets = carried = carried16 = seed16 = solving = ver = com = None
+    torch.cuda.empty_cache()
 
-    # tree-size-126 comparison: the tree verify against single-branch
-    # recurrent verification (one chain per root-to-leaf branch) on the same
-    # inputs, 8 rotating sets of width-8 best-first trees of 126 nodes
+    # ---- batch 1, 32 heads, 32-node tree: latency of each launch, replayed
+    # from a captured HIP graph (64 launches per replay, no host time inside)
+    lat = None
+    if not args.no_latency:
+        w1 = gs.WORKLOADS[1]
+        ts1 = pick("cfg", 1)[0]
+        mp1 = int(ts1.paths()[1].max())
+        d = upload(ts1, mp1)
+        d["out"] = torch.empty((1, w1.n, w1.H, w1.d_v), dtype=torch.float32, device="cuda")
+        d["u"] = [torch.empty((1, w1.n, w1.H, w1.d_v), dtype=torch.float32, device="cuda")
+                  for _ in range(2)]
+        z1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        g.commit_verify(d["S"], d["path"], z1, own(d), d["q"], d["k"], d["v"], d["alpha"],
+                        d["beta"], d["parent"], out=d["out"], u_out=d["u"][0], stream=stream)
+        torch.cuda.synchronize()
+        S_keep = d["S"].clone()
+        kinds = {
+            "verify": lambda j: g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                         d["parent"], d["S"], out=d["out"]),
+            "commit": lambda j: g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"],
+                                         d["alpha"], d["beta"], d["parent"]),
+            "fused_solving": lambda j: g.commit_verify(
+                d["S"], d["path"], d["plen"], own(d), d["q"], d["k"], d["v"], d["alpha"],
+                d["beta"], d["parent"], out=d["out"]),
+            "fused_carried": lambda j: g.commit_verify(
+                d["S"], d["path"], d["plen"], own(d), d["q"], d["k"], d["v"], d["alpha"],
+                d["beta"], d["parent"], out=d["out"], u_prev=d["u"][j & 1],
+                u_out=d["u"][1 - (j & 1)]),
+        }
+        lat = {"workload": w1.name, "launches_per_graph": 64}
+        for name, call in kinds.items():
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for j in range(2):
+                    call(j)
+            stream.wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for j in range(64):
+                    call(j)
+            torch.cuda.synchronize()
+            lat[name + "_us"] = regions(lambda i: graph.replay(), 5, 1)[0] * 1e3 / 64
+            d["S"].copy_(S_keep)
+            del graph
+        log("batch-1 layer (graph-replayed launches): " +
+            ", ".join(f"{k_[:-3]} {v_:.2f} us" for k_, v_ in lat.items() if k_.endswith("_us")))
+        d = None
+        torch.cuda.empty_cache()
+
+    # ---- the 48-layer stack: batch 32, one 64-node tree per sequence shared
+    # by the layers; a step runs every layer's fused launch in layer order
+    stack = None
+    if not args.no_stack:
+        w4 = gs.WORKLOADS[4]
+        layers = pick("layer", None)
+        L = len(layers)
+        ls = [upload(ts, MAX_PATH) for ts in layers]
+        for d in ls:
+            d["out"] = torch.empty((w4.batch, w4.n, w4.H, w4.d_v), dtype=torch.float32,
+                                   device="cuda")
+        layers = None
+        zero32 = torch.zeros(w4.batch, dtype=torch.int32, device="cuda")
+        if HEADLINE_STEP == "solving":
+            calls = [[g.commit_verify(d["S"], d["path"], d["plen"], own(d), d["q"], d["k"],
+                                      d["v"], d["alpha"], d["beta"], d["parent"], out=d["out"],
+                                      stream=stream, prepare=True)] * 2 for d in ls]
+        else:
+            calls = []
+            for d in ls:
+                d["u"] = [torch.empty_like(d["out"]) for _ in range(2)]
+                g.commit_verify(d["S"], d["path"], zero32, own(d), d["q"], d["k"], d["v"],
+                                d["alpha"], d["beta"], d["parent"], out=d["out"],
+                                u_out=d["u"][0], stream=stream)
+                calls.append([g.commit_verify(
+                    d["S"], d["path"], d["plen"], own(d), d["q"], d["k"], d["v"], d["alpha"],
+                    d["beta"], d["parent"], out=d["out"], u_prev=d["u"][par],
+                    u_out=d["u"][1 - par], stream=stream, prepare=True) for par in range(2)])
+        torch.cuda.synchronize()
+        sres = {"par": 0}
+
+        def stack_step(i):
+            for c in calls:
+                c[sres["par"]]()
+            sres["par"] ^= 1
+
+        for i in range(max(1, args.warmup // 4)):
+            stack_step(i)
+        ms4, per4, _ = regions(stack_step, max(2, K // 4), 1)
+        m4 = float(np.mean([float(np.sum(d["plen_host"])) for d in ls]))
+        b4 = L * fused_bytes(w4.batch, w4.n, w4.H, w4.d_k, w4.d_v, [m4])
+        stack = {"workload": w4.name, "layers": L, "step": HEADLINE_STEP,
+                 "ms_per_step": ms4, "nodes_per_s": w4.batch * w4.n / (ms4 * 1e-3),
+                 "layer_launch_us": ms4 * 1e3 / L, "algorithmic_bytes_per_step": b4,
+                 "hbm_gbps": b4 / (ms4 * 1e-3) / 1e9,
+                 "frac": b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                 "regions_ms": per4, "steps_per_region": max(2, K // 4)}
+        log(f"48-layer stack: {ms4:.3f} ms/step ({ms4 * 1e3 / L:.1f} us per layer), "
+            f"{stack['hbm_gbps']:.0f} GB/s algorithmic ({stack['frac']:.3f} of 8 TB/s)")
+        ls = calls = None
+        torch.cuda.empty_cache()
+
+    # ---- tree-size-126 comparison and the batch-64 / 128-node workload
     cmp126 = b64 = None
     if not args.no_compare:
-        sets = fused_u = fused_u16 = seed_u16 = fused_solve = ver = com = None
-        torch.cuda.empty_cache()
         c_sets = []
-        for s_ in range(8):
-            ts = gs.make_tree126(s_)
-            c_sets.append(dict(q=dev(ts.q_bits.view(np.int16)).view(torch.bfloat16),
-                               k=dev(ts.k_bits.view(np.int16)).view(torch.bfloat16),
-                               v=dev(ts.v_bits.view(np.int16)).view(torch.bfloat16),
-                               alpha=dev(ts.alpha), beta=dev(ts.beta), parent=dev(ts.parent),
-                               S=dev(ts.S0), leaves=sum(len(gs.leaves(p)) for p in ts.parent),
-                               steps=sum(branch_node_steps(p) for p in ts.parent)))
-        for d in c_sets:
+        for ts in pick("t126", None):
+            d = upload(ts, ts.parent.shape[1])
+            d["leaves"] = sum(len(gs.leaves(p)) for p in ts.parent)
+            d["steps"] = sum(branch_node_steps(p) for p in ts.parent)
             d["out"] = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+            c_sets.append(d)
         tv126 = [g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"],
                           out=d["out"], stream=stream, prepare=True) for d in c_sets]
         bv126 = [g.branch_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
                                  d["S"], out=d["out"], stream=stream, prepare=True)
                  for d in c_sets]
-
-        def timed_list(calls, reps):
-            for i in range(3):
-                calls[i % len(calls)]()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(reps):
-                calls[i % len(calls)]()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / reps
-
-        t_tree = timed_list(tv126, 40)
-        t_branch = timed_list(bv126, 10)
+        t_tree = regions(lambda i: tv126[i % 8](), 40, 8)[0] * 1e3
+        t_branch = regions(lambda i: bv126[i % 8](), 10, 2, 3)[0] * 1e3
         w126 = gs.TREE126
         # what the branch baseline computes: per branch node and head,
         # w = S^T k (2 d^2 flops), the update alpha S + (beta k)(v - alpha w)^T
         # (3 d^2) and o = S^T q (2 d^2); on the fp32 vector peak this is a
         # floor for any recurrent branch verify on this chip
-        steps = float(np.mean([d["steps"] for d in c_sets]))   # per set, all sequences
-        branch_flop = steps * w126.H * 7 * w126.d_k * w126.d_v
+        steps126 = float(np.mean([d["steps"] for d in c_sets]))   # per set, all sequences
+        branch_flop = steps126 * w126.H * 7 * w126.d_k * w126.d_v
         floor_us = branch_flop / FP32_VECTOR_PEAK * 1e6
         cmp126 = {"workload": w126.name, "tree_verify_us": t_tree, "branch_verify_us": t_branch,
                   "speedup": t_branch / t_tree,
-                  "branch_node_steps_per_tree": steps / w126.batch,
+                  "branch_node_steps_per_tree": steps126 / w126.batch,
                   "branch_tflop_per_s": branch_flop / (t_branch * 1e-6) / 1e12,
                   "branch_fp32_floor_us": floor_us,
                   "speedup_vs_branch_floor": floor_us / t_tree,
                   "mean_leaves_per_tree": float(np.mean([d["leaves"] / w126.batch
                                                          for d in c_sets])),
                   "tree_verify_nodes_per_s": w126.batch * w126.n / (t_tree * 1e-6),
+                  "tree_verify_hbm_gbps": verify_bytes(w126.batch, w126.n, w126.H, w126.d_k,
+                                                       w126.d_v) / (t_tree * 1e-6) / 1e9,
                   "pages_speedup_b200": 7.1}
         log(f"n=126: tree verify {t_tree:.1f} us, branch verify {t_branch:.1f} us, "
             f"speedup {t_branch / t_tree:.2f} (branch at {cmp126['branch_tflop_per_s']:.1f} "
             f"TFLOP/s; its fp32 floor {floor_us:.0f} us, {floor_us / t_tree:.2f}x the tree)")
         c_sets = tv126 = bv126 = None
-
-        # the batch-64, 128-node workload (a quarter chains, a quarter stars
-        # and 16-ary bushes, half random recursive trees): verify and the
-        # commit of each sequence's accepted branch, 2 rotating sets of
-        # ~0.6 GB each
         torch.cuda.empty_cache()
+
         w3 = gs.WORKLOADS[3]
         b_sets = []
-        for s_ in range(2):
-            ts = gs.make_config(3, s=s_)
-            pth, pl = ts.paths(max_path=w3.n)
-            b_sets.append(dict(q=dev(ts.q_bits.view(np.int16)).view(torch.bfloat16),
-                               k=dev(ts.k_bits.view(np.int16)).view(torch.bfloat16),
-                               v=dev(ts.v_bits.view(np.int16)).view(torch.bfloat16),
-                               alpha=dev(ts.alpha), beta=dev(ts.beta), parent=dev(ts.parent),
-                               S=dev(ts.S0), path=dev(pth), plen=dev(pl),
-                               m=float(np.sum(pl))))
-            b_sets[-1]["out"] = torch.empty((w3.batch, w3.n, w3.H, w3.d_v), dtype=torch.float32,
-                                            device="cuda")
+        for ts in pick("cfg", 3):
+            d = upload(ts, w3.n)
+            d["m"] = float(np.sum(d["plen_host"]))
+            d["out"] = torch.empty((w3.batch, w3.n, w3.H, w3.d_v), dtype=torch.float32,
+                                   device="cuda")
+            b_sets.append(d)
         vb = [g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"],
                        out=d["out"], stream=stream, prepare=True) for d in b_sets]
         cb = [g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"],
                        d["parent"], stream=stream, prepare=True) for d in b_sets]
-        t_vb = timed_list(vb, 20)
-        t_cb = timed_list(cb, 20)
+        t_vb = regions(lambda i: vb[i % 2](), 20, 2)[0] * 1e3
+        t_cb = regions(lambda i: cb[i % 2](), 20, 2)[0] * 1e3
         vb_bytes = verify_bytes(w3.batch, w3.n, w3.H, w3.d_k, w3.d_v)
         cb_bytes = commit_bytes(w3.batch, w3.H, w3.d_k, w3.d_v,
                                 [float(np.mean([d["m"] for d in b_sets]))])
         b64 = {"workload": w3.name, "verify_us": t_vb, "commit_us": t_cb,
                "verify_nodes_per_s": w3.batch * w3.n / (t_vb * 1e-6),
                "verify_hbm_gbps": vb_bytes / (t_vb * 1e-6) / 1e9,
+               "verify_frac": vb_bytes / (t_vb * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                "commit_hbm_gbps": cb_bytes / (t_cb * 1e-6) / 1e9,
                "verify_algorithmic_bytes": vb_bytes, "commit_algorithmic_bytes": cb_bytes}
         log(f"b64/n128: verify {t_vb:.1f} us ({b64['verify_hbm_gbps']:.0f} GB/s), commit "
             f"{t_cb:.1f} us ({b64['commit_hbm_gbps']:.0f} GB/s)")
         b_sets = vb = cb = None
+        torch.cuda.empty_cache()
 
-    # achievable-bandwidth line: a plain 1 GiB device copy
+    # ---- achievable-bandwidth line: a plain 1 GiB device copy
     src = torch.empty(2**28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 5 * 2 * src.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    copy_ms = regions(lambda i: dst.copy_(src), 5, 1, 3)[0]
+    copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
 
     result = {
@@ -494,31 +610,42 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": batch, "tree_nodes": n, "heads": H, "d_k": dk,
                    "d_v": dv, "tree": "width-8 best-first, depth<=12", "rotating_sets": R,
-                   "step": "commit the accepted path (pseudo-values carried from the previous "
-                           "verify) + verify the trees, writing their pseudo-values (one launch)"},
+                   "step": {"carried": "commit the accepted path (fp32 pseudo-values carried "
+                                       "from the previous verify) + verify the trees, writing "
+                                       "their pseudo-values (one launch)",
+                            "solving": "commit the previous trees' accepted paths (the commit "
+                                       "solving for its pseudo-values) + verify the trees "
+                                       "(one launch)"}[HEADLINE_STEP],
+                   "timing": f"median of {NREG} regions of {K} launches"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "gdn_tree_commit_verify", "algorithmic_bytes_per_launch": fbytes,
-                     "mean_launch_us": step_s * 1e6},
-        "fused_u16_us": u16_ms * 1e3,
-        "fused_commit_solving_us": solve_ms * 1e3,
-        "separate_step_us": sep_ms * 1e3,
-        "separate_step_nodes_per_s": nodes / (sep_ms * 1e-3),
-        "verify_us": ver_ms * 1e3,
-        "commit_us": com_ms * 1e3,
-        "verify_nodes_per_s": nodes / (ver_ms * 1e-3),
-        "verify_hbm_gbps": vbytes / (ver_ms * 1e-3) / 1e9,
-        "commit_hbm_gbps": cbytes / (com_ms * 1e-3) / 1e9,
-        "host_enqueue_us_per_step": host_s["fused"] * 1e6,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": read_traffic(HEADLINE_STEP),
+                     "kernel": "gdn_tree_commit_verify (%s)" % HEADLINE_STEP,
+                     "algorithmic_bytes_per_launch": fbytes,
+                     "median_launch_us": step_s * 1e6, "target_frac": 0.60},
+        "region_us": {k_: [x * 1e3 for x in v_[1]] for k_, v_ in res.items()},
+        "fused_carried_us": us["carried"],
+        "fused_carried_fp16_us": us["carried16"],
+        "fused_solving_us": us["solving"],
+        "separate_step_us": us["separate"],
+        "separate_step_nodes_per_s": nodes / (res["separate"][0] * 1e-3),
+        "verify_us": us["verify"],
+        "commit_us": us["commit"],
+        "verify_nodes_per_s": nodes / (res["verify"][0] * 1e-3),
+        "verify_hbm_gbps": vbytes / (res["verify"][0] * 1e-3) / 1e9,
+        "commit_hbm_gbps": cbytes / (res["commit"][0] * 1e-3) / 1e9,
+        "host_enqueue_us_per_step": res[HEADLINE_STEP][2] * 1e6,
         "copy_gbps": copy_gbps,
         "tree_build_us": build_us,
         "accept_us": accept_us,
         "path_us": path_us,
+        "b1_n32": lat,
+        "stack48": stack,
         "tree126_vs_branch": cmp126,
         "b64_n128": b64,
     }
     if not args.no_cpu_baseline:
-        ts, path, plen = host0
+        ts = main_host[0]
+        path, plen = ts.paths(max_path=MAX_PATH)
         result["cpu_baseline"] = cpu_baseline(ts, path, plen)
     print(json.dumps(result), flush=True)
 

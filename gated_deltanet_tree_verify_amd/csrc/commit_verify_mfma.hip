@@ -12,9 +12,9 @@
 // Schedule.  The only verify work that needs the state is Q S, K S and what
 // follows; the Gram matrices, masks and block inverses of the new tree need
 // only q, k and the parents.  So waves 0-2 request the q and k rows first
-// (wave 3 meanwhile reads the gates and the previous path: ids, then the
-// parents that validate it and the first chunk's rows and gates, and builds
-// the topology), every wave its first state tiles once q and k are in, then
+// (wave 3 meanwhile reads the gates, the previous path's ids together with
+// the previous tree's parent row, which validates the path, then the first
+// chunk's rows and gates, and builds the topology), every wave its first state tiles once q and k are in, then
 // the rest of its slab (one tile per tree-matrix phase) and last its v rows;
 // the tree matrices are built while the state streams in.
 //   * Pseudo-values carried (u_prev): while waves 0-2 compute the masks,
@@ -140,17 +140,23 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     const uint32_t pbytes = (uint32_t)((size_t)n_prev * H * kD * 2);
     const int32_t *ppar = parent_prev + (size_t)s.b * n_prev;
 
-    // ---- 1. loads: wave 3 first takes the new tree's gates and the path
-    //         ids, every wave its q/k/v rows, then its state slab; wave 3
-    //         requests the path parents and first chunk rows in between
+    // ---- 1. loads: wave 3 first takes the new tree's gates, the path ids
+    //         and the previous parents, every wave its q/k/v rows, then its
+    //         state slab; wave 3 requests the first chunk rows in between
     Gates gt{-1, 1.f, 0.f, false};
     pc::PathLanes pl{-1, -1, -2, -2};
+    // the previous tree's parent row (nodes l and 64 + l), read whole and
+    // independently of the path ids: the parents of the path nodes come out
+    // of it by lane shuffles, and with u_prev the whole tree is checked
+    int pp0 = -1, pp1 = -1;
     if (c.w == 3) {
         gt = load_gates(c, s, parent, alpha, beta);
         const int32_t *prow = path + (size_t)s.b * max_path;
         const int lim = min(min(mlen, max_path), kMaxPathIds);
         if (c.l < lim) pl.id0 = prow[c.l];
         if (64 + c.l < lim) pl.id1 = prow[64 + c.l];
+        if (c.l < n_prev) pp0 = ppar[c.l];
+        if (64 + c.l < n_prev) pp1 = ppar[64 + c.l];
     }
     uint4 rq[6], rk[6], rv[4];
     if (c.w < 3) {
@@ -166,8 +172,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     if (c.w == 3) {
         // parents of the path ids (ids out of range fail validation by
         // themselves) and the first chunk's rows and gates
-        if (pl.id0 >= 0 && pl.id0 < n_prev) pl.par0 = ppar[pl.id0];
-        if (pl.id1 >= 0 && pl.id1 < n_prev) pl.par1 = ppar[pl.id1];
+        pl.par0 = pc::parent_of(pl.id0, pp0, pp1, n_prev);
+        pl.par1 = pc::parent_of(pl.id1, pp0, pp1, n_prev);
         // ids for every wave's u or v loads
         if (pl.id0 >= 0) sm.pid[c.l] = pl.id0;
         if (pl.id1 >= 0) sm.pid[64 + c.l] = pl.id1;
@@ -225,7 +231,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     const bool tree_ok = !sm.tp.bad;
     // wave 3: the previous path's validity (and the fault flags)
     auto validate = [&]() -> bool {
-        const bool ok = pc::path_valid(pl, mlen, max_path, n_prev, c.l);
+        // with u_prev, a malformed previous tree counts as a bad path: the
+        // call that verified it wrote NaN pseudo-values
+        const bool ok = pc::path_valid(pl, mlen, max_path, n_prev, c.l) &&
+                        (!kU || pc::tree_valid(pp0, pp1, n_prev, c.l));
         if (c.l == 0) {
             sm.commit_ok = ok;
             if (s.hd == 0 && status)

@@ -93,6 +93,22 @@ __device__ __forceinline__ int slot_id(const PathLanes &p, int j) {
     return j < 64 ? a : b;
 }
 
+// parent of node id (or -2 for an id outside [0, n)) from a parent row held
+// by one wave, lane l holding the parents of nodes l (pp0) and 64 + l (pp1);
+// every lane of the wave must take part
+__device__ __forceinline__ int parent_of(int id, int pp0, int pp1, int n) {
+    const int a = __shfl(pp0, id & 63), b = __shfl(pp1, id & 63);
+    if (id < 0 || id >= n) return -2;
+    return id < 64 ? a : b;
+}
+
+// every parent of a tree of n <= 128 nodes held as in parent_of lies in
+// [-1, node)
+__device__ __forceinline__ bool tree_valid(int pp0, int pp1, int n, int l) {
+    const bool bad = (l < n && !parent_ok(pp0, l)) || (64 + l < n && !parent_ok(pp1, 64 + l));
+    return __ballot(bad) == 0ull;
+}
+
 // a path is valid when 0 <= m <= max_path, its ids lie in [0, n) and
 // increase, the first is a root and each later id's parent is the previous id
 __device__ __forceinline__ bool path_valid(const PathLanes &p, int m, int max_path, int n,

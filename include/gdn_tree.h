@@ -153,7 +153,9 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path,
  * must be the u_out that the call verifying the previous tree wrote from
  * this same S: the commit then applies that sum directly instead of
  * solving again (faster; same result up to rounding).  Other u_prev values
- * give that sum, not the commit.  The first call of a decode loop passes
+ * give that sum, not the commit.  With u_prev, a previous tree whose parent
+ * row is malformed (its verify wrote NaN pseudo-values) counts as a bad
+ * path: GDN_FAULT_BAD_PATH, S[b] left bit-unchanged.  The first call of a decode loop passes
  * path_len = 0 and u_prev = NULL.  u_dtype (read only when u_prev or u_out
  * is given) is the element type of both: GDN_DTYPE_F32, or GDN_DTYPE_F16
  * for half the bytes, u rounded to the nearest fp16 when written (relative

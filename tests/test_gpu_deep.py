@@ -1,0 +1,284 @@
+"""GPU parity on deep and wide trees, and on whole workload tensors.
+
+The 64-node kernels (gdn_tree_verify for n <= 64 and the fused
+gdn_tree_commit_verify) on the tree shapes that stress them most: chains of
+64, 63 and 33 nodes (the last pointer-jumping rounds of the topology, and a
+dense coupling block X_10 between the two 32-row halves of the solve), a
+64-node star, an 8-ary breadth-first bush and a two-root forest.  The
+method is the DFlash-TfM page's rollback-free tree verification for GDN:
+the tree is topologically sorted, X and Y follow the ancestor relations,
+(I + X) U = beta V (with the committed-state term) is solved without
+touching the state, and the commit follows the accepted branch.
+
+Every comparison is against the fp64 oracle over the whole output tensor:
+max|gpu - ref| / max|ref| <= 2e-3 (bf16 q/k/v, fp32 state).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_synth as gs
+import oracle
+from gpu_util import dev, host, upload
+
+pytestmark = pytest.mark.gpu
+
+BF16_GATE = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def forest64():
+    """two roots: a 20-node chain and a random tree of 44 nodes below the
+    second root (node 20)"""
+    rng = np.random.default_rng(77)
+    p = gs.random_recursive_tree(rng, 44, max_depth=20) + 20
+    p[0] = -1
+    return np.concatenate([gs.chain_tree(20), p]).astype(np.int32)
+
+
+def deep_random_tree(rng, n):
+    """a deep random tree: node i hangs below one of its few predecessors
+    (i - g with g ~ Geometric(0.6)), so depth grows with n and side branches
+    stay short"""
+    p = np.full(n, -1, np.int32)
+    for i in range(1, n):
+        p[i] = max(0, i - int(rng.geometric(0.6)))
+    return p
+
+
+def deep_set_n64():
+    """batch of five 64-node trees: chain, star, 8-ary bush, forest, and a
+    deep random tree"""
+    rng = np.random.default_rng(64)
+    par = np.stack([gs.chain_tree(64), gs.star_tree(64), gs.kary_bfs_tree(64, 8), forest64(),
+                    deep_random_tree(rng, 64)])
+    depth = np.array([max(gs._depths(p)) for p in par])
+    assert depth.tolist()[:3] == [63, 1, 2] and depth[4] > 32
+    return par
+
+
+# ---------------------------------------------------------------------------
+# verify, n <= 64 kernel
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["n64_mixed", "chain63", "chain33", "chain32", "chain1"])
+def test_verify_deep_trees_n64(gpu_lib, case):
+    say("verify deep", case)
+    par = {"n64_mixed": deep_set_n64(), "chain63": np.stack([gs.chain_tree(63)] * 2),
+           "chain33": np.stack([gs.chain_tree(33)] * 2),
+           "chain32": np.stack([gs.chain_tree(32)] * 2),
+           "chain1": np.stack([gs.chain_tree(1)] * 2)}[case]
+    ts = gs.make_set(par, 4, 128, 128, "bf16", seed=600 + par.shape[1])
+    d = upload(ts)
+    st = torch.full((par.shape[0],), -7, dtype=torch.int32, device="cuda")
+    out = gpu_lib.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S0"],
+                         status=st)
+    torch.cuda.synchronize()
+    ref, rst = oracle.verify_set(ts)
+    assert host(st).tolist() == rst.tolist() == [0] * par.shape[0]
+    err = oracle.rel_err(host(out), ref)
+    say("rel err", err)
+    assert err <= BF16_GATE
+    for b in range(par.shape[0]):
+        assert oracle.rel_err(host(out)[b], ref[b]) <= BF16_GATE, b
+
+
+# ---------------------------------------------------------------------------
+# fused commit + verify on the same shapes, both commit modes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["solving", "carried_fp32", "carried_fp16"])
+def test_commit_verify_deep_trees_n64(gpu_lib, mode):
+    """call 1 verifies tree set A (no commit) and, for the carried modes,
+    writes its pseudo-values; call 2 commits each sequence's accepted branch
+    of A (a 64-node path on the chain, deep branches elsewhere) and verifies
+    tree set B.  Both calls' outputs, the pseudo-values and the committed
+    state against the oracle, whole tensors."""
+    say("commit-verify deep", mode)
+    pa = deep_set_n64()
+    pb = deep_set_n64()[::-1].copy()
+    acc = np.array([63, 17, 63, 19, 0], np.int32)
+    acc[4] = int(np.argmax(gs._depths(pa[4])))          # the deepest node
+    A = gs.make_set(pa, 4, 128, 128, "bf16", seed=611, accepted=acc)
+    B = gs.make_set(pb, 4, 128, 128, "bf16", seed=612)
+    dA, dB = upload(A), upload(B)
+    path, plen = A.paths(max_path=64)
+    assert plen.tolist()[:4] == [64, 2, 3, 20]
+    udt = {"solving": None, "carried_fp32": torch.float32, "carried_fp16": torch.float16}[mode]
+    uA = uB = None
+    if udt is not None:
+        uA = torch.empty(dA["v"].shape, dtype=udt, device="cuda")
+        uB = torch.empty(dB["v"].shape, dtype=udt, device="cuda")
+    S = dA["S0"].clone()
+    prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
+    st = torch.full((5,), -7, dtype=torch.int32, device="cuda")
+    outA = gpu_lib.commit_verify(S, dev(path), dev(np.zeros(5, np.int32)), prevA, dA["q"],
+                                 dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"],
+                                 u_out=uA, status=st)
+    torch.cuda.synchronize()
+    refA, _ = oracle.verify_set(A)
+    assert host(st).tolist() == [0] * 5 and torch.equal(S, dA["S0"])
+    eA = oracle.rel_err(host(outA), refA)
+    say("call 1 out rel err", eA)
+    assert eA <= BF16_GATE
+    if uA is not None:
+        UA, _ = oracle.pseudo_set(A)
+        eu = oracle.rel_err(host(uA), UA)
+        say("call 1 u rel err", eu)
+        assert eu <= BF16_GATE
+    outB = gpu_lib.commit_verify(S, dev(path), dev(plen), prevA, dB["q"], dB["k"], dB["v"],
+                                 dB["alpha"], dB["beta"], dB["parent"], u_prev=uA, u_out=uB,
+                                 status=st)
+    torch.cuda.synchronize()
+    Sref, cst = oracle.commit_set(A, path_arr=path, path_len=plen)
+    oref, vst = oracle.verify(B.q, B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert host(st).tolist() == (cst | vst).tolist() == [0] * 5
+    es, eo = oracle.rel_err(host(S), Sref), oracle.rel_err(host(outB), oref)
+    say("call 2 rel err S", es, "out", eo)
+    assert es <= BF16_GATE and eo <= BF16_GATE
+    for b in range(5):
+        assert oracle.rel_err(host(S)[b], Sref[b]) <= BF16_GATE, b
+        assert oracle.rel_err(host(outB)[b], oref[b]) <= BF16_GATE, b
+    if uB is not None:
+        UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+        assert oracle.rel_err(host(uB), UB) <= BF16_GATE
+
+
+@pytest.mark.parametrize("udt", [torch.float32, torch.float16])
+def test_carried_commit_rejects_a_faulted_previous_tree(gpu_lib, udt):
+    """a well-formed path through a previous tree whose parent row is
+    malformed elsewhere: that tree's verify wrote NaN pseudo-values, so the
+    carried commit must not use them (GDN_FAULT_BAD_PATH, state unchanged);
+    the solving commit, which needs only the path, commits it"""
+    rng = np.random.default_rng(71)
+    pa = np.stack([gs.random_recursive_tree(rng, 48, max_depth=10) for _ in range(3)])
+    acc = np.array([gs.pick_leaf(rng, pa[i]) for i in range(3)], np.int32)
+    path_nodes = set(gs.path_to(pa[1], int(acc[1])).tolist())
+    bad = max(i for i in range(1, 48) if i not in path_nodes)
+    pa[1, bad] = bad                       # sequence 1: malformed, off its path
+    A = gs.make_set(pa, 2, 128, 128, "bf16", seed=71, accepted=acc)
+    B = gs.make_set(np.stack([gs.random_recursive_tree(rng, 48, max_depth=10)
+                              for _ in range(3)]), 2, 128, 128, "bf16", seed=72)
+    dA, dB = upload(A), upload(B)
+    prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
+    path, plen = A.paths(max_path=13)
+    uA = torch.empty(dA["v"].shape, dtype=udt, device="cuda")
+    S = dA["S0"].clone()
+    st = torch.full((3,), -7, dtype=torch.int32, device="cuda")
+    gpu_lib.commit_verify(S, dev(path), dev(np.zeros(3, np.int32)), prevA, dA["q"], dA["k"],
+                          dA["v"], dA["alpha"], dA["beta"], dA["parent"], u_out=uA, status=st)
+    torch.cuda.synchronize()
+    assert host(st).tolist() == [0, 1, 0]
+    assert np.isnan(host(uA)[1]).all()
+    Sref, cst = oracle.commit_set(A, path_arr=path, path_len=plen)
+    assert cst.tolist() == [0, 0, 0]       # the path alone is valid
+    oref_moved, _ = oracle.verify(B.q, B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    oref_kept, _ = oracle.verify(B.q, B.k, B.v, B.alpha, B.beta, B.parent, A.S0)
+    # carried: sequence 1 keeps its state
+    out = gpu_lib.commit_verify(S, dev(path), dev(plen), prevA, dB["q"], dB["k"], dB["v"],
+                                dB["alpha"], dB["beta"], dB["parent"], u_prev=uA, status=st)
+    torch.cuda.synchronize()
+    assert host(st).tolist() == [0, 2, 0]
+    Sh, oh = host(S), host(out)
+    assert np.array_equal(Sh[1], A.S0[1]) and not np.isnan(Sh).any()
+    assert oracle.rel_err(Sh[[0, 2]], Sref[[0, 2]]) <= BF16_GATE
+    assert oracle.rel_err(oh[1], oref_kept[1]) <= BF16_GATE
+    assert oracle.rel_err(oh[[0, 2]], oref_moved[[0, 2]]) <= BF16_GATE
+    # solving: every path is committed
+    S2 = dA["S0"].clone()
+    gpu_lib.commit_verify(S2, dev(path), dev(plen), prevA, dB["q"], dB["k"], dB["v"],
+                          dB["alpha"], dB["beta"], dB["parent"], status=st)
+    torch.cuda.synchronize()
+    assert host(st).tolist() == [0, 0, 0]
+    assert oracle.rel_err(host(S2), Sref) <= BF16_GATE
+
+
+# ---------------------------------------------------------------------------
+# whole workload tensors
+# ---------------------------------------------------------------------------
+def test_verify_layer_b64_n128_full(gpu_lib):
+    """the batch-64, 128-node workload (a quarter chains, a quarter stars and
+    16-ary bushes, half random recursive trees), whole output tensor, and the
+    commit of every sequence's accepted branch, whole state"""
+    say("verify b64 n128 full")
+    ts = gs.make_config(3)
+    d = upload(ts)
+    st = torch.full((64,), -7, dtype=torch.int32, device="cuda")
+    out = gpu_lib.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S0"],
+                         status=st)
+    path, plen = ts.paths(max_path=128)
+    S = d["S0"].clone()
+    gpu_lib.commit(S, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"])
+    torch.cuda.synchronize()
+    ref, rst = oracle.verify_set(ts)
+    assert host(st).tolist() == rst.tolist() == [0] * 64
+    err = oracle.rel_err(host(out), ref)
+    say("verify rel err", err)
+    assert err <= BF16_GATE
+    for b in range(64):
+        assert oracle.rel_err(host(out)[b], ref[b]) <= BF16_GATE, b
+    Sref, _ = oracle.commit_set(ts, path_arr=path, path_len=plen)
+    es = oracle.rel_err(host(S), Sref)
+    say("commit rel err", es)
+    assert es <= BF16_GATE
+
+
+def test_stack48_layers_from_the_stacked_run(gpu_lib):
+    """the 48-layer stack (batch 32, 32 heads, one 64-node tree per sequence
+    shared by all layers): per-layer tensors stacked in one allocation each,
+    every layer's decode step run in layer order (a fused call verifying the
+    tree from the layer's state and writing its pseudo-values, then a fused
+    call committing the accepted branch from them and verifying the tree
+    again); layers 0 and 47 hold the workload's seeded tensors and are
+    checked whole against the oracle, the other layers hold other random
+    values."""
+    say("stack48 stacked run")
+    L = 48
+    t0, t47 = gs.make_config(4, layer=0), gs.make_config(4, layer=47)
+    assert np.array_equal(t0.parent, t47.parent)
+    d0, d47 = upload(t0), upload(t47)
+    gen = torch.Generator(device="cuda").manual_seed(4)
+
+    def stack(key, fill):
+        x = torch.empty((L,) + tuple(d0[key].shape), dtype=d0[key].dtype, device="cuda")
+        x[0], x[L - 1] = d0[key], d47[key]
+        for l in range(1, L - 1):
+            x[l] = fill(x[l].shape)
+        return x
+
+    nrm = lambda s: torch.nn.functional.normalize(
+        torch.randn(s, generator=gen, device="cuda"), dim=-1).to(torch.bfloat16)
+    q, k = stack("q", nrm), stack("k", nrm)
+    v = stack("v", lambda s: torch.randn(s, generator=gen, device="cuda").to(torch.bfloat16))
+    uni = lambda s: torch.rand(s, generator=gen, device="cuda") * 0.98 + 0.01
+    alpha, beta = stack("alpha", uni), stack("beta", uni)
+    S = stack("S0", lambda s: torch.randn(s, generator=gen, device="cuda") / 128 ** 0.5)
+    S0_47 = S[L - 1].clone()
+    parent = d0["parent"]
+    path, plen = t0.paths(max_path=13)
+    dpath, dplen, zero = dev(path), dev(plen), dev(np.zeros(32, np.int32))
+    out1 = torch.empty_like(v, dtype=torch.float32)
+    out2 = torch.empty_like(out1)
+    u = torch.empty_like(out1)
+    st = torch.full((L, 32), -7, dtype=torch.int32, device="cuda")
+    for l in range(L):
+        prev = (k[l], v[l], alpha[l], beta[l], parent)
+        gpu_lib.commit_verify(S[l], dpath, zero, prev, q[l], k[l], v[l], alpha[l], beta[l],
+                              parent, out=out1[l], u_out=u[l], status=st[l])
+    for l in range(L):
+        prev = (k[l], v[l], alpha[l], beta[l], parent)
+        gpu_lib.commit_verify(S[l], dpath, dplen, prev, q[l], k[l], v[l], alpha[l], beta[l],
+                              parent, out=out2[l], u_prev=u[l], status=st[l])
+    torch.cuda.synchronize()
+    assert host(st).tolist() == [[0] * 32] * L
+    for l, ts in ((0, t0), (L - 1, t47)):
+        ref1, _ = oracle.verify_set(ts)
+        Sref, _ = oracle.commit_set(ts, path_arr=path, path_len=plen)
+        ref2, _ = oracle.verify(ts.q, ts.k, ts.v, ts.alpha, ts.beta, ts.parent, Sref)
+        e1 = oracle.rel_err(host(out1[l]), ref1)
+        es = oracle.rel_err(host(S[l]), Sref)
+        e2 = oracle.rel_err(host(out2[l]), ref2)
+        say("layer", l, "rel err verify", e1, "commit", es, "verify after commit", e2)
+        assert e1 <= BF16_GATE and es <= BF16_GATE and e2 <= BF16_GATE
+    assert not torch.equal(S[L - 1], S0_47)
