@@ -214,15 +214,15 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     constexpr size_t ues = kUh ? 2 : 4;   // bytes per pseudo-value
     const void *u_head = static_cast<const char *>(u_prev) + prow0 * ues;
     const uint32_t ubytes = (uint32_t)((size_t)n_prev * H * kD * ues);
-    f32x16 U0 = {};
-    if (mlen > 0 && mlen <= kMaxPathIds) {
-        if constexpr (kU)
-            U0 = pc::load_u_chunk<kUh>(u_head, ubytes, sm.pid, 0, min(32, mlen), H * kD, c.col,
-                                       c.h);
-        else   // the first chunk's values, in this wave's columns
-            U0 = pc::load_v_chunk16(v_prev + prow0, pbytes, sm.pid, 0, min(pc::kC16, mlen),
-                                    H * kD, c.col, c.h);
-    }
+    // (unconditional: with no valid slots every load reads past the end of
+    // its buffer resource and returns zero, so no merge of loaded and zero
+    // values forces a wait for these loads here)
+    const int mc0 = (mlen > 0 && mlen <= kMaxPathIds) ? min(kU ? 32 : pc::kC16, mlen) : 0;
+    pc::ChunkWords U0;
+    if constexpr (kU)
+        U0 = pc::load_u_chunk<kUh>(u_head, ubytes, sm.pid, 0, mc0, H * kD, c.col, c.h);
+    else   // the first chunk's values, in this wave's columns
+        U0 = pc::load_v_chunk16(v_prev + prow0, pbytes, sm.pid, 0, mc0, H * kD, c.col, c.h);
 
     // ---- 2. the new tree's Gram, masks and block inverses (no state needed)
     f32x16 gc, ga;
@@ -266,13 +266,14 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             inverse_subst(c, sm.b.s);
             inverse_zl(c, sm.b.s);
         }
-        if (commit) pc::apply_known_u(sm.b.kt.kc, sm.cx, U0, st, ident, c.m, c.h);
+        if (commit)
+            pc::apply_known_u(sm.b.kt.kc, sm.cx, pc::u_values<kUh>(U0), st, ident, c.m, c.h);
         if (tree_ok) inverse_split(c, sm.b.s);   // starts with a barrier: the chunk is read
         lds_barrier();                           // the inverse scratch is free from here on
         if (kLong && commit) {
             for (int c0 = 32; c0 < mlen; c0 += 32) {
                 const int mc = min(32, mlen - c0);
-                const f32x16 Uc =
+                const pc::ChunkWords Uc =
                     pc::load_u_chunk<kUh>(u_head, ubytes, sm.pid, c0, mc, H * kD, c.col, c.h);
                 if (c.w == 3) {
                     const int rj = c.l >> 1;
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
                     pc::build_keys32(sm.b.kc, sm.cx, kr, mc, c.l);
                 }
                 lds_barrier();
-                pc::apply_known_u(sm.b.kc, sm.cx, Uc, st, ident, c.m, c.h);
+                pc::apply_known_u(sm.b.kc, sm.cx, pc::u_values<kUh>(Uc), st, ident, c.m, c.h);
                 lds_barrier();   // every wave is done with this chunk
             }
         }
@@ -313,7 +314,17 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
         } else {
             lds_barrier();
         }
-        if (commit) pc::apply16_early(sm.b.kt16.ch, sm.cx, U0, st, ident, c.m, c.h);
+        if (commit) {
+            // R = K_p S over the four tiles in two accumulators (two short
+            // MFMA chains), then U = T RHS and the update
+            const pc::ChunkView cv = pc::early_view(sm.b.kt16.ch, sm.cx, c.m);
+            f32x16 Ra = {}, Rb = {};
+            pc::rp_tile(cv.kp_row, st[0], 0, Ra, c.h);
+            pc::rp_tile(cv.kp_row, st[1], 1, Rb, c.h);
+            pc::rp_tile(cv.kp_row, st[2], 2, Ra, c.h);
+            pc::rp_tile(cv.kp_row, st[3], 3, Rb, c.h);
+            pc::finish_rows_v<pc::kC16>(cv, pc::widen_bf16(U0), Ra + Rb, st, ident, c.h);
+        }
         if (tree_ok) inverse_split(c, sm.b.s);   // starts with a barrier: the chunk is read
         lds_barrier();                           // the inverse scratch is free from here on
         if (kLong && commit) {

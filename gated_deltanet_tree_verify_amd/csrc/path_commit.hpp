@@ -371,34 +371,34 @@ __device__ __forceinline__ void apply_update(const ChunkView &cv, const f32x16 &
     }
 }
 
-// Apply a prepared chunk of NR (16 or 32) path slots to this wave's state
-// slab, the chunk's values given in registers: vv[r] = v of path slot
-// crow(r, h) in this lane's column, zero past the chunk (no barrier inside).
-// NA (1 or 2) accumulators for R: two halve its MFMA chain at the cost of
-// 16 registers.
-template <int NR, int NA = 1>
-__device__ __forceinline__ void apply_rows_v(const ChunkView &cv, const f32x16 &vv,
-                                             f32x16 (&st)[4], const bf16x8 (&ident)[2], int h) {
-    constexpr int KS = NR / 16;   // k-steps over path slots that can be nonzero
-    // ---- R = K_p S: B operands straight from the state tiles (with two
-    //      accumulators, even and odd state tiles apart)
-    f32x16 Rp[NA] = {};
+// One state tile's share of R = K_p S: tile q holds rows 32 q .. 32 q + 31
+// of this wave's slab (the B operand, split hi + lo); kp_row is row m of the
+// chunk's key tile (d_k permuted).  R accumulates, so the tiles may be taken
+// one at a time as they land.
+__device__ __forceinline__ void rp_tile(const uint16_t *kp_row, const f32x16 &stq, int q,
+                                        f32x16 &R, int h) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int kk = 0; kk < 2; ++kk) {
+        float sv[8];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float sv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sv[j] = st[q][8 * kk + j];
-            bf16x8 sh, sl;
-            split8(sv, sh, sl);
-            const bf16x8 a = lds8(cv.kp_row + 32 * q + 16 * kk + 8 * h);
-            Rp[q % NA] = mfma(a, sh, Rp[q % NA]);
-            Rp[q % NA] = mfma(a, sl, Rp[q % NA]);
-        }
-    f32x16 R = Rp[0];
-    if constexpr (NA == 2) R += Rp[1];
+        for (int j = 0; j < 8; ++j) sv[j] = stq[8 * kk + j];
+        bf16x8 sh, sl;
+        split8(sv, sh, sl);
+        const bf16x8 a = lds8(kp_row + 32 * q + 16 * kk + 8 * h);
+        R = mfma(a, sh, R);
+        R = mfma(a, sl, R);
+    }
+}
 
+// The rest of a chunk's application once R = K_p S is complete: the
+// right-hand side beta (v - e^g R), U = T RHS, and the update of the slab.
+// vv[r] = v of path slot crow(r, h) in this lane's column, zero past the
+// chunk (no barrier inside).
+template <int NR>
+__device__ __forceinline__ void finish_rows_v(const ChunkView &cv, const f32x16 &vv,
+                                              const f32x16 &R, f32x16 (&st)[4],
+                                              const bf16x8 (&ident)[2], int h) {
+    constexpr int KS = NR / 16;   // k-steps over path slots that can be nonzero
     // ---- right-hand side and U = T RHS, scaled by the decay to the chunk end
     f32x16 rhs;
 #pragma unroll
@@ -421,6 +421,17 @@ __device__ __forceinline__ void apply_rows_v(const ChunkView &cv, const f32x16 &
         U = mfma(al, bhh, U);
     }
     apply_update<NR>(cv, U, st, ident, h);
+}
+
+// Apply a prepared chunk of NR (16 or 32) path slots to this wave's state
+// slab, the chunk's values given in registers (as for finish_rows_v).
+template <int NR>
+__device__ __forceinline__ void apply_rows_v(const ChunkView &cv, const f32x16 &vv,
+                                             f32x16 (&st)[4], const bf16x8 (&ident)[2], int h) {
+    f32x16 R = {};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rp_tile(cv.kp_row, st[q], q, R, h);
+    finish_rows_v<NR>(cv, vv, R, st, ident, h);
 }
 
 // the same with the chunk's values read from the LDS value tile
@@ -661,35 +672,66 @@ __device__ __forceinline__ KeyRows16 load_keys16(int row_id, bool row_live, int 
     return r;
 }
 
+// Raw words of a chunk's per-slot values in this lane's column, one per
+// result-tile register r (slot crow(r, h)): fp32 bit patterns, or 16-bit
+// patterns zero-extended.  They are widened where they are used, not where
+// they are loaded: a conversion next to the load would make the wave wait
+// for that load, and for every load issued before it, at that point.
+struct ChunkWords {
+    uint32_t x[16];
+};
+
+__device__ __forceinline__ f32x16 widen_bf16(const ChunkWords &w) {
+    f32x16 v;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = __uint_as_float(w.x[r] << 16);
+    return v;
+}
+
+__device__ __forceinline__ f32x16 widen_f16(const ChunkWords &w) {
+    f32x16 v;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        v[r] = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)w.x[r]));
+    return v;
+}
+
+__device__ __forceinline__ f32x16 as_f32(const ChunkWords &w) {
+    f32x16 v;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = __uint_as_float(w.x[r]);
+    return v;
+}
+
 // this lane's values of the first 16 slots crow(r, h), r < 8, of the chunk
-// at path slot c0, widened from bf16 (zero past the chunk): v_head points at
-// node 0 of this (sequence, head) of a [batch][n][H][128] bf16 tensor,
-// rs = H * 128, bytes = n * rs * 2
-__device__ __forceinline__ f32x16 load_v_chunk16(const uint16_t *v_head, uint32_t bytes,
-                                                 const int *pid, int c0, int mc, int rs, int col,
-                                                 int h) {
+// at path slot c0, as raw bf16 words (zero past the chunk and in r >= 8):
+// v_head points at node 0 of this (sequence, head) of a [batch][n][H][128]
+// bf16 tensor, rs = H * 128, bytes = n * rs * 2
+__device__ __forceinline__ ChunkWords load_v_chunk16(const uint16_t *v_head, uint32_t bytes,
+                                                     const int *pid, int c0, int mc, int rs,
+                                                     int col, int h) {
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_head, bytes);
-    f32x16 V = {};
+    ChunkWords w;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.x[r] = 0;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int j = crow(r, h);
         const uint32_t off =
             j < mc ? (uint32_t)(pid[min(c0 + j, kMaxPath - 1)] * rs + col) * 2 : bytes;
-        const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(vr, (int)off, 0, kNT);
-        V[r] = __uint_as_float((uint32_t)x << 16);
+        w.x[r] = __builtin_amdgcn_raw_buffer_load_b16(vr, (int)off, 0, kNT);
     }
-    return V;
+    return w;
 }
 
-__device__ __forceinline__ void apply16_early(const EarlyChunk16 &ch, const Chunk16Aux &ax,
-                                              const f32x16 &vv, f32x16 (&st)[4],
-                                              const bf16x8 (&ident)[2], int m, int h) {
+// what the application of the early chunk reads (lane row m)
+__device__ __forceinline__ ChunkView early_view(const EarlyChunk16 &ch, const Chunk16Aux &ax,
+                                                int m) {
     const bool live = m < kC16;
-    const ChunkView cv{live ? ch.kp[m] : ax.zk, live ? ch.th[m] : ax.zt, live ? ch.tl[m] : ax.zt,
-                       nullptr,                0,
-                       ax.eg,                  ax.wdec,
-                       ax.beta,                ax.glast};
-    apply_rows_v<kC16, 2>(cv, vv, st, ident, h);
+    return ChunkView{live ? ch.kp[m] : ax.zk, live ? ch.th[m] : ax.zt, live ? ch.tl[m] : ax.zt,
+                     nullptr,                0,
+                     ax.eg,                  ax.wdec,
+                     ax.beta,                ax.glast};
 }
 
 // ---- commit from known pseudo-values (u_s written by the verify that ran on
@@ -740,29 +782,34 @@ __device__ __forceinline__ void build_keys32(KeyChunk32 &kc, Chunk16Aux &ax, con
     if (l == 0) ax.glast = exp2f(gl);
 }
 
-// this lane's u entries of the chunk's slots crow(r, h) (zero past the chunk):
-// u_head points at node 0 of this (sequence, head) of a [batch][n][H][128]
-// tensor of fp32 (or, with kHalf, fp16) values, rs = H * 128, bytes = n * rs
-// times the element size
+// this lane's u entries of the chunk's slots crow(r, h) (zero past the chunk),
+// as raw words: u_head points at node 0 of this (sequence, head) of a
+// [batch][n][H][128] tensor of fp32 (or, with kHalf, fp16) values,
+// rs = H * 128, bytes = n * rs times the element size
 template <bool kHalf>
-__device__ __forceinline__ f32x16 load_u_chunk(const void *u_head, uint32_t bytes, const int *pid,
-                                               int c0, int mc, int rs, int col, int h) {
+__device__ __forceinline__ ChunkWords load_u_chunk(const void *u_head, uint32_t bytes,
+                                                   const int *pid, int c0, int mc, int rs,
+                                                   int col, int h) {
     const __amdgpu_buffer_rsrc_t ur = make_rsrc(u_head, bytes);
     constexpr uint32_t es = kHalf ? 2 : 4;
-    f32x16 U;
+    ChunkWords w;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int j = crow(r, h);
         const uint32_t off =
             j < mc ? (uint32_t)(pid[min(c0 + j, kMaxPath - 1)] * rs + col) * es : bytes;
-        if constexpr (kHalf) {
-            const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(ur, (int)off, 0, kNT);
-            U[r] = static_cast<float>(__builtin_bit_cast(_Float16, x));
-        } else {
-            U[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ur, (int)off, 0, kNT));
-        }
+        if constexpr (kHalf)
+            w.x[r] = __builtin_amdgcn_raw_buffer_load_b16(ur, (int)off, 0, kNT);
+        else
+            w.x[r] = __builtin_amdgcn_raw_buffer_load_b32(ur, (int)off, 0, kNT);
     }
-    return U;
+    return w;
+}
+
+template <bool kHalf>
+__device__ __forceinline__ f32x16 u_values(const ChunkWords &w) {
+    if constexpr (kHalf) return widen_f16(w);
+    else return as_f32(w);
 }
 
 __device__ __forceinline__ void apply_known_u(const KeyChunk32 &kc, const Chunk16Aux &ax,
