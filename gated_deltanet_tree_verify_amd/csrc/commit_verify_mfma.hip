@@ -28,10 +28,12 @@
 //     substitutes the tree's blocks, and every wave holds its own columns of
 //     the chunk's value rows in registers; every wave applies it at the same
 //     point (R = K_p S, U = T RHS, then the update).
-// Longer paths continue chunk by chunk over the inverse scratch.  The verify
-// then finishes from the committed slab, writing the slab back tile by tile
-// as the contraction consumes it, and the solve's first 32-row block is
-// stored while the second is solved.
+// Longer paths continue chunk by chunk over the inverse scratch, after the
+// inverse's last step.  The verify then finishes from the committed slab,
+// writing the slab back tile by tile as the contraction consumes it (when
+// every path fits the first chunk, the inverse's last step waits until the
+// contraction is done: the contraction does not need T), and the solve's
+// first 32-row block is stored while the second is solved.
 //
 // The new tree's v rows are needed only by the solve, so they are requested
 // behind the state and wait in registers; once the contraction has read the
@@ -268,8 +270,12 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
         }
         if (commit)
             pc::apply_known_u(sm.b.kt.kc, sm.cx, pc::u_values<kUh>(U0), st, ident, c.m, c.h);
-        if (tree_ok) inverse_split(c, sm.b.s);   // starts with a barrier: the chunk is read
-        lds_barrier();                           // the inverse scratch is free from here on
+        if constexpr (kLong) {
+            // the later chunks need the inverse scratch: the inverse's last
+            // step first (it starts with a barrier: the first chunk is read)
+            if (tree_ok) inverse_split(c, sm.b.s);
+            lds_barrier();   // the inverse scratch is free from here on
+        }
         if (kLong && commit) {
             for (int c0 = 32; c0 < mlen; c0 += 32) {
                 const int mc = min(32, mlen - c0);
@@ -325,8 +331,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             pc::rp_tile(cv.kp_row, st[3], 3, Rb, c.h);
             pc::finish_rows_v<pc::kC16>(cv, pc::widen_bf16(U0), Ra + Rb, st, ident, c.h);
         }
-        if (tree_ok) inverse_split(c, sm.b.s);   // starts with a barrier: the chunk is read
-        lds_barrier();                           // the inverse scratch is free from here on
+        if constexpr (kLong) {
+            if (tree_ok) inverse_split(c, sm.b.s);   // starts with a barrier: the chunk is read
+            lds_barrier();                           // the inverse scratch is free from here on
+        }
         if (kLong && commit) {
             // later chunks: wave 3 loads and prepares each over the inverse
             // scratch, every wave applies it
@@ -365,6 +373,12 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     // stores issued there.  One explicit wait here settles it.
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     contract(c, sm.a.t, st, P, R, commit ? slab : nullptr);
+    // Without the later chunks, the inverse's last step (the T rows, over
+    // the first chunk) comes only now: the contraction needs the committed
+    // slab but not T, so no wave waits for that step's barriers before
+    // contracting.  It starts with a barrier (every wave has applied the
+    // chunk); the barrier after it publishes T and frees the K tile.
+    if constexpr (!kLong) inverse_split(c, sm.b.s);
     // the V tile through the K tile's place (free once every wave has
     // finished the contraction) into this lane's columns
     lds_barrier();
