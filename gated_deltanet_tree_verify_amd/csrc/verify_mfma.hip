@@ -72,15 +72,18 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     // ---- 3. X and Y blocks, 4. block inverses
     if (c.w < 3) mask(c, sm.tp, gc, ga, sm.b.s);
     lds_barrier();
-    inverse(c, sm.b.s);
+    inverse_subst(c, sm.b.s);
+    inverse_zl(c, sm.b.s);
 
-    // ---- 5. P = Q S0, R = K S0
+    // ---- 5. P = Q S0, R = K S0 (the contraction does not need T, so the
+    //         inverse's last step and its barrier come after it)
     if (!state_first) {
         load_state(st, slab, c.col, c.h);
         load_rows(c, s, v, rv);
     }
     f32x16 P[2], R[2];
     contract(c, sm.a.t, st, P, R);
+    inverse_split(c, sm.b.s);
     // the V tile through the K tile's place into this lane's columns (the
     // first block's staging rows lie in the Q tile's place)
     lds_barrier();
