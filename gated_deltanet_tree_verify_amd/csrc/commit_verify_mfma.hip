@@ -260,8 +260,9 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
         load_state_tile(st[3], 3, slab, c.col, c.h);
         // v is needed only by the solve: its rows are requested behind the
         // last state tile and wait in registers (the V tile passes through
-        // LDS after the contraction)
-        load_rows(c, s, v, rv);
+        // LDS after the contraction); with the later chunks they are
+        // requested after those, which need the registers
+        if constexpr (!kLong) load_rows(c, s, v, rv);
         lds_barrier();
         commit = sm.commit_ok && mlen > 0;
         if (tree_ok) {
@@ -309,8 +310,9 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
         load_state_tile(st[3], 3, slab, c.col, c.h);
         // v is needed only by the solve: its rows are requested behind the
         // last state tile and wait in registers (the V tile passes through
-        // LDS after the contraction)
-        load_rows(c, s, v, rv);
+        // LDS after the contraction); with the later chunks they are
+        // requested after those, which need the registers
+        if constexpr (!kLong) load_rows(c, s, v, rv);
         lds_barrier();
         commit = sm.commit_ok && mlen > 0;
         if (commit && c.w == 0) pc::build16_t(sm.b.kt16.ch, c.l);
@@ -354,6 +356,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
             }
         }
     }
+
+    if constexpr (kLong) load_rows(c, s, v, rv);
 
     // ---- 4. verify from the committed slab, writing the slab back as the
     //         contraction consumes it
