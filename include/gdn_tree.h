@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 7
+#define GDN_TREE_ABI_VERSION 8
 #define GDN_MAX_NODES 128
 #define GDN_MAX_DIM 128
 #define GDN_MAX_CANDIDATES 32   /* child candidates per node, gdn_tree_build */
