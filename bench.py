@@ -522,7 +522,11 @@ def main():
     if not args.no_compare:
         c_sets = []
         for ts in pick("t126", None):
-            d = upload(ts, ts.parent.shape[1])
+            d = upload(ts, 17)     # depth <= 16: paths of at most 17 nodes
+            # the same accepted paths cut to their first 16 nodes (a path to
+            # an ancestor of the accepted leaf), for the decode-step timing
+            d["path16"] = d["path"][:, :16].contiguous()
+            d["plen16"] = torch.clamp(d["plen"], max=16)
             d["leaves"] = sum(len(gs.leaves(p)) for p in ts.parent)
             d["steps"] = sum(branch_node_steps(p) for p in ts.parent)
             d["out"] = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
@@ -532,8 +536,20 @@ def main():
         bv126 = [g.branch_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
                                  d["S"], out=d["out"], stream=stream, prepare=True)
                  for d in c_sets]
+        # the decode step on these trees: set i's state advanced along set
+        # i - 1's accepted path, then set i's trees verified: one fused
+        # launch, or a commit launch and a verify launch
+        fs126 = [g.commit_verify(d["S"], c_sets[i - 1]["path16"], c_sets[i - 1]["plen16"],
+                                 own(c_sets[i - 1]), d["q"], d["k"], d["v"], d["alpha"],
+                                 d["beta"], d["parent"], out=d["out"], stream=stream, prepare=True)
+                 for i, d in enumerate(c_sets)]
+        cm126 = [g.commit(d["S"], c_sets[i - 1]["path16"], c_sets[i - 1]["plen16"],
+                          *own(c_sets[i - 1]),
+                          stream=stream, prepare=True) for i, d in enumerate(c_sets)]
         t_tree = regions(lambda i: tv126[i % 8](), 40, 8)[0] * 1e3
         t_branch = regions(lambda i: bv126[i % 8](), 10, 2, 3)[0] * 1e3
+        t_fs126 = regions(lambda i: fs126[i % 8](), 40, 8)[0] * 1e3
+        t_sep126 = regions(lambda i: (cm126[i % 8](), tv126[i % 8]()), 40, 8)[0] * 1e3
         w126 = gs.TREE126
         # what the branch baseline computes: per branch node and head,
         # w = S^T k (2 d^2 flops), the update alpha S + (beta k)(v - alpha w)^T
@@ -553,11 +569,14 @@ def main():
                   "tree_verify_nodes_per_s": w126.batch * w126.n / (t_tree * 1e-6),
                   "tree_verify_hbm_gbps": verify_bytes(w126.batch, w126.n, w126.H, w126.d_k,
                                                        w126.d_v) / (t_tree * 1e-6) / 1e9,
+                  "decode_step_paths16": {"one_launch_us": t_fs126,
+                                          "commit_then_verify_us": t_sep126},
                   "pages_speedup_b200": 7.1}
         log(f"n=126: tree verify {t_tree:.1f} us, branch verify {t_branch:.1f} us, "
             f"speedup {t_branch / t_tree:.2f} (branch at {cmp126['branch_tflop_per_s']:.1f} "
-            f"TFLOP/s; its fp32 floor {floor_us:.0f} us, {floor_us / t_tree:.2f}x the tree)")
-        c_sets = tv126 = bv126 = None
+            f"TFLOP/s; its fp32 floor {floor_us:.0f} us, {floor_us / t_tree:.2f}x the tree); "
+            f"decode step: fused {t_fs126:.1f} us, two launches {t_sep126:.1f} us")
+        c_sets = tv126 = bv126 = fs126 = cm126 = None
         torch.cuda.empty_cache()
 
         w3 = gs.WORKLOADS[3]
@@ -572,20 +591,43 @@ def main():
                        out=d["out"], stream=stream, prepare=True) for d in b_sets]
         cb = [g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"],
                        d["parent"], stream=stream, prepare=True) for d in b_sets]
+        # the fused step on this workload: set i's state advanced along set
+        # i - 1's accepted paths (the commit solving), then set i's trees
+        # verified, one launch
+        # (paths up to 128 nodes: the library takes a commit launch and a
+        # verify launch, unless the new pseudo-values are asked for, which
+        # makes it one launch: timed both ways)
+        for d in b_sets:
+            d["u"] = torch.empty_like(d["out"])
+        fb = [g.commit_verify(d["S"], b_sets[(i - 1) % 2]["path"], b_sets[(i - 1) % 2]["plen"],
+                              own(b_sets[(i - 1) % 2]), d["q"], d["k"], d["v"], d["alpha"],
+                              d["beta"], d["parent"], out=d["out"], stream=stream, prepare=True)
+              for i, d in enumerate(b_sets)]
+        fbu = [g.commit_verify(d["S"], b_sets[(i - 1) % 2]["path"], b_sets[(i - 1) % 2]["plen"],
+                               own(b_sets[(i - 1) % 2]), d["q"], d["k"], d["v"], d["alpha"],
+                               d["beta"], d["parent"], out=d["out"], u_out=d["u"],
+                               stream=stream, prepare=True)
+               for i, d in enumerate(b_sets)]
         t_vb = regions(lambda i: vb[i % 2](), 20, 2)[0] * 1e3
         t_cb = regions(lambda i: cb[i % 2](), 20, 2)[0] * 1e3
+        t_fb = regions(lambda i: fb[i % 2](), 20, 2)[0] * 1e3
+        t_fbu = regions(lambda i: fbu[i % 2](), 20, 2)[0] * 1e3
         vb_bytes = verify_bytes(w3.batch, w3.n, w3.H, w3.d_k, w3.d_v)
         cb_bytes = commit_bytes(w3.batch, w3.H, w3.d_k, w3.d_v,
                                 [float(np.mean([d["m"] for d in b_sets]))])
+        fb_bytes = vb_bytes + cb_bytes - w3.batch * w3.H * 4 * w3.d_k * w3.d_v
         b64 = {"workload": w3.name, "verify_us": t_vb, "commit_us": t_cb,
+               "commit_verify_us": t_fb, "commit_verify_one_launch_u_out_us": t_fbu,
+               "commit_verify_hbm_gbps": fb_bytes / (t_fb * 1e-6) / 1e9,
                "verify_nodes_per_s": w3.batch * w3.n / (t_vb * 1e-6),
                "verify_hbm_gbps": vb_bytes / (t_vb * 1e-6) / 1e9,
                "verify_frac": vb_bytes / (t_vb * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                "commit_hbm_gbps": cb_bytes / (t_cb * 1e-6) / 1e9,
                "verify_algorithmic_bytes": vb_bytes, "commit_algorithmic_bytes": cb_bytes}
         log(f"b64/n128: verify {t_vb:.1f} us ({b64['verify_hbm_gbps']:.0f} GB/s), commit "
-            f"{t_cb:.1f} us ({b64['commit_hbm_gbps']:.0f} GB/s)")
-        b_sets = vb = cb = None
+            f"{t_cb:.1f} us ({b64['commit_hbm_gbps']:.0f} GB/s), commit_verify {t_fb:.1f} us "
+            f"(one launch with u_out: {t_fbu:.1f} us)")
+        b_sets = vb = cb = fb = fbu = None
         torch.cuda.empty_cache()
 
     # ---- achievable-bandwidth line: a plain 1 GiB device copy

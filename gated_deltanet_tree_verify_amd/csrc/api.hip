@@ -134,6 +134,13 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
         u_dtype == GDN_DTYPE_F16};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::commit_verify_mfma_supports(a)) return from_hip(gdn::launch_commit_verify_mfma(a, s));
+    // 65..128 new nodes: one launch (the commit solving for its
+    // pseudo-values, u_prev not needed) when the new tree's pseudo-values are
+    // asked for or the paths fit one 16-slot chunk; longer paths go faster as
+    // a commit launch and a verify launch (that verify keeps one workgroup
+    // per CU, and the commit's chunk loop would lengthen its chain)
+    if (gdn::commit_verify_mfma128_supports(a) && (u_out || max_path <= 16))
+        return from_hip(gdn::launch_commit_verify_mfma128(a, s));
     if (u_out) return GDN_ERR_UNSUPPORTED;
     // other shapes: the two halves as separate launches on the same stream
     // (the commit solves for the pseudo-values itself, so u_prev is not

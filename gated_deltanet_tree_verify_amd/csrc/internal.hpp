@@ -59,6 +59,8 @@ bool commit_mfma_supports(const CommitArgs &a);
 hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s);
 bool commit_verify_mfma_supports(const CommitVerifyArgs &a);
 hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s);
+bool commit_verify_mfma128_supports(const CommitVerifyArgs &a);
+hipError_t launch_commit_verify_mfma128(const CommitVerifyArgs &a, hipStream_t s);
 hipError_t launch_path(const int32_t *parent, const int32_t *accepted,
                        int32_t *path, int32_t *path_len, int batch, int n,
                        int max_path, int32_t *status, hipStream_t s);

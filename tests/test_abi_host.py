@@ -108,7 +108,7 @@ def test_commit_verify_null_pointer(lib, null):
     (dict(n_prev=129), -2), (dict(n=129), -2), (dict(dk=12), -2), (dict(dv=256), -2),
     (dict(dtype=2), -1), (dict(ptr=MISALIGNED), -1), (dict(status=MISALIGNED), -1),
     (dict(u_prev=MISALIGNED), -1), (dict(u_out=MISALIGNED), -1),
-    (dict(u_out=FAKE), -2),        # pseudo-values out need the bf16, d = 128, n <= 64 kernel
+    (dict(u_out=FAKE), -2),        # pseudo-values out need bf16 q/k/v and d = 128
     (dict(u_out=FAKE, u_dtype=2), -2),
     (dict(u_out=FAKE, u_dtype=1), -1),   # pseudo-values are fp32 or fp16
     (dict(u_prev=FAKE, u_dtype=3), -1),

@@ -282,3 +282,108 @@ def test_stack48_layers_from_the_stacked_run(gpu_lib):
         say("layer", l, "rel err verify", e1, "commit", es, "verify after commit", e2)
         assert e1 <= BF16_GATE and es <= BF16_GATE and e2 <= BF16_GATE
     assert not torch.equal(S[L - 1], S0_47)
+
+
+# ---------------------------------------------------------------------------
+# fused commit + verify for 65..128-node trees: one launch
+# ---------------------------------------------------------------------------
+def prev_set_n128(max_path):
+    """previous trees of 128 nodes (chain, star, 16-ary bush, random of depth
+    <= 16) and accepted nodes whose paths fit max_path"""
+    rng = np.random.default_rng(128)
+    par = np.stack([gs.chain_tree(128), gs.star_tree(128), gs.kary_bfs_tree(128, 16),
+                    gs.random_recursive_tree(rng, 128, max_depth=16)])
+    d3 = gs._depths(par[3])
+    acc = np.array([min(127, max_path - 1), 5, 127,
+                    int(np.argmax(np.where(d3 < max_path, d3, -1)))], np.int32)
+    return par, acc
+
+
+@pytest.mark.parametrize("n", [128, 65])
+@pytest.mark.parametrize("max_path", [16, 128])
+@pytest.mark.parametrize("udt", [None, torch.float32, torch.float16])
+def test_commit_verify_n128_one_launch(gpu_lib, n, max_path, udt):
+    """the previous trees' accepted paths committed (the solving commit; a
+    128-node path on the chain when max_path allows it) and 65..128-node
+    trees verified in one launch, with and without the new pseudo-values:
+    state, outputs and pseudo-values against the oracle, whole tensors"""
+    say("commit-verify n128", n, max_path, udt)
+    pa, acc = prev_set_n128(max_path)
+    rng = np.random.default_rng(n + max_path)
+    pb = np.stack([gs.star_tree(n), gs.chain_tree(n), gs.random_recursive_tree(rng, n, 16),
+                   gs.kary_bfs_tree(n, 8)])
+    A = gs.make_set(pa, 3, 128, 128, "bf16", seed=130 + max_path, accepted=acc)
+    B = gs.make_set(pb, 3, 128, 128, "bf16", seed=131 + n)
+    dA, dB = upload(A), upload(B)
+    path, plen = A.paths(max_path=max_path)
+    assert plen.max() <= max_path and (max_path < 128 or plen[0] == 128)
+    S = dA["S0"].clone()
+    u = None if udt is None else torch.empty(dB["v"].shape, dtype=udt, device="cuda")
+    st = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    out = gpu_lib.commit_verify(S, dev(path), dev(plen),
+                                (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"]),
+                                dB["q"], dB["k"], dB["v"], dB["alpha"], dB["beta"], dB["parent"],
+                                u_out=u, status=st)
+    torch.cuda.synchronize()
+    Sref, cst = oracle.commit_set(A, path_arr=path, path_len=plen)
+    oref, vst = oracle.verify(B.q, B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert host(st).tolist() == (cst | vst).tolist() == [0] * 4
+    es, eo = oracle.rel_err(host(S), Sref), oracle.rel_err(host(out), oref)
+    say("rel err S", es, "out", eo)
+    assert es <= BF16_GATE and eo <= BF16_GATE
+    for b in range(4):
+        assert oracle.rel_err(host(S)[b], Sref[b]) <= BF16_GATE, b
+        assert oracle.rel_err(host(out)[b], oref[b]) <= BF16_GATE, b
+    if u is not None:
+        UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+        eu = oracle.rel_err(host(u), UB)
+        say("u rel err", eu)
+        assert eu <= BF16_GATE
+        if udt == torch.float16:
+            u32 = torch.empty(dB["v"].shape, dtype=torch.float32, device="cuda")
+            S2 = dA["S0"].clone()
+            gpu_lib.commit_verify(S2, dev(path), dev(plen),
+                                  (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"]),
+                                  dB["q"], dB["k"], dB["v"], dB["alpha"], dB["beta"],
+                                  dB["parent"], u_out=u32)
+            torch.cuda.synchronize()
+            assert torch.equal(u.view(torch.int16), u32.half().view(torch.int16))
+
+
+@pytest.mark.parametrize("max_path", [16, 128])
+def test_commit_verify_n128_faults(gpu_lib, max_path):
+    """sequence 0 clean, 1 a path with an id out of range (state bit-unchanged),
+    2 a malformed new tree (NaN outputs and pseudo-values; its commit still
+    applies), 3 both, 4 an empty path"""
+    rng = np.random.default_rng(77 + max_path)
+    pa = np.stack([gs.random_recursive_tree(rng, 128, max_depth=14) for _ in range(5)])
+    pb = np.stack([gs.random_recursive_tree(rng, 96, max_depth=14) for _ in range(5)])
+    acc = np.array([gs.pick_leaf(rng, pa[i]) for i in range(5)], np.int32)
+    A = gs.make_set(pa, 2, 128, 128, "bf16", seed=91, accepted=acc)
+    B = gs.make_set(pb, 2, 128, 128, "bf16", seed=92)
+    path, plen = A.paths(max_path=max_path)
+    path[1, plen[1] - 1] = 128
+    path[3, 0] = 300
+    plen[4] = 0
+    B.parent[2, 95] = 95
+    B.parent[3, 0] = -4
+    dA, dB = upload(A), upload(B)
+    S = dA["S0"].clone()
+    u = torch.empty(dB["v"].shape, dtype=torch.float32, device="cuda")
+    st = torch.full((5,), -7, dtype=torch.int32, device="cuda")
+    out = gpu_lib.commit_verify(S, dev(path), dev(plen),
+                                (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"]),
+                                dB["q"], dB["k"], dB["v"], dB["alpha"], dB["beta"], dB["parent"],
+                                u_out=u, status=st)
+    torch.cuda.synchronize()
+    Sref, cst = oracle.commit_set(A, path_arr=path, path_len=plen)
+    oref, vst = oracle.verify(B.q, B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert host(st).tolist() == (cst | vst).tolist() == [0, 2, 1, 3, 0]
+    Sh, oh, uh = host(S), host(out), host(u)
+    for b in (1, 3, 4):
+        assert np.array_equal(Sh[b], A.S0[b]), b
+    for b in (0, 2):
+        assert oracle.rel_err(Sh[b], Sref[b]) <= BF16_GATE, b
+    assert np.isnan(oh[2:4]).all() and np.isnan(uh[2:4]).all()
+    for b in (0, 1, 4):
+        assert oracle.rel_err(oh[b], oref[b]) <= BF16_GATE, b
