@@ -47,32 +47,50 @@ struct Topo {
     int bad;
 };
 
-// wave 3, two nodes per lane (l and 64 + l): parent validation, ancestor
+// parent and gates of nodes l and 64 + l (one wave; dead nodes neutral)
+struct Gates2 {
+    int par[2];
+    float a[2], bt[2];
+    bool live[2];
+};
+
+__device__ __forceinline__ Gates2 load_gates2(const Lane &c, const Seq &s, const int32_t *parent,
+                                              const float *alpha, const float *beta) {
+    Gates2 g;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = 64 * u + c.l;
+        g.live[u] = i < s.n;
+        g.par[u] = -1;
+        g.a[u] = 1.f;
+        g.bt[u] = 0.f;
+        if (g.live[u]) {
+            const size_t row = ((size_t)s.b * s.n + i) * s.H + s.hd;
+            g.par[u] = parent[(size_t)s.b * s.n + i];
+            g.a[u] = alpha[row];
+            g.bt[u] = beta[row];
+        }
+    }
+    return g;
+}
+
+// one wave, two nodes per lane (l and 64 + l): parent validation, ancestor
 // bitmasks and log2 decay prefix by pointer jumping (7 rounds cover 128).
 // status[b] gets the fault flag (ORed into what is there when status_or).
-__device__ __forceinline__ void topology(const Lane &c, const Seq &s, const int32_t *parent,
-                                         const float *alpha, const float *beta, Topo &tp,
+__device__ __forceinline__ void topology(const Lane &c, const Seq &s, const Gates2 &gt, Topo &tp,
                                          int32_t *status, bool write_status, bool status_or) {
-    int par[2], jmp[2];
+    int jmp[2];
     float gs[2], bt[2];
     bool live[2], badi[2];
     unsigned long long a0[2], a1[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = 64 * u + c.l;
-        live[u] = i < s.n;
-        par[u] = -1;
-        float a = 1.f;
-        bt[u] = 0.f;
-        if (live[u]) {
-            const size_t row = ((size_t)s.b * s.n + i) * s.H + s.hd;
-            par[u] = parent[(size_t)s.b * s.n + i];
-            a = alpha[row];
-            bt[u] = beta[row];
-        }
-        badi[u] = live[u] && !parent_ok(par[u], i);
-        jmp[u] = (live[u] && !badi[u]) ? par[u] : -1;
-        gs[u] = live[u] ? log2f(a) : 0.f;
+        live[u] = gt.live[u];
+        bt[u] = gt.bt[u];
+        badi[u] = live[u] && !parent_ok(gt.par[u], i);
+        jmp[u] = (live[u] && !badi[u]) ? gt.par[u] : -1;
+        gs[u] = live[u] ? log2f(gt.a[u]) : 0.f;
         a0[u] = (live[u] && u == 0) ? (1ull << c.l) : 0ull;
         a1[u] = (live[u] && u == 1) ? (1ull << c.l) : 0ull;
     }
@@ -128,6 +146,12 @@ __device__ __forceinline__ void topology(const Lane &c, const Seq &s, const int3
         if (write_status && status)
             status[s.b] = (status_or ? status[s.b] : 0) | (bad ? kFaultBadParent : 0);
     }
+}
+
+__device__ __forceinline__ void topology(const Lane &c, const Seq &s, const int32_t *parent,
+                                         const float *alpha, const float *beta, Topo &tp,
+                                         int32_t *status, bool write_status, bool status_or) {
+    topology(c, s, load_gates2(c, s, parent, alpha, beta), tp, status, write_status, status_or);
 }
 
 // 128 node rows of a bf16 [batch][n][H][128] tensor: eight 16-byte chunks
@@ -314,10 +338,11 @@ __device__ __forceinline__ void contract_tile(const Lane &c, const QKTiles &t, i
     }
 }
 
-// right-hand side beta (v - e^g R) and e^g P for rows 64 hf + 32 t + crow
+// right-hand side beta (v - e^g R) and e^g P for rows 64 hf + 32 t + crow;
+// vh[t] holds the v values of rows 64 hf + 32 t + crow as bf16 pairs
 __device__ __forceinline__ void rhs_and_decay(const Lane &c, const Topo &tp, int hf,
                                               f32x16 (&P)[2], const f32x16 (&R)[2],
-                                              const uint32_t (&vpk)[4][8], f32x16 (&rhs)[2]) {
+                                              const uint32_t (*vh)[8], f32x16 (&rhs)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -329,12 +354,18 @@ __device__ __forceinline__ void rhs_and_decay(const Lane &c, const Topo &tp, int
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * q4 + e;
-                const uint32_t pr = vpk[2 * hf + t][r >> 1];
+                const uint32_t pr = vh[t][r >> 1];
                 const float vval = __uint_as_float((r & 1) ? (pr & 0xffff0000u) : (pr << 16));
                 rhs[t][r] = bb[e] * (vval - ee[e] * R[t][r]);
                 P[t][r] *= ee[e];
             }
         }
+}
+
+__device__ __forceinline__ void rhs_and_decay(const Lane &c, const Topo &tp, int hf,
+                                              f32x16 (&P)[2], const f32x16 (&R)[2],
+                                              const uint32_t (&vpk)[4][8], f32x16 (&rhs)[2]) {
+    rhs_and_decay(c, tp, hf, P, R, &vpk[2 * hf], rhs);
 }
 
 // the 64-node solve on prepared right-hand sides and decayed P:
