@@ -62,7 +62,6 @@ gdn_status gdn_tree_verify(const void *q, const void *k, const void *v, gdn_dtyp
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::verify_mfma_supports(a)) return from_hip(gdn::launch_verify_mfma(a, s));
     if (gdn::verify_mfma128h_supports(a)) return from_hip(gdn::launch_verify_mfma128h(a, s));
-    if (gdn::verify_mfma128_supports(a)) return from_hip(gdn::launch_verify_mfma128(a, s));
     return from_hip(gdn::launch_verify_generic(a, s));
 }
 
@@ -135,12 +134,9 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
         u_dtype == GDN_DTYPE_F16};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::commit_verify_mfma_supports(a)) return from_hip(gdn::launch_commit_verify_mfma(a, s));
-    // 65..128 new nodes: one launch (the commit solving for its
-    // pseudo-values, u_prev not needed) when the new tree's pseudo-values are
-    // asked for or the paths fit one 16-slot chunk; longer paths go faster as
-    // a commit launch and a verify launch (that verify keeps one workgroup
-    // per CU, and the commit's chunk loop would lengthen its chain)
-    if (gdn::commit_verify_mfma128_supports(a) && (u_out || max_path <= 16))
+    // 65..128 new nodes: one launch, the commit solving for its
+    // pseudo-values (u_prev not needed)
+    if (gdn::commit_verify_mfma128_supports(a))
         return from_hip(gdn::launch_commit_verify_mfma128(a, s));
     if (u_out) return GDN_ERR_UNSUPPORTED;
     // other shapes: the two halves as separate launches on the same stream
@@ -150,7 +146,6 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
                                                         : gdn::launch_commit(a.c, s);
     if (e != hipSuccess) return GDN_ERR_HIP;
     if (gdn::verify_mfma128h_supports(a.v)) return from_hip(gdn::launch_verify_mfma128h(a.v, s));
-    if (gdn::verify_mfma128_supports(a.v)) return from_hip(gdn::launch_verify_mfma128(a.v, s));
     return from_hip(gdn::launch_verify_generic(a.v, s));
 }
 

@@ -8,8 +8,10 @@
 //              O_01 = e^g P_01 + Y_{01,01} U_01
 //     half 1:  U_23 = (I + X_{23,23})^{-1} (RHS_23 - X_{23,01} U_01),
 //              O_23 = e^g P_23 + Y_{23,01} U_01 + Y_{23,23} U_23
-// Each half reuses the 64-node solve blocks (tv::SolveBlocks, tv::inverse);
-// the four cross blocks X_{23,01}, Y_{23,01} have their own LDS.
+// Each half reuses the 64-node solve blocks (tv::SolveBlocks, tv::inverse).
+// This file holds the pieces: the 128-node topology, the masked Gram blocks,
+// a half's right-hand side and solve; the schedule (which rows are in LDS
+// when, and the cross blocks X_{23,01}, Y_{23,01}) is in tree_verify128h.hpp.
 #pragma once
 
 #include "tree_verify.hpp"
@@ -20,18 +22,11 @@ namespace tv128 {
 using namespace tile;
 using tv::kBL;
 using tv::kD;
-using tv::kQK;
-using tv::kThreads;
 using tv::Lane;
 using tv::Seq;
 using tv::SolveBlocks;
 
 constexpr int kN = 128;
-
-struct QKTiles {
-    uint16_t q[kN][kQK];   // d_k index permuted within 16-blocks
-    uint16_t k[kN][kQK];
-};
 
 // cross blocks (row block 2 + a, key block b), a, b in {0, 1}
 struct Cross {
@@ -148,90 +143,6 @@ __device__ __forceinline__ void topology(const Lane &c, const Seq &s, const Gate
     }
 }
 
-__device__ __forceinline__ void topology(const Lane &c, const Seq &s, const int32_t *parent,
-                                         const float *alpha, const float *beta, Topo &tp,
-                                         int32_t *status, bool write_status, bool status_or) {
-    topology(c, s, load_gates2(c, s, parent, alpha, beta), tp, status, write_status, status_or);
-}
-
-// 128 node rows of a bf16 [batch][n][H][128] tensor: eight 16-byte chunks
-// per thread; rows past n read as zero (past the end of the resource)
-__device__ __forceinline__ void load_rows(const Lane &c, const Seq &s, const uint16_t *src,
-                                          uint4 (&x)[8]) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + s.base, (uint32_t)(s.n * s.rstride * 2));
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
-        x[it] = load16(rs, (uint32_t)((row * s.rstride + c8) * 2));
-    }
-}
-
-__device__ __forceinline__ void store_rows_permuted(const Lane &c, const uint4 (&x)[8],
-                                                    uint16_t (*dst)[kQK]) {
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
-        store_row8_permuted(dst[row], c8, x[it]);
-    }
-}
-
-// the same rows loaded by waves 0-2 alone (192 threads, e = tid + 192 it,
-// eleven chunks per thread, the last round partly empty)
-__device__ __forceinline__ void load_rows3(const Lane &c, const Seq &s, const uint16_t *src,
-                                           uint4 (&x)[11]) {
-    const uint32_t bytes = (uint32_t)(s.n * s.rstride * 2);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + s.base, bytes);
-#pragma unroll
-    for (int it = 0; it < 11; ++it) {
-        const int e = c.tid + 192 * it, row = e >> 4, c8 = (e & 15) * 8;
-        x[it] = load16(rs, e < kN * 16 ? (uint32_t)((row * s.rstride + c8) * 2) : bytes);
-    }
-}
-
-__device__ __forceinline__ void store_rows3_permuted(const Lane &c, const uint4 (&x)[11],
-                                                     uint16_t (*dst)[kQK]) {
-#pragma unroll
-    for (int it = 0; it < 11; ++it) {
-        const int e = c.tid + 192 * it, row = e >> 4, c8 = (e & 15) * 8;
-        if (e < kN * 16) store_row8_permuted(dst[row], c8, x[it]);
-    }
-}
-
-__device__ __forceinline__ void store_rows(const Lane &c, const uint4 (&x)[8],
-                                           uint16_t (*dst)[kQK]) {
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
-        *reinterpret_cast<uint4 *>(&dst[row][c8]) = x[it];
-    }
-}
-
-// V values of this lane's four result tiles, as bf16 pairs
-__device__ __forceinline__ void v_to_regs(const Lane &c, const uint16_t (*v)[kQK],
-                                          uint32_t (&vpk)[4][8]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2)
-            vpk[t][r / 2] = (uint32_t)v[32 * t + crow(r, c.h)][c.col] |
-                            ((uint32_t)v[32 * t + crow(r + 1, c.h)][c.col] << 16);
-}
-
-// Gram block (row block a, key block b), transposed: lane (node 32 a + m, h)
-// holds k_s.q_i and k_s.k_i for s = 32 b + crow(r, h)
-__device__ __forceinline__ void gram(const Lane &c, const QKTiles &t, int a, int b, f32x16 &gc,
-                                     f32x16 &ga) {
-    gc = f32x16{};
-    ga = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ks = lds8(&t.k[32 * b + c.m][16 * kk + 8 * c.h]);
-        const bf16x8 qi = lds8(&t.q[32 * a + c.m][16 * kk + 8 * c.h]);
-        const bf16x8 ki = lds8(&t.k[32 * a + c.m][16 * kk + 8 * c.h]);
-        gc = mfma(ks, qi, gc);
-        ga = mfma(ks, ki, ga);
-    }
-}
 
 // ancestor mask and decay weights on a Gram block: y = Y entries, x = X
 // entries (not yet negated; the diagonal of X is never read)
@@ -266,17 +177,9 @@ __device__ __forceinline__ void store_split(const Lane &c, const float (&v)[16],
     }
 }
 
-// the three blocks of half hf (row / key blocks 2 hf, 2 hf + 1), wave w < 3
-// taking block (0,0), (1,0), (1,1): masked Gram values into registers, then
-// into the 64-node solve blocks
-__device__ __forceinline__ void half_values(const Lane &c, const QKTiles &t, const Topo &tp,
-                                            int hf, float (&y)[16], float (&x)[16]) {
-    const int la = c.w == 0 ? 0 : 1, lb = c.w == 2 ? 1 : 0;
-    f32x16 gc, ga;
-    gram(c, t, 2 * hf + la, 2 * hf + lb, gc, ga);
-    mask(c, tp, 2 * hf + la, 2 * hf + lb, gc, ga, y, x);
-}
-
+// wave w < 3's masked block of a half ((0,0), (1,0) or (1,1)) into the
+// 64-node solve blocks: Y into yh / yl [w]; X as -X_10 (hi / lo, wave 1) or
+// as the fp32 diagonal block that the inverse reads (waves 0 and 2)
 __device__ __forceinline__ void half_store(const Lane &c, float (&y)[16], float (&x)[16],
                                            SolveBlocks &sb) {
     const int la = c.w == 0 ? 0 : 1;
@@ -290,51 +193,6 @@ __device__ __forceinline__ void half_store(const Lane &c, float (&y)[16], float 
         for (int q4 = 0; q4 < 4; ++q4)
             *reinterpret_cast<float4 *>(&sb.d[la][c.m][8 * q4 + 4 * c.h]) =
                 make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
-    }
-}
-
-// cross block (2 + a, b) for wave w = 2 a + b
-__device__ __forceinline__ void cross_block(const Lane &c, const QKTiles &t, const Topo &tp,
-                                            Cross &cr) {
-    const int a = c.w >> 1, b = c.w & 1;
-    f32x16 gc, ga;
-    gram(c, t, 2 + a, b, gc, ga);
-    float y[16], x[16];
-    mask(c, tp, 2 + a, b, gc, ga, y, x);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = -x[r];
-    store_split(c, y, cr.yh[a][b], cr.yl[a][b]);
-    store_split(c, x, cr.xh[a][b], cr.xl[a][b]);
-}
-
-// state tile q's share of P = Q S0 and R = K S0 for this wave's columns over
-// both halves (rows 64 hf + 32 tt + crow), the state split into bf16 hi + lo;
-// the caller takes q = 0, 1, 2, 3 in turn, each as its tile lands
-__device__ __forceinline__ void contract_tile(const Lane &c, const QKTiles &t, int q,
-                                              const f32x16 &sq, f32x16 (&P0)[2],
-                                              f32x16 (&R0)[2], f32x16 (&P1)[2],
-                                              f32x16 (&R1)[2]) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        float sv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] = sq[8 * kk + j];
-        bf16x8 sh, sl;
-        split8(sv, sh, sl);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f32x16 &p = hf ? P1[tt] : P0[tt];
-                f32x16 &r = hf ? R1[tt] : R0[tt];
-                const int row = 64 * hf + 32 * tt + c.m;
-                const bf16x8 aq = lds8(&t.q[row][32 * q + 16 * kk + 8 * c.h]);
-                const bf16x8 ak = lds8(&t.k[row][32 * q + 16 * kk + 8 * c.h]);
-                p = mfma(aq, sh, p);
-                p = mfma(aq, sl, p);
-                r = mfma(ak, sh, r);
-                r = mfma(ak, sl, r);
-            }
     }
 }
 
@@ -362,12 +220,6 @@ __device__ __forceinline__ void rhs_and_decay(const Lane &c, const Topo &tp, int
         }
 }
 
-__device__ __forceinline__ void rhs_and_decay(const Lane &c, const Topo &tp, int hf,
-                                              f32x16 (&P)[2], const f32x16 (&R)[2],
-                                              const uint32_t (&vpk)[4][8], f32x16 (&rhs)[2]) {
-    rhs_and_decay(c, tp, hf, P, R, &vpk[2 * hf], rhs);
-}
-
 // the 64-node solve on prepared right-hand sides and decayed P:
 // u0 = T_0 rhs0, u1 = T_1 (rhs1 - X_10 u0), o = P + Y u
 __device__ __forceinline__ void solve_half(const Lane &c, const SolveBlocks &sb,
@@ -381,29 +233,6 @@ __device__ __forceinline__ void solve_half(const Lane &c, const SolveBlocks &sb,
     o[0] = mm3<kBL>(sb.yh[0], sb.yl[0], u0s, P[0], c.m, c.h);
     o[1] = mm3<kBL>(sb.yh[1], sb.yl[1], u0s, P[1], c.m, c.h);
     o[1] = mm3<kBL>(sb.yh[2], sb.yl[2], split_tile(u[1]), o[1], c.m, c.h);
-}
-
-// output rows 64 hf .. 64 hf + 63 (rows < n): this wave's result tiles into
-// the LDS staging rows (row stride kD + 4 floats), then whole rows as 16-byte
-// chunks, eight per thread (four times fewer store instructions than the
-// tiles' own 4-byte entries); a barrier of the caller must separate the
-// staging area's previous readers from this call
-__device__ __forceinline__ void store_out_staged(const Lane &c, const Seq &s, int hf,
-                                                 const f32x16 (&o)[2], float (*stage)[kD + 4],
-                                                 float *out) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) stage[32 * t + crow(r, c.h)][c.col] = o[t][r];
-    tv::lds_barrier();
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int e = c.tid + kThreads * it, row = e >> 5, c4 = (e & 31) * 4;
-        const int i = 64 * hf + row;
-        if (i < s.n)
-            store16(out + s.base + (size_t)i * s.rstride + c4,
-                    *reinterpret_cast<const float4 *>(&stage[row][c4]));
-    }
 }
 
 __device__ __forceinline__ void store_nan(const Lane &c, const Seq &s, float *out) {

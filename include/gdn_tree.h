@@ -165,10 +165,8 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path,
  * |k_s| |u_s|^T elementwise (plus rounding).  u_out needs bf16 and
  * d_k = d_v = 128 (else GDN_ERR_UNSUPPORTED).  u_prev is used when n <= 64.
  * For 64 < n <= 128 the commit solves for the pseudo-values itself and
- * u_prev is ignored; the call is one launch when u_out is given or
- * max_path <= 16, else a commit launch then a verify launch (faster for
- * long paths), with the same results.  Other shapes (fp32 q/k/v, d != 128)
- * also take a commit launch then a verify launch and ignore u_prev.
+ * u_prev is ignored (one launch).  Other shapes (fp32 q/k/v, d != 128) take
+ * a commit launch then a verify launch and ignore u_prev.
  *
  * out and u_out must not alias any input, S must not alias any other
  * argument; the previous-tree tensors may be the same tensors as the new
