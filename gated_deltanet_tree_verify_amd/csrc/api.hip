@@ -61,7 +61,7 @@ gdn_status gdn_tree_verify(const void *q, const void *k, const void *v, gdn_dtyp
                       batch, n, H, d_k, d_v, status};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::verify_mfma_supports(a)) return from_hip(gdn::launch_verify_mfma(a, s));
-    if (gdn::verify_mfma128h_supports(a)) return from_hip(gdn::launch_verify_mfma128h(a, s));
+    if (gdn::verify_mfma128_supports(a)) return from_hip(gdn::launch_verify_mfma128(a, s));
     return from_hip(gdn::launch_verify_generic(a, s));
 }
 
@@ -145,7 +145,7 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
     const hipError_t e = gdn::commit_mfma_supports(a.c) ? gdn::launch_commit_mfma(a.c, s)
                                                         : gdn::launch_commit(a.c, s);
     if (e != hipSuccess) return GDN_ERR_HIP;
-    if (gdn::verify_mfma128h_supports(a.v)) return from_hip(gdn::launch_verify_mfma128h(a.v, s));
+    if (gdn::verify_mfma128_supports(a.v)) return from_hip(gdn::launch_verify_mfma128(a.v, s));
     return from_hip(gdn::launch_verify_generic(a.v, s));
 }
 

@@ -52,8 +52,8 @@ hipError_t launch_verify_generic(const VerifyArgs &a, hipStream_t s);
 hipError_t launch_branch_verify(const VerifyArgs &a, hipStream_t s);
 bool verify_mfma_supports(const VerifyArgs &a);
 hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s);
-bool verify_mfma128h_supports(const VerifyArgs &a);
-hipError_t launch_verify_mfma128h(const VerifyArgs &a, hipStream_t s);
+bool verify_mfma128_supports(const VerifyArgs &a);
+hipError_t launch_verify_mfma128(const VerifyArgs &a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
 bool commit_mfma_supports(const CommitArgs &a);
 hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s);

@@ -46,13 +46,13 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n128_halves_kernel(
 
 }  // namespace
 
-bool verify_mfma128h_supports(const VerifyArgs &a) {
+bool verify_mfma128_supports(const VerifyArgs &a) {
     // byte extents of a head's rows must fit the 32-bit buffer ranges
     return a.dtype == GDN_DTYPE_BF16 && a.dk == kD && a.dv == kD && a.n > 64 &&
            a.n <= tv128::kN && a.H <= 4096;
 }
 
-hipError_t launch_verify_mfma128h(const VerifyArgs &a, hipStream_t s) {
+hipError_t launch_verify_mfma128(const VerifyArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(verify_mfma_n128_halves_kernel, dim3((unsigned)(a.batch * a.H)),
                        dim3(kThreads), 0, s, (const uint16_t *)a.q, (const uint16_t *)a.k,
                        (const uint16_t *)a.v, a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H,
