@@ -132,6 +132,26 @@ __device__ __forceinline__ void load_v_direct(const Lane &c, const Seq &s, const
         }
 }
 
+// state tile q's share of P = Q S and R = K S for this wave's columns over
+// the tiles' 64 rows, the tile given already split into bf16 hi + lo
+// (split_tile): the products and their order are tv::contract_tile's, so
+// the sums are the same bit for bit; the split is done once for both halves
+__device__ __forceinline__ void contract_split_tile(const Lane &c, const tv::QKTiles &t,
+                                                    const SplitTile &sq, int q, f32x16 (&P)[2],
+                                                    f32x16 (&R)[2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const bf16x8 aq = lds8(&t.q[32 * tt + c.m][32 * q + 16 * kk + 8 * c.h]);
+            const bf16x8 ak = lds8(&t.k[32 * tt + c.m][32 * q + 16 * kk + 8 * c.h]);
+            P[tt] = mfma(aq, sq.hi[kk], P[tt]);
+            P[tt] = mfma(aq, sq.lo[kk], P[tt]);
+            R[tt] = mfma(ak, sq.hi[kk], R[tt]);
+            R[tt] = mfma(ak, sq.lo[kk], R[tt]);
+        }
+}
+
 // one half's output rows (and, with kUout, its pseudo-value rows, fp32 or
 // with kUh fp16 rounded to nearest) as whole rows: the result tiles into the
 // LDS staging rows (outputs over the Q / K tiles, pseudo-values over the
@@ -213,7 +233,7 @@ __device__ __forceinline__ void verify_halves(const Lane &c, const Seq &s, Smem 
     // waves 0-2 take the blocks (0,0), (1,0), (1,1) of a half
     const int la = c.w == 0 ? 0 : 1, lb = c.w == 2 ? 1 : 0;
 
-    // ---- half 0: blocks, inverse, P_01 / R_01 (the slab stays), solve
+    // ---- half 0: blocks, inverse, P_01 / R_01 (the slab kept, split), solve
     if (c.w < 3) {
         f32x16 gc, ga;
         gram_tiles(c, sm.a.t, la, lb, gc, ga);
@@ -226,8 +246,13 @@ __device__ __forceinline__ void verify_halves(const Lane &c, const Seq &s, Smem 
     lds_barrier();
     tv::inverse_subst(c, sm.b.s);
     tv::inverse_zl(c, sm.b.s);
-    f32x16 P[2], R[2];
-    tv::contract(c, sm.a.t, st, P, R);
+    f32x16 P[2] = {}, R[2] = {};
+    SplitTile ss[4];   // the slab as bf16 hi + lo, kept for half 1
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        ss[q] = split_tile(st[q]);
+        contract_split_tile(c, sm.a.t, ss[q], q, P, R);
+    }
     tv::inverse_split(c, sm.b.s);   // starts with a barrier: the tiles are read
     tv::store_rows(c, rv, sm.a.t.k);   // the V rows over the K tile
     lds_barrier();
@@ -252,9 +277,11 @@ __device__ __forceinline__ void verify_halves(const Lane &c, const Seq &s, Smem 
     tv::store_rows_permuted(c1, rk, sm.a.t.k);
     lds_barrier();
 
-    // ---- P_23 / R_23 (the slab's last use), then the cross blocks: wave
+    // ---- P_23 / R_23 (the split slab's last use), then the cross blocks: wave
     //      w = 2 a + b forms (2 + a, b) from key fragments of rows 32 b..
-    tv::contract(c1, sm.a.t, st, P, R);
+    P[0] = P[1] = R[0] = R[1] = f32x16{};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) contract_split_tile(c1, sm.a.t, ss[q], q, P, R);
     load_v_direct(c1, s1, v, vpk);
     bf16x8 kf[8];
     load_key_frags(c1, s, k, c1.w & 1, kf);
