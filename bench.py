@@ -68,7 +68,6 @@ HEADLINE_STEP = "solving"
 # fp32 accumulation; everything else is fp32
 KERNEL_DTYPE = "bf16"
 TRAFFIC_FILES = {
-    "carried": os.path.join(ROOT, "profiles", "commit_verify_b16_n64_h32_d128_traffic.txt"),
     "solving": os.path.join(ROOT, "profiles",
                             "commit_verify_solving_b16_n64_h32_d128_traffic.txt"),
 }
@@ -536,6 +535,7 @@ def main():
             # an ancestor of the accepted leaf), for the decode-step timing
             d["path16"] = d["path"][:, :16].contiguous()
             d["plen16"] = torch.clamp(d["plen"], max=16)
+            d["m16"] = float(np.sum(np.minimum(d["plen_host"], 16)))
             d["leaves"] = sum(len(gs.leaves(p)) for p in ts.parent)
             d["steps"] = sum(branch_node_steps(p) for p in ts.parent)
             d["out"] = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
@@ -578,8 +578,13 @@ def main():
                   "tree_verify_nodes_per_s": w126.batch * w126.n / (t_tree * 1e-6),
                   "tree_verify_hbm_gbps": verify_bytes(w126.batch, w126.n, w126.H, w126.d_k,
                                                        w126.d_v) / (t_tree * 1e-6) / 1e9,
-                  "decode_step_paths16": {"one_launch_us": t_fs126,
-                                          "commit_then_verify_us": t_sep126},
+                  "tree_verify_algorithmic_bytes": verify_bytes(w126.batch, w126.n, w126.H,
+                                                                w126.d_k, w126.d_v),
+                  "decode_step_paths16": {
+                      "one_launch_us": t_fs126, "commit_then_verify_us": t_sep126,
+                      "algorithmic_bytes": fused_bytes(
+                          w126.batch, w126.n, w126.H, w126.d_k, w126.d_v,
+                          [float(np.mean([d["m16"] for d in c_sets]))])},
                   "pages_speedup_b200": 7.1}
         log(f"n=126: tree verify {t_tree:.1f} us, branch verify {t_branch:.1f} us, "
             f"speedup {t_branch / t_tree:.2f} (branch at {cmp126['branch_tflop_per_s']:.1f} "
@@ -602,10 +607,8 @@ def main():
                        d["parent"], stream=stream, prepare=True) for d in b_sets]
         # the fused step on this workload: set i's state advanced along set
         # i - 1's accepted paths (the commit solving), then set i's trees
-        # verified, one launch
-        # (paths up to 128 nodes: the library takes a commit launch and a
-        # verify launch, unless the new pseudo-values are asked for, which
-        # makes it one launch: timed both ways)
+        # verified in one launch, without and with the new pseudo-values
+        # out; and the same as a commit launch then a verify launch
         for d in b_sets:
             d["u"] = torch.empty_like(d["out"])
         fb = [g.commit_verify(d["S"], b_sets[(i - 1) % 2]["path"], b_sets[(i - 1) % 2]["plen"],
@@ -617,26 +620,34 @@ def main():
                                d["beta"], d["parent"], out=d["out"], u_out=d["u"],
                                stream=stream, prepare=True)
                for i, d in enumerate(b_sets)]
+        cbp = [g.commit(d["S"], b_sets[(i - 1) % 2]["path"], b_sets[(i - 1) % 2]["plen"],
+                        *own(b_sets[(i - 1) % 2]), stream=stream, prepare=True)
+               for i, d in enumerate(b_sets)]
         t_vb = regions(lambda i: vb[i % 2](), 20, 2)[0] * 1e3
         t_cb = regions(lambda i: cb[i % 2](), 20, 2)[0] * 1e3
         t_fb = regions(lambda i: fb[i % 2](), 20, 2)[0] * 1e3
         t_fbu = regions(lambda i: fbu[i % 2](), 20, 2)[0] * 1e3
+        t_sep = regions(lambda i: (cbp[i % 2](), vb[i % 2]()), 20, 2)[0] * 1e3
         vb_bytes = verify_bytes(w3.batch, w3.n, w3.H, w3.d_k, w3.d_v)
         cb_bytes = commit_bytes(w3.batch, w3.H, w3.d_k, w3.d_v,
                                 [float(np.mean([d["m"] for d in b_sets]))])
         fb_bytes = vb_bytes + cb_bytes - w3.batch * w3.H * 4 * w3.d_k * w3.d_v
         b64 = {"workload": w3.name, "verify_us": t_vb, "commit_us": t_cb,
-               "commit_verify_us": t_fb, "commit_verify_one_launch_u_out_us": t_fbu,
+               "commit_verify_us": t_fb, "commit_verify_u_out_us": t_fbu,
+               "commit_then_verify_us": t_sep,
                "commit_verify_hbm_gbps": fb_bytes / (t_fb * 1e-6) / 1e9,
+               "commit_verify_frac": fb_bytes / (t_fb * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                "verify_nodes_per_s": w3.batch * w3.n / (t_vb * 1e-6),
                "verify_hbm_gbps": vb_bytes / (t_vb * 1e-6) / 1e9,
                "verify_frac": vb_bytes / (t_vb * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                "commit_hbm_gbps": cb_bytes / (t_cb * 1e-6) / 1e9,
-               "verify_algorithmic_bytes": vb_bytes, "commit_algorithmic_bytes": cb_bytes}
-        log(f"b64/n128: verify {t_vb:.1f} us ({b64['verify_hbm_gbps']:.0f} GB/s), commit "
-            f"{t_cb:.1f} us ({b64['commit_hbm_gbps']:.0f} GB/s), commit_verify {t_fb:.1f} us "
-            f"(one launch with u_out: {t_fbu:.1f} us)")
-        b_sets = vb = cb = fb = fbu = None
+               "verify_algorithmic_bytes": vb_bytes, "commit_algorithmic_bytes": cb_bytes,
+               "commit_verify_algorithmic_bytes": fb_bytes}
+        log(f"b64/n128: verify {t_vb:.1f} us ({b64['verify_hbm_gbps']:.0f} GB/s, "
+            f"{b64['verify_frac']:.3f}), commit {t_cb:.1f} us ({b64['commit_hbm_gbps']:.0f} GB/s), "
+            f"commit_verify {t_fb:.1f} us ({b64['commit_verify_frac']:.3f}; with u_out "
+            f"{t_fbu:.1f} us; as two launches {t_sep:.1f} us)")
+        b_sets = vb = cb = cbp = fb = fbu = None
         torch.cuda.empty_cache()
 
     # ---- achievable-bandwidth line: a plain 1 GiB device copy
