@@ -224,6 +224,38 @@ def test_verify_layer_b64_n128_full(gpu_lib):
     assert es <= BF16_GATE
 
 
+def test_commit_verify_b64_n128_full(gpu_lib):
+    """the batch-64, 128-node workload as one fused step (two workgroups per
+    CU, 2048 of them: the commit of set 0's accepted branches, then set 1's
+    trees verified from the committed state, with the new pseudo-values
+    out): whole state, output and pseudo-value tensors against the oracle"""
+    say("commit-verify b64 n128 full")
+    A, B = gs.make_config(3, s=0), gs.make_config(3, s=1)
+    dA, dB = upload(A), upload(B)
+    path, plen = A.paths(max_path=128)
+    S = dA["S0"].clone()
+    u = torch.empty(dB["v"].shape, dtype=torch.float32, device="cuda")
+    st = torch.full((64,), -7, dtype=torch.int32, device="cuda")
+    out = gpu_lib.commit_verify(S, dev(path), dev(plen),
+                                (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"]),
+                                dB["q"], dB["k"], dB["v"], dB["alpha"], dB["beta"], dB["parent"],
+                                u_out=u, status=st)
+    torch.cuda.synchronize()
+    Sref, cst = oracle.commit_set(A, path_arr=path, path_len=plen)
+    oref, vst = oracle.verify(B.q, B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert host(st).tolist() == (cst | vst).tolist() == [0] * 64
+    es, eo = oracle.rel_err(host(S), Sref), oracle.rel_err(host(out), oref)
+    say("rel err S", es, "out", eo)
+    assert es <= BF16_GATE and eo <= BF16_GATE
+    for b in range(64):
+        assert oracle.rel_err(host(S)[b], Sref[b]) <= BF16_GATE, b
+        assert oracle.rel_err(host(out)[b], oref[b]) <= BF16_GATE, b
+    UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    eu = oracle.rel_err(host(u), UB)
+    say("u rel err", eu)
+    assert eu <= BF16_GATE
+
+
 def test_stack48_layers_from_the_stacked_run(gpu_lib):
     """the 48-layer stack (batch 32, 32 heads, one 64-node tree per sequence
     shared by all layers): per-layer tensors stacked in one allocation each,
