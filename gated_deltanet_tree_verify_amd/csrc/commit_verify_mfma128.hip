@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma128_kernel(
     load_state(st, slab, c.col, c.h);
     uint4 rq[4], rk[4];
     tv::load_rows(c, s, q, rq);
-    tv::load_rows(c, s, k, rk);
+    tv::load_rows<0>(c, s, k, rk);   // cached: rows 0..63 of K are read again for the cross blocks
     if (c.w == 3) {
         pl.par0 = pc::parent_of(pl.id0, pp0, pp1, n_prev);
         pl.par1 = pc::parent_of(pl.id1, pp0, pp1, n_prev);

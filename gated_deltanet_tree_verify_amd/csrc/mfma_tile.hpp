@@ -154,8 +154,9 @@ constexpr int kNT = 2;
 // 11:8 left at their maxima)
 constexpr int kVmcntZero = 0x0F70;
 
+template <int kAux = kNT>
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNT));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAux));
 }
 
 // 16-byte store of 8 fp16 values (raw bits), non-temporal

@@ -143,13 +143,15 @@ __device__ __forceinline__ void topology(const Lane &c, const Seq &s, const Gate
 // 64 node rows of one (sequence, head) of a bf16 [batch][n][H][128] tensor:
 // four 16-byte chunks per thread; rows past n lie past the end of the buffer
 // resource and read as zero
+// (kAux: the cache policy, non-temporal unless a caller reads the rows again)
+template <int kAux = kNT>
 __device__ __forceinline__ void load_rows(const Lane &c, const Seq &s, const uint16_t *src,
                                           uint4 (&x)[4]) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + s.base, (uint32_t)(s.n * s.rstride * 2));
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int e = c.tid + kThreads * it, row = e >> 4, c8 = (e & 15) * 8;
-        x[it] = load16(rs, (uint32_t)((row * s.rstride + c8) * 2));
+        x[it] = load16<kAux>(rs, (uint32_t)((row * s.rstride + c8) * 2));
     }
 }
 

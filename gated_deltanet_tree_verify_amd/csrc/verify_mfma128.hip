@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n128_halves_kernel(
     if (c.w == 3) gt = tv128::load_gates2(c, s, parent, alpha, beta);
     uint4 rq[4], rk[4];
     tv::load_rows(c, s, q, rq);
-    tv::load_rows(c, s, k, rk);
+    tv::load_rows<0>(c, s, k, rk);   // cached: rows 0..63 of K are read again for the cross blocks
     if (c.w == 3) tv128::topology(c, s, gt, sm.tp, status, s.hd == 0, status_or);
     tv::store_rows_permuted(c, rq, sm.a.t.q);
     tv::store_rows_permuted(c, rk, sm.a.t.k);
