@@ -92,6 +92,9 @@ struct Node {
     int j, jn;
 };
 
+// KB: a compile-time bound on K (8, 16 or 32), so that the per-row sort
+// unrolls to it with no per-slot branch
+template <int KB>
 __global__ __launch_bounds__(64) void tree_build_kernel(
     const float *__restrict__ cand_logp, const int32_t *__restrict__ cand_tok,
     const int32_t *__restrict__ root_tok, int32_t *__restrict__ parent_out,
@@ -100,12 +103,20 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
     __shared__ float s_lp[kMaxN][kMaxK + 2];          // sorted log-probs of each row, -inf padded
     __shared__ unsigned char s_j[kMaxN][kMaxK + 2];   // their original slots
     __shared__ float s_raw[kMaxN * kMaxK];            // the table as read
+    __shared__ int32_t s_tok[kMaxN * kMaxK];          // the token ids, for the outputs
+    __shared__ unsigned long long s_pop[kMaxN];       // the current round's popped words
     const int b = blockIdx.x, l = threadIdx.x;
     const float *lp = cand_logp + (size_t)b * n * K;
+    const int32_t *tk = cand_tok + (size_t)b * n * K;
 
-    // ---- stage the table in LDS (coalesced), then sort every row: the rank
-    //      of slot j is the number of slots that come before it
-    for (int e = l; e < n * K; e += 64) s_raw[e] = lp[e];
+    // ---- stage the table and the token ids in LDS (coalesced; the token
+    //      ids are needed only for the outputs, so their loads run under the
+    //      whole build), then sort every row: the rank of slot j is the
+    //      number of slots that come before it
+    for (int e = l; e < n * K; e += 64) {
+        s_raw[e] = lp[e];
+        s_tok[e] = tk[e];
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -121,19 +132,22 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
     for (int u = 0; u < 2; ++u) {
         const int i = 64 * u + l;
         const bool row = i < n;
-        unsigned long long w[kMaxK];
+        // every slot read at once, from an index clamped into the table (no
+        // branch between the reads, so one wait covers them all); slots past
+        // K get the word 0, below every slot's word, so they never count
+        float v[KB];
+        unsigned long long w[KB];
 #pragma unroll
-        for (int t = 0; t < kMaxK; ++t)
-            w[t] = (t < K && row) ? sort_word(s_raw[i * K + t], t) : 0ull;
-        for (int j = 0; j < K; ++j) {
-            const float vj = row ? s_raw[i * K + j] : 0.f;
-            const unsigned long long wj = sort_word(vj, j);
+        for (int t = 0; t < KB; ++t) v[t] = s_raw[min(i * K + t, kMaxN * kMaxK - 1)];
+#pragma unroll
+        for (int t = 0; t < KB; ++t) w[t] = (t < K && row) ? sort_word(v[t], t) : 0ull;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
             int rank = 0;
 #pragma unroll
-            for (int t = 0; t < kMaxK; ++t)
-                if (t < K) rank += w[t] > wj ? 1 : 0;   // K is uniform
-            if (row) {
-                s_lp[i][rank] = isfinite(vj) ? vj : -INFINITY;
+            for (int t = 0; t < KB; ++t) rank += w[t] > w[j] ? 1 : 0;
+            if (j < K && row) {
+                s_lp[i][rank] = isfinite(v[j]) ? v[j] : -INFINITY;
                 s_j[i][rank] = (unsigned char)j;
             }
         }
@@ -194,22 +208,10 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
         for (; popped < cnt; ++popped) {
             const unsigned long long best = wave_max_2level(c0 > c1 ? c0 : c1);
             if (best == 0ull) break;   // nothing left this round
-            const int key = 8191 - (int)(((uint32_t)best >> 8) & 0xffffffu);
-            const int pnode = key >> 6, pslot = key & 63;
-            const int pdep = (int)(best & 0xffu);
-            const int id = nn + popped;
-            // the new node's lane records it (live only from the next round)
-            if ((id & 63) == l) {
-                auto record = [&](Node &d) {
-                    d.par = pnode;
-                    d.slot = pslot;
-                    d.sc = unpack_score(best);
-                    d.dep = pdep + 1;
-                };
-                // id is uniform: a branch, not an indexed register array
-                if (id < 64) record(nd[0]);
-                else record(nd[1]);
-            }
+            const int pnode = (8191 - (int)(((uint32_t)best >> 8) & 0xffffffu)) >> 6;
+            // the new node (live only from the next round) is recorded by
+            // its lane after the round, from this word
+            if (l == 0) s_pop[popped] = best;
             // the parent's lane advances its head (u is uniform)
             if ((pnode & 63) == l) {
                 if (pnode < 64) {
@@ -221,11 +223,23 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
                 }
             }
         }
-        // the round's nodes become live
+        // the round's nodes: each lane records its own from the popped
+        // words, and they become live
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int i = 64 * u + l;
-            if (i >= nn && i < nn + popped) make_live(u);
+            if (i >= nn && i < nn + popped) {
+                const unsigned long long wd = s_pop[i - nn];
+                const int key = 8191 - (int)(((uint32_t)wd >> 8) & 0xffffffu);
+                nd[u].par = key >> 6;
+                nd[u].slot = key & 63;
+                nd[u].sc = unpack_score(wd);
+                nd[u].dep = (int)(wd & 0xffu) + 1;
+                make_live(u);
+            }
         }
         c0 = cand(0);
         c1 = cand(1);
@@ -246,7 +260,7 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
             score_out[row0] = 0.f;
         } else if (i < nn) {
             parent_out[row0 + i] = nd[u].par;
-            token_out[row0 + i] = cand_tok[((size_t)b * n + nd[u].par) * K + nd[u].slot];
+            token_out[row0 + i] = s_tok[nd[u].par * K + nd[u].slot];
             score_out[row0 + i] = nd[u].sc;
         } else {
             parent_out[row0 + i] = -1;
@@ -263,8 +277,18 @@ hipError_t launch_tree_build(const float *cand_logp, const int32_t *cand_tok,
                              const int32_t *root_tok, int32_t *parent, int32_t *token,
                              float *score, int32_t *n_built, int batch, int n, int K, int width,
                              int max_depth, hipStream_t s) {
-    hipLaunchKernelGGL(tree_build_kernel, dim3((unsigned)batch), dim3(64), 0, s, cand_logp,
-                       cand_tok, root_tok, parent, token, score, n_built, n, K, width, max_depth);
+    if (K <= 8)
+        hipLaunchKernelGGL(tree_build_kernel<8>, dim3((unsigned)batch), dim3(64), 0, s, cand_logp,
+                           cand_tok, root_tok, parent, token, score, n_built, n, K, width,
+                           max_depth);
+    else if (K <= 16)
+        hipLaunchKernelGGL(tree_build_kernel<16>, dim3((unsigned)batch), dim3(64), 0, s,
+                           cand_logp, cand_tok, root_tok, parent, token, score, n_built, n, K,
+                           width, max_depth);
+    else
+        hipLaunchKernelGGL(tree_build_kernel<kMaxK>, dim3((unsigned)batch), dim3(64), 0, s,
+                           cand_logp, cand_tok, root_tok, parent, token, score, n_built, n, K,
+                           width, max_depth);
     return hipGetLastError();
 }
 
