@@ -119,8 +119,10 @@ __device__ __forceinline__ void store_rows3_permuted(const Lane &c, const uint4 
 // later chunks are applied too; without it a longer path is never read
 // (the host takes the kLong instance whenever max_path exceeds the first
 // chunk), and the kernel carries no code and no registers for them.  kUh:
-// u_prev and u_out hold fp16 values (fp32 otherwise).
-template <bool kU, bool kUout, bool kLong, bool kUh>
+// u_prev and u_out hold fp16 values (fp32 otherwise).  kOne: the new
+// trees have at most 32 nodes, so only the first 32-row block is contracted
+// and solved.
+template <bool kU, bool kUout, bool kLong, bool kUh, bool kOne>
 __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     float *__restrict__ S, const int32_t *__restrict__ path, const int32_t *__restrict__ path_len,
     int max_path, const uint16_t *__restrict__ k_prev, const uint16_t *__restrict__ v_prev,
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     // on the memory counter inside the contraction, i.e. for the slab
     // stores issued there.  One explicit wait here settles it.
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    contract(c, sm.a.t, st, P, R, commit ? slab : nullptr);
+    contract<kOne ? 1 : 2>(c, sm.a.t, st, P, R, commit ? slab : nullptr);
     // Without the later chunks, the inverse's last step (the T rows, over
     // the first chunk) comes only now: the contraction needs the committed
     // slab but not T, so no wave waits for that step's barriers before
@@ -398,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_verify_mfma_kernel(
     f32x16 u0, o0, u1, o1;
     solve_block0(c, sm.tp, sm.b.s, P, R, vpk, u0, o0, cy);
     store_block<kUout, kUh>(c, s, sm.a.o, o0, out, u0, u_out, 0);
+    if constexpr (kOne) return;
     solve_block1(c, sm.b.s, P, cy, u1, o1);
     lds_barrier();   // every thread has read the first block from the staging area
     store_block<kUout, kUh>(c, s, sm.a.o, o1, out, u1, u_out, 32);
@@ -413,9 +416,9 @@ bool commit_verify_mfma_supports(const CommitVerifyArgs &a) {
 
 namespace {
 
-template <bool kU, bool kUout, bool kLong, bool kUh>
-hipError_t launch_cv(const CommitVerifyArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((commit_verify_mfma_kernel<kU, kUout, kLong, kUh>),
+template <bool kU, bool kUout, bool kLong, bool kUh, bool kOne>
+hipError_t launch_cv1(const CommitVerifyArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((commit_verify_mfma_kernel<kU, kUout, kLong, kUh, kOne>),
                        dim3((unsigned)(a.v.batch * a.v.H)), dim3(kThreads), 0, s, a.c.S,
                        a.c.path, a.c.path_len, a.c.max_path, (const uint16_t *)a.c.k,
                        (const uint16_t *)a.c.v, a.c.alpha, a.c.beta, a.c.parent, a.u_prev,
@@ -423,6 +426,12 @@ hipError_t launch_cv(const CommitVerifyArgs &a, hipStream_t s) {
                        (const uint16_t *)a.v.v, a.v.alpha, a.v.beta, a.v.parent, a.v.out,
                        a.u_out, a.v.n, a.v.H, device_cu_count(), a.v.status);
     return hipGetLastError();
+}
+
+template <bool kU, bool kUout, bool kLong, bool kUh>
+hipError_t launch_cv(const CommitVerifyArgs &a, hipStream_t s) {
+    if (a.v.n <= 32) return launch_cv1<kU, kUout, kLong, kUh, true>(a, s);
+    return launch_cv1<kU, kUout, kLong, kUh, false>(a, s);
 }
 
 template <bool kU, bool kUout, bool kLong>

@@ -383,7 +383,10 @@ __device__ __forceinline__ void inverse_split(const Lane &c, SolveBlocks &sb) {
 // columns: tile q holds rows 32 q .. 32 q + 31 of S0, i.e. contraction
 // indices 32 q .. 32 q + 31; it enters as the B operand, split hi/lo.  P and
 // R accumulate, so the tiles may be taken one at a time as they arrive;
-// taken in order 0..3 the sums are the same as contract()'s.
+// taken in order 0..3 the sums are the same as contract()'s.  NT: the
+// number of 32-row node blocks formed (1 when the tree has at most 32 nodes:
+// the second block's rows are all zero).
+template <int NT = 2>
 __device__ __forceinline__ void contract_tile(const Lane &c, const QKTiles &t, const f32x16 &stq,
                                               int q, f32x16 (&P)[2], f32x16 (&R)[2]) {
 #pragma unroll
@@ -394,7 +397,7 @@ __device__ __forceinline__ void contract_tile(const Lane &c, const QKTiles &t, c
         bf16x8 sh, sl;
         split8(sv, sh, sl);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < NT; ++tt) {
             const bf16x8 aq = lds8(&t.q[32 * tt + c.m][32 * q + 16 * kk + 8 * c.h]);
             const bf16x8 ak = lds8(&t.k[32 * tt + c.m][32 * q + 16 * kk + 8 * c.h]);
             P[tt] = mfma(aq, sh, P[tt]);
@@ -406,14 +409,15 @@ __device__ __forceinline__ void contract_tile(const Lane &c, const QKTiles &t, c
 }
 
 // P = Q S0 and R = K S0 for this wave's 32 columns from the whole slab
-// (four result tiles of S0 rows)
+// (four result tiles of S0 rows); NT as for contract_tile
+template <int NT = 2>
 __device__ __forceinline__ void contract(const Lane &c, const QKTiles &t, const f32x16 (&st)[4],
                                          f32x16 (&P)[2], f32x16 (&R)[2],
                                          float *store_slab = nullptr) {
     P[0] = P[1] = R[0] = R[1] = f32x16{};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        contract_tile(c, t, st[q], q, P, R);
+        contract_tile<NT>(c, t, st[q], q, P, R);
         // optionally write the state tile back as soon as it has been read,
         // spreading the slab's stores over the contraction
         if (store_slab) store_state_tile(st[q], q, store_slab, c.col, c.h);

@@ -32,6 +32,9 @@ struct Smem {
     Topo tp;
 };
 
+// kOne: the trees have at most 32 nodes, so only the first 32-row block is
+// contracted and solved (the host picks the instance)
+template <bool kOne>
 __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ beta,
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
         load_rows(c, s, v, rv);
     }
     f32x16 P[2], R[2];
-    contract(c, sm.a.t, st, P, R);
+    contract<kOne ? 1 : 2>(c, sm.a.t, st, P, R);
     inverse_split(c, sm.b.s);
     // the V tile through the K tile's place into this lane's columns (the
     // first block's staging rows lie in the Q tile's place)
@@ -98,6 +101,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_mfma_n64_kernel(
     f32x16 u0, o0, u1, o1;
     solve_block0(c, sm.tp, sm.b.s, P, R, vpk, u0, o0, cy);
     store_block<false>(c, s, sm.a.o, o0, out, u0, nullptr, 0);
+    if constexpr (kOne) return;
     solve_block1(c, sm.b.s, P, cy, u1, o1);
     lds_barrier();   // every thread has read the first block from the staging area
     store_block<false>(c, s, sm.a.o, o1, out, u1, nullptr, 32);
@@ -111,8 +115,9 @@ bool verify_mfma_supports(const VerifyArgs &a) {
 }
 
 hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(verify_mfma_n64_kernel, dim3((unsigned)(a.batch * a.H)), dim3(kThreads), 0,
-                       s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+    auto kernel = a.n <= 32 ? verify_mfma_n64_kernel<true> : verify_mfma_n64_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(a.batch * a.H)), dim3(kThreads), 0, s,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                        a.alpha, a.beta, a.parent, a.S0, a.out, a.n, a.H, device_cu_count(),
                        a.status);
     return hipGetLastError();

@@ -145,6 +145,57 @@ def test_commit_verify_deep_trees_n64(gpu_lib, mode):
         assert oracle.rel_err(host(uB), UB) <= BF16_GATE
 
 
+@pytest.mark.parametrize("n", [32, 17, 1])
+@pytest.mark.parametrize("max_path", [16, 32])
+@pytest.mark.parametrize("mode", ["solving", "carried_fp32", "carried_fp16"])
+def test_commit_verify_one_block_trees(gpu_lib, n, max_path, mode):
+    """new trees of at most 32 nodes (the kernels' one-block instances: only
+    the first 32-row block contracted and solved) after previous 32-node
+    trees: call 1 verifies set A, call 2 commits A's accepted branches (a
+    32-node path on the chain when max_path allows it) and verifies set B;
+    outputs, pseudo-values and the committed state against the oracle"""
+    say("commit-verify one block", n, max_path, mode)
+    rng = np.random.default_rng(n + 7 * max_path)
+    pa = np.stack([gs.chain_tree(32), gs.star_tree(32), gs.random_recursive_tree(rng, 32, 8)])
+    pb = np.stack([gs.chain_tree(n), gs.star_tree(n), gs.random_recursive_tree(rng, n, 8)])
+    acc = np.array([min(31, max_path - 1), 9, int(np.argmax(gs._depths(pa[2])))], np.int32)
+    A = gs.make_set(pa, 4, 128, 128, "bf16", seed=700 + max_path, accepted=acc)
+    B = gs.make_set(pb, 4, 128, 128, "bf16", seed=701 + n)
+    dA, dB = upload(A), upload(B)
+    path, plen = A.paths(max_path=max_path)
+    udt = {"solving": None, "carried_fp32": torch.float32, "carried_fp16": torch.float16}[mode]
+    uA = uB = None
+    if udt is not None:
+        uA = torch.empty(dA["v"].shape, dtype=udt, device="cuda")
+        uB = torch.empty(dB["v"].shape, dtype=udt, device="cuda")
+    S = dA["S0"].clone()
+    prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
+    st = torch.full((3,), -7, dtype=torch.int32, device="cuda")
+    outA = gpu_lib.commit_verify(S, dev(path), dev(np.zeros(3, np.int32)), prevA, dA["q"],
+                                 dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"],
+                                 u_out=uA, status=st)
+    torch.cuda.synchronize()
+    refA, _ = oracle.verify_set(A)
+    assert host(st).tolist() == [0] * 3 and torch.equal(S, dA["S0"])
+    assert oracle.rel_err(host(outA), refA) <= BF16_GATE
+    outB = gpu_lib.commit_verify(S, dev(path), dev(plen), prevA, dB["q"], dB["k"], dB["v"],
+                                 dB["alpha"], dB["beta"], dB["parent"], u_prev=uA, u_out=uB,
+                                 status=st)
+    torch.cuda.synchronize()
+    Sref, cst = oracle.commit_set(A, path_arr=path, path_len=plen)
+    oref, vst = oracle.verify(B.q, B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert host(st).tolist() == (cst | vst).tolist() == [0] * 3
+    es, eo = oracle.rel_err(host(S), Sref), oracle.rel_err(host(outB), oref)
+    say("rel err S", es, "out", eo)
+    assert es <= BF16_GATE and eo <= BF16_GATE
+    for b in range(3):
+        assert oracle.rel_err(host(S)[b], Sref[b]) <= BF16_GATE, b
+        assert oracle.rel_err(host(outB)[b], oref[b]) <= BF16_GATE, b
+    if uB is not None:
+        UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+        assert oracle.rel_err(host(uB), UB) <= BF16_GATE
+
+
 @pytest.mark.parametrize("udt", [torch.float32, torch.float16])
 def test_carried_commit_rejects_a_faulted_previous_tree(gpu_lib, udt):
     """a well-formed path through a previous tree whose parent row is
