@@ -264,14 +264,19 @@ __device__ __forceinline__ void verify_halves(const Lane &c, const Seq &s, Smem 
         tv128::rhs_and_decay(c, sm.tp, 0, P, R, vpk, rhs);
         tv128::solve_half(c, sm.b.s, rhs, P, u01, o);
     }
-    lds_barrier();   // every wave has read its V values and the solve blocks
-    store_half<kUout, kUh>(c, s, 0, o, u01, sm, out, u_out);
-
-    // ---- half 1's Q / K rows over half 0's
+    // ---- half 1's Q / K rows requested before half 0's stores, the key
+    //      fragments of the cross blocks right after them: both arrive while
+    //      the stores drain, not on the critical path behind them (issued
+    //      later, the compiler schedules the fragments into the contraction
+    //      and the cross blocks wait for them)
     const Lane c1 = fresh_lane();
     uint4 rq[4], rk[4];
     tv::load_rows(c1, s1, q, rq);
     tv::load_rows(c1, s1, k, rk);
+    lds_barrier();   // every wave has read its V values and the solve blocks
+    store_half<kUout, kUh>(c, s, 0, o, u01, sm, out, u_out);
+    bf16x8 kf[8];
+    load_key_frags(c1, s, k, c1.w & 1, kf);
     lds_barrier();   // every thread has stored its staged rows
     tv::store_rows_permuted(c1, rq, sm.a.t.q);
     tv::store_rows_permuted(c1, rk, sm.a.t.k);
@@ -283,8 +288,6 @@ __device__ __forceinline__ void verify_halves(const Lane &c, const Seq &s, Smem 
 #pragma unroll
     for (int q = 0; q < 4; ++q) contract_split_tile(c1, sm.a.t, ss[q], q, P, R);
     load_v_direct(c1, s1, v, vpk);
-    bf16x8 kf[8];
-    load_key_frags(c1, s, k, c1.w & 1, kf);
     {
         f32x16 gc, ga;
         gram_frags(c1, sm.a.t, c1.w >> 1, kf, gc, ga);
