@@ -60,6 +60,7 @@ gdn_status gdn_tree_verify(const void *q, const void *k, const void *v, gdn_dtyp
     gdn::VerifyArgs a{q, k, v, qkv_dtype, alpha, beta, parent, S0, out,
                       batch, n, H, d_k, d_v, status};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gdn::verify_split_supports(a)) return from_hip(gdn::launch_verify_split(a, s));
     if (gdn::verify_mfma_supports(a)) return from_hip(gdn::launch_verify_mfma(a, s));
     if (gdn::verify_mfma128_supports(a)) return from_hip(gdn::launch_verify_mfma128(a, s));
     return from_hip(gdn::launch_verify_generic(a, s));

@@ -50,6 +50,8 @@ int device_cu_count();
 // every launcher returns the launch's hipError_t (hipGetLastError after it)
 hipError_t launch_verify_generic(const VerifyArgs &a, hipStream_t s);
 hipError_t launch_branch_verify(const VerifyArgs &a, hipStream_t s);
+bool verify_split_supports(const VerifyArgs &a);
+hipError_t launch_verify_split(const VerifyArgs &a, hipStream_t s);
 bool verify_mfma_supports(const VerifyArgs &a);
 hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s);
 bool verify_mfma128_supports(const VerifyArgs &a);

@@ -146,6 +146,56 @@ def test_commit_verify_deep_trees_n64(gpu_lib, mode):
 
 
 @pytest.mark.parametrize("n", [32, 17, 1])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_verify_small_trees_both_launch_shapes(gpu_lib, n, batch):
+    """gdn_tree_verify on trees of at most 32 nodes with 32 heads: batch 1
+    takes the d_v-split launch (four single-wave workgroups per sequence and
+    head, each forming the tree matrices itself and solving a quarter of the
+    d_v columns), batch 8 the one-block instance of the 64-node kernel (one
+    workgroup per sequence and head); chains, stars, random trees and
+    two-root forests, whole tensors against the oracle"""
+    say("verify small trees", n, batch)
+    rng = np.random.default_rng(31 * n + batch)
+    shapes = [gs.chain_tree(n), gs.star_tree(n), gs.random_recursive_tree(rng, n, 8)]
+    if n >= 4:
+        f = gs.random_recursive_tree(rng, n, 6)
+        f[n // 2] = -1                     # a second root
+        shapes.append(f)
+    par = np.stack([shapes[b % len(shapes)] for b in range(batch)])
+    ts = gs.make_set(par, 32, 128, 128, "bf16", seed=900 + n + batch)
+    d = upload(ts)
+    st = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
+    out = gpu_lib.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S0"],
+                         status=st)
+    torch.cuda.synchronize()
+    ref, rst = oracle.verify_set(ts)
+    assert host(st).tolist() == rst.tolist() == [0] * batch
+    for b in range(batch):
+        err = oracle.rel_err(host(out)[b], ref[b])
+        say("seq", b, "rel err", err)
+        assert err <= BF16_GATE, b
+    assert torch.equal(d["S0"], upload(ts)["S0"])   # the state is only read
+
+
+def test_verify_split_launch_bad_parent(gpu_lib):
+    """the d_v-split launch on a malformed tree: that sequence's output rows
+    are NaN in every quarter, its status flag is set once, the other
+    sequence is verified as usual"""
+    rng = np.random.default_rng(5)
+    par = np.stack([gs.random_recursive_tree(rng, 32, 8) for _ in range(2)])
+    par[1, 5] = 5                          # a node that is its own parent
+    ts = gs.make_set(par, 32, 128, 128, "bf16", seed=905)
+    d = upload(ts)
+    st = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    out = host(gpu_lib.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                              d["S0"], status=st))
+    ref, rst = oracle.verify_set(ts)
+    assert host(st).tolist() == rst.tolist() == [0, 1]
+    assert np.isnan(out[1]).all() and np.isfinite(out[0]).all()
+    assert oracle.rel_err(out[0], ref[0]) <= BF16_GATE
+
+
+@pytest.mark.parametrize("n", [32, 17, 1])
 @pytest.mark.parametrize("max_path", [16, 32])
 @pytest.mark.parametrize("mode", ["solving", "carried_fp32", "carried_fp16"])
 def test_commit_verify_one_block_trees(gpu_lib, n, max_path, mode):
