@@ -134,6 +134,8 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
         u_out,
         u_dtype == GDN_DTYPE_F16};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gdn::commit_verify_split_supports(a))
+        return from_hip(gdn::launch_commit_verify_split(a, s));
     if (gdn::commit_verify_mfma_supports(a)) return from_hip(gdn::launch_commit_verify_mfma(a, s));
     // 65..128 new nodes: one launch, the commit solving for its
     // pseudo-values (u_prev not needed)

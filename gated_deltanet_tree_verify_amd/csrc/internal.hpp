@@ -59,6 +59,8 @@ hipError_t launch_verify_mfma128(const VerifyArgs &a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
 bool commit_mfma_supports(const CommitArgs &a);
 hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s);
+bool commit_verify_split_supports(const CommitVerifyArgs &a);
+hipError_t launch_commit_verify_split(const CommitVerifyArgs &a, hipStream_t s);
 bool commit_verify_mfma_supports(const CommitVerifyArgs &a);
 hipError_t launch_commit_verify_mfma(const CommitVerifyArgs &a, hipStream_t s);
 bool commit_verify_mfma128_supports(const CommitVerifyArgs &a);

@@ -246,6 +246,79 @@ def test_commit_verify_one_block_trees(gpu_lib, n, max_path, mode):
         assert oracle.rel_err(host(uB), UB) <= BF16_GATE
 
 
+@pytest.mark.parametrize("n", [32, 17, 1])
+@pytest.mark.parametrize("mode", ["solving", "carried_fp32", "carried_fp16"])
+def test_commit_verify_split_launch(gpu_lib, n, mode):
+    """the d_v-split fused launch (2 sequences x 32 heads: four three-wave
+    workgroups per sequence and head, each committing and verifying a
+    quarter of the d_v columns): call 1 verifies the 32-node trees A and
+    writes their pseudo-values, call 2 commits A's accepted branches (16
+    nodes for the solving commit, 32 with pseudo-values carried) and
+    verifies the trees B; then a call with a malformed new tree on
+    sequence 0 (its branch still committed, NaN outputs) and an id out of
+    range on sequence 1's path (state unchanged)"""
+    say("commit-verify split launch", n, mode)
+    rng = np.random.default_rng(n + 17)
+    max_path = 16 if mode == "solving" else 32
+    pa = np.stack([gs.random_recursive_tree(rng, 32, 8), gs.chain_tree(32)])
+    pb = np.stack([gs.chain_tree(n), gs.random_recursive_tree(rng, n, 8)])
+    acc = np.array([int(np.argmax(gs._depths(pa[0]))), max_path - 1], np.int32)
+    A = gs.make_set(pa, 32, 128, 128, "bf16", seed=760 + n, accepted=acc)
+    B = gs.make_set(pb, 32, 128, 128, "bf16", seed=761 + n)
+    dA, dB = upload(A), upload(B)
+    path, plen = A.paths(max_path=max_path)
+    udt = {"solving": None, "carried_fp32": torch.float32, "carried_fp16": torch.float16}[mode]
+    uA = uB = None
+    if udt is not None:
+        uA = torch.empty(dA["v"].shape, dtype=udt, device="cuda")
+        uB = torch.empty(dB["v"].shape, dtype=udt, device="cuda")
+    S = dA["S0"].clone()
+    prevA = (dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"])
+    st = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    outA = gpu_lib.commit_verify(S, dev(path), dev(np.zeros(2, np.int32)), prevA, dA["q"],
+                                 dA["k"], dA["v"], dA["alpha"], dA["beta"], dA["parent"],
+                                 u_out=uA, status=st)
+    torch.cuda.synchronize()
+    refA, _ = oracle.verify_set(A)
+    assert host(st).tolist() == [0, 0] and torch.equal(S, dA["S0"])
+    assert oracle.rel_err(host(outA), refA) <= BF16_GATE
+    if uA is not None:
+        UA, _ = oracle.pseudo(A.k, A.v, A.alpha, A.beta, A.parent, A.S0)
+        assert oracle.rel_err(host(uA), UA) <= BF16_GATE
+    outB = gpu_lib.commit_verify(S, dev(path), dev(plen), prevA, dB["q"], dB["k"], dB["v"],
+                                 dB["alpha"], dB["beta"], dB["parent"], u_prev=uA, u_out=uB,
+                                 status=st)
+    torch.cuda.synchronize()
+    Sref, cst = oracle.commit_set(A, path_arr=path, path_len=plen)
+    oref, vst = oracle.verify(B.q, B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+    assert host(st).tolist() == (cst | vst).tolist() == [0, 0]
+    for b in range(2):
+        assert oracle.rel_err(host(S)[b], Sref[b]) <= BF16_GATE, b
+        assert oracle.rel_err(host(outB)[b], oref[b]) <= BF16_GATE, b
+    if uB is not None:
+        UB, _ = oracle.pseudo(B.k, B.v, B.alpha, B.beta, B.parent, Sref)
+        assert oracle.rel_err(host(uB), UB) <= BF16_GATE
+    # faults: sequence 0's new tree malformed, sequence 1's path out of range
+    S = dA["S0"].clone()
+    badB = B.parent.copy()
+    badB[0, 0] = -5
+    bpath = path.copy()
+    bpath[1, plen[1] - 1] = 32
+    outF = gpu_lib.commit_verify(S, dev(bpath), dev(plen), prevA, dB["q"], dB["k"], dB["v"],
+                                 dB["alpha"], dB["beta"], dev(badB), u_prev=uA, u_out=uB,
+                                 status=st)
+    torch.cuda.synchronize()
+    assert host(st).tolist() == [1, 2]
+    assert oracle.rel_err(host(S)[0], Sref[0]) <= BF16_GATE
+    assert np.array_equal(host(S)[1], A.S0[1])
+    assert np.isnan(host(outF)[0]).all()
+    if uB is not None:
+        assert np.isnan(host(uB)[0].astype(np.float32)).all()
+    o1, _ = oracle.verify(B.q[1:], B.k[1:], B.v[1:], B.alpha[1:], B.beta[1:], B.parent[1:],
+                          A.S0[1:])
+    assert oracle.rel_err(host(outF)[1], o1[0]) <= BF16_GATE
+
+
 @pytest.mark.parametrize("udt", [torch.float32, torch.float16])
 def test_carried_commit_rejects_a_faulted_previous_tree(gpu_lib, udt):
     """a well-formed path through a previous tree whose parent row is
