@@ -17,10 +17,15 @@
 //           the chunk's keys and gates, then the chunk (path_commit.hpp);
 //   wave 1: the new tree's K rows, the quarter's state columns and v values,
 //           then the chunk's values (or carried pseudo-values) in its
-//           columns; the commit once the chunk is built, the committed
-//           columns written back, P and R, the solve and the output rows;
+//           columns.  Solving commit: Q S and K S from the slab before the
+//           commit while the chunk is built; R_p = K_p S and the Grams of the
+//           path keys against the new tree's queries and keys; the commit
+//           once the chunk's T is in, Q S' and K S' by the commit's rank-m
+//           correction.  Carried: the commit as soon as the chunk's keys are
+//           in, then Q S' and K S'.  Then the committed columns written back,
+//           the solve and the output rows;
 //   wave 2: the new tree's gates and Q rows, the topology, the Gram tile,
-//           masks and T = (I + X)^{-1}.
+//           masks and T = (I + X)^{-1}, its substitution beside the chunk's.
 #include "internal.hpp"
 #include "path_commit.hpp"
 #include "tree_split.hpp"
@@ -44,6 +49,36 @@ struct Smem {
     int pid[kMaxPathIds];     // previous path ids
     int commit_ok;
 };
+
+// Q S' and K S' from P = Q S and R = K S (S the slab before the commit):
+// the commit is S' = e^{g_l} S + K_p^T W with W_j = e^{g_l - g_j} u_j, so
+// Q S' = e^{g_l} Q S + (Q K_p^T) W and likewise for K.  Gq, Gk are the
+// transposed Grams K_p Q^T and K_p K^T (rows = path slots crow(r, h)),
+// i.e. register for register the A operands of Q K_p^T and K K_p^T; W
+// enters split hi / lo as in the update of the slab (pc::apply_update).
+template <int NR>
+__device__ __forceinline__ void correct(f32x16 &P, f32x16 &R, const f32x16 &Gq,
+                                        const f32x16 &Gk, const f32x16 &U, const float *wdec,
+                                        float gl, int h) {
+    constexpr int KS = NR / 16;   // k-steps over path slots that can be nonzero
+    P = P * gl;
+    R = R * gl;
+    const SplitTile gq = split_tile(Gq), gk = split_tile(Gk);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        float wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[j] = wdec[crow(8 * kk + j, h)] * U[8 * kk + j];
+        bf16x8 wh, wl;
+        split8(wv, wh, wl);
+        P = mfma(gq.hi[kk], wh, P);
+        P = mfma(gq.hi[kk], wl, P);
+        P = mfma(gq.lo[kk], wh, P);
+        R = mfma(gk.hi[kk], wh, R);
+        R = mfma(gk.hi[kk], wl, R);
+        R = mfma(gk.lo[kk], wh, R);
+    }
+}
 
 // kU: the previous tree's pseudo-values u_prev are given (the commit is the
 // rank-m update, no solve); kUout: the new tree's pseudo-values go to u_out;
@@ -132,20 +167,17 @@ __global__ __launch_bounds__(kThreads) void commit_verify_split_kernel(
     const bool tree_ok = !sm.t.bad;
     const bool commit = sm.commit_ok;
 
-    // ---- 2. the chunk (wave 0), its values (wave 1), the new tree's Gram
-    //         and masks (wave 2)
+    // ---- 2. the chunk's keys (and X) (wave 0); the chunk's values, then Q S
+    //         and K S from the slab before the commit (wave 1); the new tree's
+    //         Gram and masks (wave 2)
     pc::ChunkWords U0;
+    f32x16 P, R;
     if (w == 0) {
         if (l == 0 && quarter == 0 && s.hd == 0 && status)
             status[s.b] = (path_ok ? 0 : kFaultBadPath) | (tree_ok ? 0 : kFaultBadParent);
         if (commit) {
-            if constexpr (kU) {
-                pc::build_keys32(sm.ch.kc, sm.cx, k32, min(32, mlen), l);
-            } else {
-                pc::build16_x(sm.ch.e, sm.cx, r16.k, r16.la, r16.bt, min(pc::kC16, mlen), l);
-                ts::wave_lds_sync();
-                pc::build16_t(sm.ch.e, l);
-            }
+            if constexpr (kU) pc::build_keys32(sm.ch.kc, sm.cx, k32, min(32, mlen), l);
+            else pc::build16_x(sm.ch.e, sm.cx, r16.k, r16.la, r16.bt, min(pc::kC16, mlen), l);
         }
     } else if (w == 1) {
         // (unconditional: with no valid slots every load reads past the end
@@ -159,37 +191,84 @@ __global__ __launch_bounds__(kThreads) void commit_verify_split_kernel(
         } else {
             U0 = pc::load_v_chunk16(v_prev + prow0, pbytes, sm.pid, 0, mc0, H * tv::kD, col, h);
         }
+        // (the solving commit's chunk takes longer to build than the
+        // contraction: Q S and K S from the slab before the commit, corrected
+        // after it; with pseudo-values carried the chunk is ready at once and
+        // the contraction follows the commit)
+        if (!kU && tree_ok) ts::contract(sm.t, st, m, h, P, R);
     } else if (tree_ok) {
         ts::gram_mask(sm.t, m, h);
     }
-    lds_barrier();   // the chunk, X and Y
+    lds_barrier();   // the chunk's keys (and X); the tree's X and Y
 
-    // ---- 3. the commit of the quarter's columns and P / R (wave 1), T (wave 2)
-    f32x16 P, R;
-    if (w == 1) {
+    // ---- 3. the solving commit: the chunk's T (wave 0); R_p = K_p S and the
+    //         Grams of the path keys against the new tree's queries and keys
+    //         (wave 1); the substitution of the tree's diagonal sub-blocks
+    //         (wave 2).  Pseudo-values carried: the commit and the contraction
+    //         (wave 1), the tree's whole inverse (wave 2).
+    f32x16 Rp, Gq, Gk;
+    if (w == 0) {
+        if constexpr (!kU) {
+            if (commit) pc::build16_t(sm.ch.e, l);
+        }
+    } else if (w == 1 && kU) {
+        // pseudo-values carried: the commit, the committed columns written
+        // back, then Q S' and K S'
         if (commit) {
             bf16x8 ident[2];
             pc::key_identity(ident, m, h);
-            if constexpr (kU) {
-                pc::apply_known_u(sm.ch.kc, sm.cx, pc::u_values<kUh>(U0), st, ident, m, h);
-            } else {
-                // R = K_p S over the four tiles in two accumulators, then
-                // U = T RHS and the update
-                const pc::ChunkView cv = pc::early_view(sm.ch.e, sm.cx, m);
-                f32x16 Ra = {}, Rb = {};
-                pc::rp_tile(cv.kp_row, st[0], 0, Ra, h);
-                pc::rp_tile(cv.kp_row, st[1], 1, Rb, h);
-                pc::rp_tile(cv.kp_row, st[2], 2, Ra, h);
-                pc::rp_tile(cv.kp_row, st[3], 3, Rb, h);
-                pc::finish_rows_v<pc::kC16>(cv, pc::widen_bf16(U0), Ra + Rb, st, ident, h);
-            }
+            pc::apply_known_u(sm.ch.kc, sm.cx, pc::u_values<kUh>(U0), st, ident, m, h);
             store_state(st, slab, col, h);
         }
         if (tree_ok) ts::contract(sm.t, st, m, h, P, R);
-    } else if (w == 2 && tree_ok) {
-        ts::inverse(sm.t, l);
+    } else if (w == 1) {
+        if (commit) {
+            const uint16_t *kp_row;
+            if constexpr (kU) kp_row = sm.ch.kc.kp[m];
+            else kp_row = m < pc::kC16 ? sm.ch.e.kp[m] : sm.cx.zk;
+            if constexpr (!kU) {
+                // two accumulators (two short MFMA chains)
+                f32x16 Ra = {}, Rb = {};
+                pc::rp_tile(kp_row, st[0], 0, Ra, h);
+                pc::rp_tile(kp_row, st[1], 1, Rb, h);
+                pc::rp_tile(kp_row, st[2], 2, Ra, h);
+                pc::rp_tile(kp_row, st[3], 3, Rb, h);
+                Rp = Ra + Rb;
+            }
+            if (tree_ok) {
+                // transposed: lane (node i = m, h) holds k_p,s.q_i and k_p,s.k_i
+                // for path slot s = crow(r, h)
+                Gq = Gk = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const bf16x8 a = lds8(kp_row + 16 * kk + 8 * h);
+                    Gq = mfma(a, lds8(&sm.t.q[m][16 * kk + 8 * h]), Gq);
+                    Gk = mfma(a, lds8(&sm.t.k[m][16 * kk + 8 * h]), Gk);
+                }
+            }
+        }
+    } else if (tree_ok) {
+        if constexpr (kU) ts::inverse(sm.t, l);
+        else ts::inverse_subst(sm.t, l);
     }
-    lds_barrier();   // T
+    lds_barrier();   // the chunk's T; the tree's sub-block inverses (all of T when carried)
+
+    // ---- 4. the solving commit of the quarter's columns, then Q S' and K S'
+    //         from Q S and K S (wave 1); the rest of the tree's inverse (wave 2)
+    if (w == 1 && !kU) {
+        if (commit) {
+            bf16x8 ident[2];
+            pc::key_identity(ident, m, h);
+            const pc::ChunkView cv = pc::early_view(sm.ch.e, sm.cx, m);
+            const f32x16 U = pc::chunk_u<pc::kC16>(cv, pc::widen_bf16(U0), Rp, h);
+            pc::apply_update<pc::kC16>(cv, U, st, ident, h);
+            if (tree_ok) correct<pc::kC16>(P, R, Gq, Gk, U, cv.wdec, cv.glast, h);
+            store_state(st, slab, col, h);
+        }
+    } else if (w == 2 && !kU && tree_ok) {
+        ts::inverse_finish(sm.t, l);
+    }
+    lds_barrier();   // the tree's T
     if (w != 1) return;
 
     // ---- 4. the solve and the output rows of the quarter's columns

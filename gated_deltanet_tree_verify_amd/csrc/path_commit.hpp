@@ -390,16 +390,14 @@ __device__ __forceinline__ void rp_tile(const uint16_t *kp_row, const f32x16 &st
     }
 }
 
-// The rest of a chunk's application once R = K_p S is complete: the
-// right-hand side beta (v - e^g R), U = T RHS, and the update of the slab.
-// vv[r] = v of path slot crow(r, h) in this lane's column, zero past the
-// chunk (no barrier inside).
+// The chunk's pseudo-values once R = K_p S is complete: the right-hand side
+// beta (v - e^g R) and U = T RHS (rows = path slots crow(r, h)).  vv[r] = v
+// of path slot crow(r, h) in this lane's column, zero past the chunk (no
+// barrier inside).
 template <int NR>
-__device__ __forceinline__ void finish_rows_v(const ChunkView &cv, const f32x16 &vv,
-                                              const f32x16 &R, f32x16 (&st)[4],
-                                              const bf16x8 (&ident)[2], int h) {
+__device__ __forceinline__ f32x16 chunk_u(const ChunkView &cv, const f32x16 &vv, const f32x16 &R,
+                                          int h) {
     constexpr int KS = NR / 16;   // k-steps over path slots that can be nonzero
-    // ---- right-hand side and U = T RHS, scaled by the decay to the chunk end
     f32x16 rhs;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -420,7 +418,16 @@ __device__ __forceinline__ void finish_rows_v(const ChunkView &cv, const f32x16 
         U = mfma(ah, bll, U);
         U = mfma(al, bhh, U);
     }
-    apply_update<NR>(cv, U, st, ident, h);
+    return U;
+}
+
+// the rest of a chunk's application once R = K_p S is complete: U, then the
+// update of the slab
+template <int NR>
+__device__ __forceinline__ void finish_rows_v(const ChunkView &cv, const f32x16 &vv,
+                                              const f32x16 &R, f32x16 (&st)[4],
+                                              const bf16x8 (&ident)[2], int h) {
+    apply_update<NR>(cv, chunk_u<NR>(cv, vv, R, h), st, ident, h);
 }
 
 // Apply a prepared chunk of NR (16 or 32) path slots to this wave's state

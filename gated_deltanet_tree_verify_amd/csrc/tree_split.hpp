@@ -174,11 +174,12 @@ __device__ __forceinline__ void gram_mask(Tree &t, int m, int h) {
 }
 
 // One wave (X written and visible to it): T = (I + X)^{-1} as bf16 hi / lo
-// operand rows.  The diagonal sub-blocks by forward substitution (lane =
-// sub-block (l >> 4) & 1, column l & 15, lanes 32.. repeating 0..31; row r's
-// entries requested two rows ahead of their use), then Z = B A^{-1} over A
+// operand rows, in two parts.  inverse_subst: the diagonal sub-blocks by
+// forward substitution (lane = sub-block (l >> 4) & 1, column l & 15, lanes
+// 32.. repeating 0..31; row r's entries requested two rows ahead of their
+// use).  inverse_finish (the sub-block inverses visible): Z = B A^{-1} over A
 // and L = -C^{-1} Z over B (lane = row, four columns), then the split.
-__device__ __forceinline__ void inverse(Tree &t, int l) {
+__device__ __forceinline__ void inverse_subst(Tree &t, int l) {
     {
         const int sbk = (l >> 4) & 1, cl = l & 15, o16 = 16 * sbk;
         float tv[16];
@@ -209,7 +210,9 @@ __device__ __forceinline__ void inverse(Tree &t, int l) {
             for (int r = 0; r < 16; ++r) t.tinv[sbk][r][cl] = tv[r];
         }
     }
-    wave_lds_sync();
+}
+
+__device__ __forceinline__ void inverse_finish(Tree &t, int l) {
     {
         const int r = l >> 2, c4 = 4 * (l & 3);
         auto row_times = [&](const float *a, const float *b, int ldb) {
@@ -262,6 +265,12 @@ __device__ __forceinline__ void inverse(Tree &t, int l) {
         st8(&t.th[r][8 * seg], th8);
         st8(&t.tl[r][8 * seg], tl8);
     }
+}
+
+__device__ __forceinline__ void inverse(Tree &t, int l) {
+    inverse_subst(t, l);
+    wave_lds_sync();
+    inverse_finish(t, l);
 }
 
 // P = Q S and R = K S for this lane's column, the slab split hi / lo (the
