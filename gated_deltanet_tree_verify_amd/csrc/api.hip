@@ -98,6 +98,7 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path, const int32_t *path_le
     gdn::CommitArgs a{S, path, path_len, max_path, k, v, qkv_dtype, alpha, beta, parent,
                       batch, n, H, d_k, d_v, status};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gdn::commit_split_supports(a)) return from_hip(gdn::launch_commit_split(a, s));
     if (gdn::commit_mfma_supports(a)) return from_hip(gdn::launch_commit_mfma(a, s));
     return from_hip(gdn::launch_commit(a, s));
 }

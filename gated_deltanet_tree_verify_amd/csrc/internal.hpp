@@ -57,6 +57,8 @@ hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s);
 bool verify_mfma128_supports(const VerifyArgs &a);
 hipError_t launch_verify_mfma128(const VerifyArgs &a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
+bool commit_split_supports(const CommitArgs &a);
+hipError_t launch_commit_split(const CommitArgs &a, hipStream_t s);
 bool commit_mfma_supports(const CommitArgs &a);
 hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s);
 bool commit_verify_split_supports(const CommitVerifyArgs &a);

@@ -319,6 +319,44 @@ def test_commit_verify_split_launch(gpu_lib, n, mode):
     assert oracle.rel_err(host(outF)[1], o1[0]) <= BF16_GATE
 
 
+@pytest.mark.parametrize("n", [128, 32, 16])
+def test_commit_split_launch(gpu_lib, n):
+    """gdn_tree_commit on a small launch (2 sequences x 32 heads: four
+    two-wave workgroups per sequence and head, each committing a quarter of
+    the d_v columns) with paths of up to 16 nodes: a chain's first 16 nodes
+    (the whole chunk) and a random tree's deepest path; then the same with
+    an id out of range on sequence 1 (state unchanged) and an empty path on
+    sequence 0 (a no-op)"""
+    say("commit split launch", n)
+    rng = np.random.default_rng(n + 3)
+    par = np.stack([gs.chain_tree(n), gs.random_recursive_tree(rng, n, 12)])
+    d1 = gs._depths(par[1])
+    leaf = int(np.argmax(np.where(d1 < 16, d1, -1)))
+    ts = gs.make_set(par, 32, 128, 128, "bf16", seed=880 + n,
+                     accepted=np.array([15, leaf], np.int32))
+    d = upload(ts)
+    path, plen = ts.paths(max_path=16)
+    assert plen.tolist() == [16, int(d1[leaf]) + 1]
+    S = d["S0"].clone()
+    st = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    gpu_lib.commit(S, dev(path), dev(plen), d["k"], d["v"], d["alpha"], d["beta"], d["parent"],
+                   status=st)
+    torch.cuda.synchronize()
+    Sref, rst = oracle.commit_set(ts, path_arr=path, path_len=plen)
+    assert host(st).tolist() == rst.tolist() == [0, 0]
+    for b in range(2):
+        assert oracle.rel_err(host(S)[b], Sref[b]) <= BF16_GATE, b
+    bpath, bplen = path.copy(), plen.copy()
+    bplen[0] = 0
+    bpath[1, bplen[1] - 1] = n
+    S = d["S0"].clone()
+    gpu_lib.commit(S, dev(bpath), dev(bplen), d["k"], d["v"], d["alpha"], d["beta"],
+                   d["parent"], status=st)
+    torch.cuda.synchronize()
+    assert host(st).tolist() == [0, 2]
+    assert torch.equal(S, d["S0"])
+
+
 @pytest.mark.parametrize("udt", [torch.float32, torch.float16])
 def test_carried_commit_rejects_a_faulted_previous_tree(gpu_lib, udt):
     """a well-formed path through a previous tree whose parent row is
