@@ -421,13 +421,36 @@ __device__ __forceinline__ f32x16 chunk_u(const ChunkView &cv, const f32x16 &vv,
     return U;
 }
 
-// the rest of a chunk's application once R = K_p S is complete: U, then the
-// update of the slab
+// The rest of a chunk's application once R = K_p S is complete: the
+// right-hand side beta (v - e^g R), U = T RHS, and the update of the slab
+// (vv as for chunk_u; the same steps written out in one body)
 template <int NR>
 __device__ __forceinline__ void finish_rows_v(const ChunkView &cv, const f32x16 &vv,
                                               const f32x16 &R, f32x16 (&st)[4],
                                               const bf16x8 (&ident)[2], int h) {
-    apply_update<NR>(cv, chunk_u<NR>(cv, vv, R, h), st, ident, h);
+    constexpr int KS = NR / 16;   // k-steps over path slots that can be nonzero
+    // ---- right-hand side and U = T RHS, scaled by the decay to the chunk end
+    f32x16 rhs;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int j = crow(r, h);
+        rhs[r] = j < NR ? cv.beta[j] * (vv[r] - cv.eg[j] * R[r]) : 0.f;
+    }
+    f32x16 U = {};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        float bv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = rhs[8 * kk + j];
+        bf16x8 bhh, bll;
+        split8(bv, bhh, bll);
+        const bf16x8 ah = lds8(cv.th_row + 16 * kk + 8 * h);
+        const bf16x8 al = lds8(cv.tl_row + 16 * kk + 8 * h);
+        U = mfma(ah, bhh, U);
+        U = mfma(ah, bll, U);
+        U = mfma(al, bhh, U);
+    }
+    apply_update<NR>(cv, U, st, ident, h);
 }
 
 // Apply a prepared chunk of NR (16 or 32) path slots to this wave's state
