@@ -443,9 +443,10 @@ def main():
                 d["beta"], d["parent"], out=d["out"], u_prev=d["u"][j & 1],
                 u_out=d["u"][1 - (j & 1)]),
         }
-        # the same layer cut to its first 8 heads (8 workgroups instead of 32):
-        # if the latency stays, the chain of dependent stages inside one
-        # workgroup sets it, not the number of CUs the launch occupies
+        # the same layer cut to its first 8 heads (a quarter of the
+        # workgroups): if the latency stays, the chain of dependent stages
+        # inside one workgroup sets it, not the number of CUs the launch
+        # occupies
         d8 = {k_: (v_[:, :, :8].contiguous() if v_.dim() >= 3 else v_.clone())
               for k_, v_ in d.items() if isinstance(v_, torch.Tensor) and k_ not in ("S", "u")}
         d8["S"] = d["S"][:, :8].contiguous()
