@@ -684,7 +684,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": read_traffic(HEADLINE_STEP),
                      "kernel": "gdn_tree_commit_verify (%s)" % HEADLINE_STEP,
                      "algorithmic_bytes_per_launch": fbytes,
-                     "median_launch_us": step_s * 1e6, "target_frac": 0.60},
+                     "median_launch_us": step_s * 1e6, "target_frac": 0.60,
+                     "frac_of_copy": achieved / copy_gbps},
         "region_us": {k_: [x * 1e3 for x in v_[1]] for k_, v_ in res.items()},
         "fused_carried_us": us["carried"],
         "fused_carried_fp16_us": us["carried16"],
@@ -698,6 +699,7 @@ def main():
         "commit_hbm_gbps": cbytes / (res["commit"][0] * 1e-3) / 1e9,
         "host_enqueue_us_per_step": res[HEADLINE_STEP][2] * 1e6,
         "copy_gbps": copy_gbps,
+        "verify_frac_of_copy": vbytes / (res["verify"][0] * 1e-3) / 1e9 / copy_gbps,
         "tree_build_us": build_us,
         "accept_us": accept_us,
         "path_us": path_us,
