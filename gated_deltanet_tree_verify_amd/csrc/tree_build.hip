@@ -13,8 +13,9 @@
 // the next round on.
 //
 // One wave per sequence.  Every table row is sorted once (descending score,
-// ties by slot) into LDS, so a node's best remaining candidate is the head
-// of its sorted row: the heap becomes "best head over the live nodes", one
+// ties by slot) into LDS, and put in pop order when its node is inserted
+// (entries whose scores round to the same value ordered by slot), so a
+// node's best remaining candidate is the head of its row: the heap becomes "best head over the live nodes", one
 // wave-wide maximum per popped candidate.  Lane l owns nodes l and 64 + l
 // and keeps their heads, and the entries after them, in registers; a
 // candidate is one 64-bit word whose unsigned order is the pop order, and
@@ -82,6 +83,40 @@ __device__ __forceinline__ unsigned long long wave_max_2level(unsigned long long
     return ((unsigned long long)mhi << 32) | mlo;
 }
 
+// Puts one row of the sorted table in pop order for a node of score sc:
+// (rounded score sc + x descending, slot ascending), entries with no
+// candidate (x = -inf) last, by slot.  Called only when two distinct
+// log-probs of the row may round to the same score (see make_live); kept
+// out of line so that the build's round loop does not carry its code.
+__device__ __attribute__((noinline)) void pop_order_row(float *lp, unsigned char *js, float sc,
+                                                        int K) {
+    bool tie = false;
+    for (int t = 1; t < K; ++t)
+        tie |= lp[t] != -INFINITY && sc + lp[t] == sc + lp[t - 1];
+    if (!tie) return;
+    float xv[kMaxK];
+    int jv[kMaxK];
+    for (int t = 0; t < K; ++t) {
+        xv[t] = lp[t];
+        jv[t] = js[t];
+    }
+    for (int t = 0; t < K; ++t) {
+        const bool ct = xv[t] != -INFINITY;
+        const float st = sc + xv[t];
+        int rank = 0;
+        for (int t2 = 0; t2 < K; ++t2) {
+            const bool c2 = xv[t2] != -INFINITY;
+            const float s2 = sc + xv[t2];
+            const bool before =
+                (c2 && !ct) ||
+                (c2 == ct && ((c2 && s2 > st) || ((!c2 || s2 == st) && jv[t2] < jv[t])));
+            rank += before ? 1 : 0;
+        }
+        lp[rank] = xv[t];
+        js[rank] = (unsigned char)jv[t];
+    }
+}
+
 // One tree node owned by a lane.  x / j: log-probability and original slot
 // of its best remaining candidate (the head of its sorted row); xn / jn: the
 // entry after it, read ahead so that advancing the head waits for no LDS.
@@ -105,6 +140,8 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
     __shared__ float s_raw[kMaxN * kMaxK];            // the table as read
     __shared__ int32_t s_tok[kMaxN * kMaxK];          // the token ids, for the outputs
     __shared__ unsigned long long s_pop[kMaxN];       // the current round's popped words
+    __shared__ float2 s_gap[kMaxN];   // per row: smallest gap between distinct finite
+                                      // log-probs, largest |log-prob| (see pop_order)
     const int b = blockIdx.x, l = threadIdx.x;
     const float *lp = cand_logp + (size_t)b * n * K;
     const int32_t *tk = cand_tok + (size_t)b * n * K;
@@ -158,6 +195,23 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
         s_lp[i][K] = s_lp[i][K + 1] = -INFINITY;
         s_j[i][K] = s_j[i][K + 1] = 0;
     }
+    // per row (the lane's own, sorted above): the smallest gap between
+    // adjacent distinct finite log-probs and the largest |log-prob|, for
+    // the tie check of pop_order
+    for (int i = l; i < n; i += 64) {
+        float gap = INFINITY, vmax = 0.f, prev = s_lp[i][0];
+        if (prev != -INFINITY) vmax = fabsf(prev);
+#pragma unroll
+        for (int t = 1; t < KB; ++t) {
+            const float x = t < K ? s_lp[i][t] : -INFINITY;
+            if (x != -INFINITY) {
+                if (x < prev) gap = fminf(gap, prev - x);
+                vmax = fmaxf(vmax, fabsf(x));
+            }
+            prev = x;
+        }
+        s_gap[i] = make_float2(gap, vmax);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -174,12 +228,23 @@ __global__ __launch_bounds__(64) void tree_build_kernel(
         if (!d.live || d.dep + 1 > max_depth || d.x == -INFINITY) return 0ull;
         return pack(d.sc + d.x, i * 64 + d.j, d.dep);   // one fp32 addition, parent score first
     };
-    // node u becomes live with its head at slot rank 0
+    // Node u becomes live with its head at slot rank 0.  Its row was sorted
+    // by log-probability (descending, ties by slot), which gives
+    // non-increasing scores sc + x; but two entries whose scores round to the
+    // same fp32 value pop by slot (the earlier push), whatever their
+    // log-probabilities, and then the row is put in pop order first
+    // (pop_order_row).  That can only happen when two distinct log-probs of
+    // the row lie closer than the spacing of fp32 values at the scores'
+    // magnitude, at most (|sc| + max |x|) 2^-23: the row's smallest gap
+    // above twice that rules it out (an infinite score never passes).
     auto make_live = [&](int u) {
         const int i = 64 * u + l;
         nd[u].live = i < n;
         nd[u].head = 0;
         if (i < n) {
+            const float2 gp = s_gap[i];
+            if (!(gp.x > (fabsf(nd[u].sc) + gp.y) * 0x1p-22f))
+                pop_order_row(s_lp[i], s_j[i], nd[u].sc, K);
             nd[u].x = s_lp[i][0];
             nd[u].j = s_j[i][0];
             nd[u].xn = s_lp[i][1];

@@ -757,6 +757,29 @@ def test_tree_build_hand_worked_ties(gpu_lib):
         assert np.array_equal(host(sc)[0].view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("K,w", [(8, 4), (8, 1), (16, 8), (32, 3)])
+def test_tree_build_rounding_ties(gpu_lib, K, w):
+    """log-probs near -8 that differ by less than a unit in the last place of
+    the running scores (|score| 16..128): many pairs of one row round to the
+    same fp32 score although their log-probs differ, in random slot order;
+    such ties pop by slot, so the order of the raw log-probs must not
+    decide.  Bit-exact against the oracle."""
+    rng = np.random.default_rng(K * 10 + w)
+    batch, n = 6, 48
+    base = -8.0 + 0.5 * rng.integers(0, 3, size=(batch, n, K))
+    lp = (base + rng.uniform(-3e-7, 3e-7, size=base.shape)).astype(np.float32)
+    lp[rng.random(lp.shape) < 0.15] = -np.inf
+    lp[:, 0, 0] = -8.0                       # the root proposes something
+    tok = rng.integers(0, 50000, size=lp.shape).astype(np.int32)
+    root = rng.integers(0, 50000, size=batch).astype(np.int32)
+    par, tk, sc, nb = gpu_lib.build_tree(dev(lp), dev(tok), dev(root), w, 16)
+    torch.cuda.synchronize()
+    rp, rt, rs, rn = oracle.build_trees(lp, tok, root, w, 16)
+    assert host(nb).tolist() == rn.tolist()
+    assert np.array_equal(host(par), rp) and np.array_equal(host(tk), rt)
+    assert np.array_equal(host(sc).view(np.uint32), rs.view(np.uint32))
+
+
 def test_tree_build_overflowing_scores(gpu_lib):
     # scores that overflow to -inf are still candidates (popped last, by push
     # order), and a +inf score is popped first

@@ -635,10 +635,12 @@ def _tie_golden():
     return out
 
 
-@pytest.mark.parametrize("case", [0, 1])
+@pytest.mark.parametrize("case", [0, 1, 2])
 def test_tree_build_tie_order_hand_worked(case):
     """ties between equal scores go to the lower node id, then the lower slot
-    (hand-derived fixture; a reversed tie order changes every case)"""
+    (hand-derived fixture; a reversed tie order changes every case), also
+    when two log-probs of one row differ but their fp32 sums with the
+    node's score round to the same value (case 2)"""
     c, lp, tok, sc = _tie_golden()[case]
     par, tk, s, nb = oracle.build_tree(lp, tok, c["root_tok"], c["n"], c["width"],
                                        c["max_depth"])
