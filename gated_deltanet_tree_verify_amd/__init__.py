@@ -25,7 +25,7 @@ import threading
 
 __all__ = ["load", "lib_path", "verify", "branch_verify", "commit", "commit_verify", "build_tree", "accept", "path", "Launch", "index", "status_string",
            "GdnError", "FAULT_BAD_PARENT", "FAULT_BAD_PATH", "DTYPE_F32", "DTYPE_BF16",
-           "MAX_NODES", "MAX_DIM", "build"]
+           "MAX_NODES", "MAX_DIM", "ABI_VERSION", "build"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libgdntree.so"
@@ -38,6 +38,8 @@ DTYPE_F16 = 2     # pseudo-values of commit_verify only
 MAX_NODES = 128
 MAX_DIM = 128
 MAX_CANDIDATES = 32
+# GDN_TREE_ABI_VERSION of include/gdn_tree.h that the signatures below follow
+ABI_VERSION = 8
 
 _lock = threading.Lock()
 _lib = None
@@ -93,6 +95,10 @@ def load() -> ctypes.CDLL:
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_tree_abi_version.argtypes = []
         lib.gdn_tree_abi_version.restype = I
+        got = lib.gdn_tree_abi_version()
+        if got != ABI_VERSION:
+            raise RuntimeError(f"{p} has ABI version {got}, this binding expects {ABI_VERSION}; "
+                               "rebuild with gated_deltanet_tree_verify_amd.build()")
         _lib = lib
         return lib
 

@@ -41,6 +41,9 @@ def test_exports_every_declared_symbol(lib):
 def test_abi_version_and_strings(lib):
     m = re.search(r"#define GDN_TREE_ABI_VERSION (\d+)", open(HEADER).read())
     assert lib.gdn_tree_abi_version() == int(m.group(1))
+    # the binding's signatures follow the same header version (load() refuses
+    # a library of another version)
+    assert g.ABI_VERSION == int(m.group(1))
     for code in (0, -1, -2, -3, 5):
         assert isinstance(g.status_string(code), str) and g.status_string(code)
 
