@@ -48,6 +48,16 @@ def test_abi_version_and_strings(lib):
         assert isinstance(g.status_string(code), str) and g.status_string(code)
 
 
+def test_load_refuses_another_abi_version(lib, monkeypatch):
+    # a binding that expects another version must not call into this library
+    monkeypatch.setattr(g, "_lib", None)
+    monkeypatch.setattr(g, "ABI_VERSION", lib.gdn_tree_abi_version() + 1)
+    with pytest.raises(RuntimeError, match="ABI version"):
+        g.load()
+    monkeypatch.undo()
+    assert g.load() is lib
+
+
 def _verify(lib, ptr=FAKE, batch=1, n=8, H=1, dk=16, dv=16, dtype=1, null=None, status=None,
             fn="gdn_tree_verify"):
     p = [ptr] * 8
