@@ -500,8 +500,8 @@ def test_commit_verify_matches_separate_calls(gpu_lib):
     (128, 64, 128, 128, "bf16", None),   # fused kernel, four commit chunks
     (20, 1, 128, 128, "bf16", None),     # fused kernel, one-node tree
     (64, 64, 128, 128, "bf16", 13),      # fused kernel, paths within the first chunk
-    (64, 100, 128, 128, "bf16", None),   # MFMA commit + generic verify
-    (8, 65, 128, 128, "bf16", None),
+    (64, 100, 128, 128, "bf16", None),   # 65..128-node fused kernel, 32-slot chunks
+    (8, 65, 128, 128, "bf16", None),     # 65..128-node fused kernel, one 16-slot chunk
     (37, 37, 64, 64, "fp32", None),      # generic commit + generic verify
     (50, 30, 32, 48, "bf16", None),
 ])
