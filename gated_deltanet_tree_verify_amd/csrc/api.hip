@@ -63,6 +63,7 @@ gdn_status gdn_tree_verify(const void *q, const void *k, const void *v, gdn_dtyp
     if (gdn::verify_split_supports(a)) return from_hip(gdn::launch_verify_split(a, s));
     if (gdn::verify_mfma_supports(a)) return from_hip(gdn::launch_verify_mfma(a, s));
     if (gdn::verify_mfma128_supports(a)) return from_hip(gdn::launch_verify_mfma128(a, s));
+    if (gdn::verify_f32_supports(a)) return from_hip(gdn::launch_verify_f32(a, s));
     return from_hip(gdn::launch_verify_generic(a, s));
 }
 
@@ -150,6 +151,7 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
                                                         : gdn::launch_commit(a.c, s);
     if (e != hipSuccess) return GDN_ERR_HIP;
     if (gdn::verify_mfma128_supports(a.v)) return from_hip(gdn::launch_verify_mfma128(a.v, s));
+    if (gdn::verify_f32_supports(a.v)) return from_hip(gdn::launch_verify_f32(a.v, s));
     return from_hip(gdn::launch_verify_generic(a.v, s));
 }
 

@@ -56,6 +56,8 @@ bool verify_mfma_supports(const VerifyArgs &a);
 hipError_t launch_verify_mfma(const VerifyArgs &a, hipStream_t s);
 bool verify_mfma128_supports(const VerifyArgs &a);
 hipError_t launch_verify_mfma128(const VerifyArgs &a, hipStream_t s);
+bool verify_f32_supports(const VerifyArgs &a);
+hipError_t launch_verify_f32(const VerifyArgs &a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs &a, hipStream_t s);
 bool commit_split_supports(const CommitArgs &a);
 hipError_t launch_commit_split(const CommitArgs &a, hipStream_t s);
