@@ -74,6 +74,12 @@ TRAFFIC_FILES = {
 TRAFFIC_SOURCES = ("commit_verify_mfma.hip", "path_commit.hpp", "tree_verify.hpp",
                    "mfma_tile.hpp", "device_common.hpp")
 MAX_PATH = 13            # deepest path of the depth <= 12 trees, plus one
+# fp32 matrix peak of the chip (dense), for the all-fp32 verify leg
+FP32_MFMA_PEAK_TFLOPS = 157.3
+# 32x32x2 fp32 MFMA instructions the all-fp32 verify issues per (sequence,
+# head) at 64 nodes: 3 Gram blocks x (Q, K) x 64 k-steps, 4 waves x 256 for
+# Q S0 and K S0, 4 waves x 96 for the block solve; 4096 flops each
+F32_MFMA_PER_PAIR = 3 * 2 * 64 + 4 * 256 + 4 * 96
 GEN_WORKERS = 16         # host processes drawing the synthetic inputs
 
 
@@ -192,6 +198,12 @@ def _draw(job):
         ts = gs.make_config(wi, s=s)
     elif kind == "layer":
         ts = gs.make_config(4, layer=a)
+    elif kind == "f32":
+        # the 64-node workload's tree shapes with all-fp32 q/k/v
+        import numpy as np
+        ts = gs.make_set(gs.make_trees(2, np.random.default_rng(1000 + a)), 32, 128, 128,
+                         "fp32", seed=1000 + a)
+        return ts
     else:
         ts = gs.make_tree126(a)
     if not keep:
@@ -224,6 +236,8 @@ def main():
                          "batch-64 / 128-node side measurement")
     ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack")
     ap.add_argument("--no-latency", action="store_true", help="skip the batch-1 latency leg")
+    ap.add_argument("--no-fp32", action="store_true",
+                    help="skip the all-fp32 leg (64-node workload with fp32 q/k/v)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -248,6 +262,8 @@ def main():
     if not args.no_compare:
         jobs += [("t126", s, False) for s in range(8)]
         jobs += [("cfg", (3, s), False) for s in range(2)]
+    if not args.no_fp32:
+        jobs += [("f32", s, True) for s in range(2)]
     drawn = draw_all(jobs, GEN_WORKERS)
     pick = lambda kind, a: [ts for (k_, a_, _), ts in zip(jobs, drawn) if k_ == kind and
                             (a is None or a_ == a or (isinstance(a_, tuple) and a_[0] == a))]
@@ -651,6 +667,47 @@ def main():
         b_sets = vb = cb = cbp = fb = fbu = None
         torch.cuda.empty_cache()
 
+    # ---- the same 64-node workload with all-fp32 q/k/v: the verify on the
+    #      fp32-MFMA kernel, the commit and the fused call on the generic
+    #      kernels (the fused call is a commit launch then that verify)
+    f32 = None
+    if not args.no_fp32:
+        f_sets = []
+        for ts in pick("f32", None):
+            path, plen = ts.paths(max_path=MAX_PATH)
+            d = dict(q=dev(ts.q), k=dev(ts.k), v=dev(ts.v), alpha=dev(ts.alpha),
+                     beta=dev(ts.beta), parent=dev(ts.parent), S=dev(ts.S0), path=dev(path),
+                     plen=dev(plen), m=float(np.sum(plen)))
+            d["out"] = torch.empty((batch, n, H, dv), dtype=torch.float32, device="cuda")
+            f_sets.append(d)
+        vf = [g.verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["parent"], d["S"],
+                       out=d["out"], stream=stream, prepare=True) for d in f_sets]
+        cf = [g.commit(d["S"], d["path"], d["plen"], d["k"], d["v"], d["alpha"], d["beta"],
+                       d["parent"], stream=stream, prepare=True) for d in f_sets]
+        ff = [g.commit_verify(d["S"], f_sets[(i - 1) % 2]["path"], f_sets[(i - 1) % 2]["plen"],
+                              own(f_sets[(i - 1) % 2]), d["q"], d["k"], d["v"], d["alpha"],
+                              d["beta"], d["parent"], out=d["out"], stream=stream, prepare=True)
+              for i, d in enumerate(f_sets)]
+        t_vf = regions(lambda i: vf[i % 2](), 20, 2)[0] * 1e3
+        t_cf = regions(lambda i: cf[i % 2](), 4, 1)[0] * 1e3
+        t_ff = regions(lambda i: ff[i % 2](), 4, 1)[0] * 1e3
+        vf_bytes = verify_bytes(batch, n, H, dk, dv, elem=4)
+        cf_bytes = commit_bytes(batch, H, dk, dv, [np.mean([d["m"] for d in f_sets])], elem=4)
+        vf_tflops = batch * H * F32_MFMA_PER_PAIR * 4096 / (t_vf * 1e-6) / 1e12
+        f32 = {"workload": w.name + "-fp32", "verify_us": t_vf, "commit_us": t_cf,
+               "commit_verify_us": t_ff,
+               "verify_nodes_per_s": batch * n / (t_vf * 1e-6),
+               "verify_hbm_gbps": vf_bytes / (t_vf * 1e-6) / 1e9,
+               "verify_mfma_tflops": vf_tflops,
+               "verify_mfma_frac": vf_tflops / FP32_MFMA_PEAK_TFLOPS,
+               "commit_hbm_gbps": cf_bytes / (t_cf * 1e-6) / 1e9,
+               "verify_algorithmic_bytes": vf_bytes, "commit_algorithmic_bytes": cf_bytes}
+        log(f"fp32 b16/n64: verify {t_vf:.1f} us ({vf_tflops:.1f} TFLOP/s on the fp32 matrix "
+            f"units, {f32['verify_hbm_gbps']:.0f} GB/s), commit {t_cf:.1f} us, "
+            f"commit_verify {t_ff:.1f} us")
+        f_sets = vf = cf = ff = None
+        torch.cuda.empty_cache()
+
     # ---- achievable-bandwidth line: a plain 1 GiB device copy
     src = torch.empty(2**28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -707,6 +764,7 @@ def main():
         "stack48": stack,
         "tree126_vs_branch": cmp126,
         "b64_n128": b64,
+        "fp32_b16_n64": f32,
     }
     if not args.no_cpu_baseline:
         ts = main_host[0]
