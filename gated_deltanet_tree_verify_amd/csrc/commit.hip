@@ -9,7 +9,10 @@
 // columns and all d_k rows of it, split over four row groups of threads;
 // w for a column is the sum of four partial dot products exchanged in LDS.
 // The tile stays in registers for the whole path: S is read once and
-// written once, which is the HBM floor for an in-place commit.
+// written once, which is the HBM floor for an in-place commit.  The path's
+// rows (k, this tile's v, alpha, beta) are staged in LDS 8 nodes at a
+// time, all of a chunk's loads in flight together, so the steps wait on no
+// global load.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -20,6 +23,9 @@ constexpr int kThreads = 256;
 constexpr int kTileV = 64;
 constexpr int kGroups = kThreads / kTileV;               // row groups
 constexpr int kRowsMax = GDN_MAX_DIM / kGroups;          // rows per thread (<= 32)
+constexpr int kChunk = 8;                                // path nodes staged at a time
+constexpr int kKLoads = kChunk * GDN_MAX_DIM / kThreads; // k values per thread and chunk
+constexpr int kVLoads = kChunk * kTileV / kThreads;      // v values per thread and chunk
 
 // A path is valid when 0 <= m <= max_path, every id is in [0, n), the first
 // node is a root (parent -1) and every later node's parent is the previous
@@ -48,8 +54,10 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     const float *__restrict__ alpha, const float *__restrict__ beta,
     const int32_t *__restrict__ parent, int n, int H, int dk, int dv,
     int32_t *__restrict__ status) {
-    __shared__ float s_k[GDN_MAX_DIM];
-    __shared__ float s_v[kTileV];
+    __shared__ float s_k[kChunk][GDN_MAX_DIM];
+    __shared__ float s_v[kChunk][kTileV];
+    __shared__ float s_a[kChunk], s_b[kChunk];
+    __shared__ int s_id[kChunk];
     __shared__ float s_part[kGroups][kTileV];
     __shared__ int s_ok;
 
@@ -83,31 +91,62 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
         reg[j] = (j < rows && r < dk && c < dv) ? st[(size_t)r * dv + c] : 0.f;
     }
 
-    for (int t = 0; t < m; ++t) {
-        const int node = prow[t];
-        const size_t row = ((size_t)b * n + node) * H + h;
-        for (int d = tid; d < dk; d += kThreads) s_k[d] = to_f32(k[row * dk + d]);
-        if (tid < kTileV) s_v[tid] = (c0 + tid < dv) ? to_f32(v[row * dv + c0 + tid]) : 0.f;
-        const float a = alpha[row], be = beta[row];
+    const size_t row0 = (size_t)b * n * H + h;   // gate row of node 0 (node stride H)
+    for (int t0 = 0; t0 < m; t0 += kChunk) {
+        const int mc = min(kChunk, m - t0);
+        __syncthreads();   // the previous chunk is consumed
+        if (tid < mc) s_id[tid] = prow[t0 + tid];
         __syncthreads();
-        float part = 0.f;
+        // every load of the chunk issued before any is stored
+        float kx[kKLoads], vx[kVLoads];
 #pragma unroll
-        for (int j = 0; j < kRowsMax; ++j)
-            if (j < rows && r0 + j < dk) part = fmaf(reg[j], s_k[r0 + j], part);
-        s_part[grp][cl] = part;
-        __syncthreads();
-        float w = 0.f;
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) w += s_part[g][cl];
-        const float vc = s_v[cl];
-#pragma unroll
-        for (int j = 0; j < kRowsMax; ++j) {
-            if (j < rows && r0 + j < dk) {
-                const float bk = be * s_k[r0 + j];
-                reg[j] = a * (reg[j] - bk * w) + bk * vc;
-            }
+        for (int it = 0; it < kKLoads; ++it) {
+            const int e = tid + kThreads * it, t = e / dk, d = e - t * dk;
+            const int id = s_id[min(t, kChunk - 1)];   // read only when t < mc
+            kx[it] = (t < mc) ? to_f32(k[(row0 + (size_t)id * H) * dk + d]) : 0.f;
         }
-        __syncthreads();   // s_k / s_v / s_part are rewritten by the next step
+#pragma unroll
+        for (int it = 0; it < kVLoads; ++it) {
+            const int e = tid + kThreads * it, t = e / kTileV, cc = e - t * kTileV;
+            vx[it] = (t < mc && c0 + cc < dv)
+                         ? to_f32(v[(row0 + (size_t)s_id[t] * H) * dv + c0 + cc]) : 0.f;
+        }
+        if (tid < mc) {
+            const size_t row = row0 + (size_t)s_id[tid] * H;
+            s_a[tid] = alpha[row];
+            s_b[tid] = beta[row];
+        }
+#pragma unroll
+        for (int it = 0; it < kKLoads; ++it) {
+            const int e = tid + kThreads * it, t = e / dk, d = e - t * dk;
+            if (t < mc) s_k[t][d] = kx[it];
+        }
+#pragma unroll
+        for (int it = 0; it < kVLoads; ++it) {
+            const int e = tid + kThreads * it;
+            s_v[e / kTileV][e % kTileV] = vx[it];
+        }
+        __syncthreads();
+        for (int t = 0; t < mc; ++t) {
+            float part = 0.f;
+#pragma unroll
+            for (int j = 0; j < kRowsMax; ++j)
+                if (j < rows && r0 + j < dk) part = fmaf(reg[j], s_k[t][r0 + j], part);
+            s_part[grp][cl] = part;
+            __syncthreads();
+            float w = 0.f;
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) w += s_part[g][cl];
+            const float vc = s_v[t][cl], a = s_a[t], be = s_b[t];
+#pragma unroll
+            for (int j = 0; j < kRowsMax; ++j) {
+                if (j < rows && r0 + j < dk) {
+                    const float bk = be * s_k[t][r0 + j];
+                    reg[j] = a * (reg[j] - bk * w) + bk * vc;
+                }
+            }
+            __syncthreads();   // s_part is rewritten by the next step
+        }
     }
 
 #pragma unroll
