@@ -101,6 +101,7 @@ gdn_status gdn_tree_commit(float *S, const int32_t *path, const int32_t *path_le
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gdn::commit_split_supports(a)) return from_hip(gdn::launch_commit_split(a, s));
     if (gdn::commit_mfma_supports(a)) return from_hip(gdn::launch_commit_mfma(a, s));
+    if (gdn::commit_f32_supports(a)) return from_hip(gdn::launch_commit_f32(a, s));
     return from_hip(gdn::launch_commit(a, s));
 }
 
@@ -148,7 +149,8 @@ gdn_status gdn_tree_commit_verify(float *S, const int32_t *path, const int32_t *
     // (the commit solves for the pseudo-values itself, so u_prev is not
     // needed), the verify ORing its flag into what the commit wrote
     const hipError_t e = gdn::commit_mfma_supports(a.c) ? gdn::launch_commit_mfma(a.c, s)
-                                                        : gdn::launch_commit(a.c, s);
+                         : gdn::commit_f32_supports(a.c) ? gdn::launch_commit_f32(a.c, s)
+                                                         : gdn::launch_commit(a.c, s);
     if (e != hipSuccess) return GDN_ERR_HIP;
     if (gdn::verify_mfma128_supports(a.v)) return from_hip(gdn::launch_verify_mfma128(a.v, s));
     if (gdn::verify_f32_supports(a.v)) return from_hip(gdn::launch_verify_f32(a.v, s));

@@ -63,6 +63,8 @@ bool commit_split_supports(const CommitArgs &a);
 hipError_t launch_commit_split(const CommitArgs &a, hipStream_t s);
 bool commit_mfma_supports(const CommitArgs &a);
 hipError_t launch_commit_mfma(const CommitArgs &a, hipStream_t s);
+bool commit_f32_supports(const CommitArgs &a);
+hipError_t launch_commit_f32(const CommitArgs &a, hipStream_t s);
 bool commit_verify_split_supports(const CommitVerifyArgs &a);
 hipError_t launch_commit_verify_split(const CommitVerifyArgs &a, hipStream_t s);
 bool commit_verify_mfma_supports(const CommitVerifyArgs &a);
