@@ -17,9 +17,10 @@
 // so that a result tile (register t = row crow(t, h)) feeds in as B.
 //   per chunk: every thread loads the chunk's key rows (as A rows of K_p and
 //   transposed, as A rows of K_p^T) and its column's v values, wave 0 the
-//   gates and their prefix; wave 0 forms the path Gram and T by forward
-//   substitution while the other waves contract R = K_p S; then every wave
-//   forms U, W and the update of its columns.
+//   gates and their prefix; wave 1 forms the path Gram and X while waves 0,
+//   2 and 3 contract R = K_p S, then wave 0 forms T by forward substitution
+//   while wave 1 contracts its R; then every wave forms U, W and the update
+//   of its columns.
 #include "internal.hpp"
 #include "path_commit.hpp"
 #include "tree_verify.hpp"
@@ -58,13 +59,6 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
 
 __device__ __forceinline__ float4 lds4(const float *p) {
     return *reinterpret_cast<const float4 *>(p);
-}
-
-// the wave's LDS writes visible to its own lanes (no workgroup barrier)
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // acc + A B for a 32-wide A-operand block (rows m, positions 16 h + t) and a
@@ -171,8 +165,22 @@ __global__ __launch_bounds__(kThreads, 2) void commit_f32_kernel(
         }
         lds_barrier();
 
-        // ---- wave 0: path Gram, X and T; every wave: R = K_p S
-        if (w == 0) {
+        // ---- wave 1: the path Gram and X while waves 0, 2 and 3 contract
+        //      R = K_p S; then wave 0: T while wave 1 contracts its R
+        f32x16 R = {};
+        auto contract_r = [&]() {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4) {
+                    const float4 a4 = lds4(&sm.kp[m][32 * q + 16 * h + 4 * t4]);
+                    R = mfma32(a4.x, st[q][4 * t4], R);
+                    R = mfma32(a4.y, st[q][4 * t4 + 1], R);
+                    R = mfma32(a4.z, st[q][4 * t4 + 2], R);
+                    R = mfma32(a4.w, st[q][4 * t4 + 3], R);
+                }
+        };
+        if (w == 1) {
             // transposed: lane (node j = m, h), register r: s = crow(r, h)
             f32x16 ga = {};
             const float *ka = &sm.kp[m][64 * h];
@@ -199,7 +207,11 @@ __global__ __launch_bounds__(kThreads, 2) void commit_f32_kernel(
                 *reinterpret_cast<float4 *>(&sm.xd[m][8 * q4 + 4 * h]) =
                     make_float4(x[0], x[1], x[2], x[3]);
             }
-            wave_lds_sync();
+        } else {
+            contract_r();
+        }
+        lds_barrier();   // X in
+        if (w == 0) {
             if (h == 0) {
                 // lane m: column j = m of T, (I + X) T = I row by row
                 float t[32];
@@ -214,18 +226,9 @@ __global__ __launch_bounds__(kThreads, 2) void commit_f32_kernel(
 #pragma unroll
                 for (int i = 0; i < 32; ++i) sm.t[i][pj] = t[i];
             }
+        } else if (w == 1) {
+            contract_r();
         }
-        f32x16 R = {};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
-                const float4 a4 = lds4(&sm.kp[m][32 * q + 16 * h + 4 * t4]);
-                R = mfma32(a4.x, st[q][4 * t4], R);
-                R = mfma32(a4.y, st[q][4 * t4 + 1], R);
-                R = mfma32(a4.z, st[q][4 * t4 + 2], R);
-                R = mfma32(a4.w, st[q][4 * t4 + 3], R);
-            }
         lds_barrier();   // T in
 
         // ---- U = T beta (V - e^g R), W = e^{g_l - g} U, S <- e^{g_l} S + K_p^T W
