@@ -503,7 +503,7 @@ def test_commit_verify_matches_separate_calls(gpu_lib):
     (64, 100, 128, 128, "bf16", None),   # 65..128-node fused kernel, 32-slot chunks
     (8, 65, 128, 128, "bf16", None),     # 65..128-node fused kernel, one 16-slot chunk
     (37, 37, 64, 64, "fp32", None),      # generic commit + generic verify
-    (40, 64, 128, 128, "fp32", None),    # generic commit + fp32-MFMA verify ORing its flag
+    (40, 64, 128, 128, "fp32", None),    # fp32-MFMA commit, then fp32-MFMA verify ORing its flag
     (50, 30, 32, 48, "bf16", None),
 ])
 def test_commit_verify_shapes_and_faults(gpu_lib, n_prev, n, dk, dv, dtype, max_path):
