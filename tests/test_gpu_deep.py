@@ -631,3 +631,35 @@ def test_commit_verify_n128_faults(gpu_lib, max_path):
     assert np.isnan(oh[2:4]).all() and np.isnan(uh[2:4]).all()
     for b in (0, 1, 4):
         assert oracle.rel_err(oh[b], oref[b]) <= BF16_GATE, b
+
+
+# ---------------------------------------------------------------------------
+# more heads than the MFMA kernels' 32-bit buffer ranges take
+# ---------------------------------------------------------------------------
+def test_many_heads_take_the_generic_kernels(gpu_lib):
+    """4097 heads (past the MFMA kernels' limit of 4096, whose byte extents
+    must fit 32-bit buffer offsets): verify, commit and the fused call run
+    on the generic kernels and match the oracle"""
+    say("4097 heads")
+    par = np.stack([np.array([-1, 0, 1, 1], np.int32)])
+    prev = gs.make_set(par, 4097, 128, 128, "bf16", seed=44, accepted=np.array([3], np.int32))
+    cur = gs.make_set(par, 4097, 128, 128, "bf16", seed=45)
+    dp, dc = upload(prev), upload(cur)
+    path, plen = prev.paths(max_path=4)
+    out = gpu_lib.verify(dc["q"], dc["k"], dc["v"], dc["alpha"], dc["beta"], dc["parent"],
+                         dc["S0"])
+    ref, _ = oracle.verify_set(cur)
+    assert oracle.rel_err(host(out), ref) <= BF16_GATE
+    S = dp["S0"].clone()
+    gpu_lib.commit(S, dev(path), dev(plen), dp["k"], dp["v"], dp["alpha"], dp["beta"],
+                   dp["parent"])
+    Sref, _ = oracle.commit_set(prev, path_arr=path, path_len=plen)
+    assert oracle.rel_err(host(S), Sref) <= BF16_GATE
+    S2 = dp["S0"].clone()
+    out2 = gpu_lib.commit_verify(S2, dev(path), dev(plen),
+                                 (dp["k"], dp["v"], dp["alpha"], dp["beta"], dp["parent"]),
+                                 dc["q"], dc["k"], dc["v"], dc["alpha"], dc["beta"], dc["parent"])
+    torch.cuda.synchronize()
+    assert torch.equal(S2, S)
+    ref2, _ = oracle.verify(cur.q, cur.k, cur.v, cur.alpha, cur.beta, cur.parent, Sref)
+    assert oracle.rel_err(host(out2), ref2) <= BF16_GATE
