@@ -123,6 +123,7 @@ def test_commit_verify_null_pointer(lib, null):
     (dict(u_prev=MISALIGNED), -1), (dict(u_out=MISALIGNED), -1),
     (dict(u_out=FAKE), -2),        # pseudo-values out need bf16 q/k/v and d = 128
     (dict(u_out=FAKE, u_dtype=2), -2),
+    (dict(u_out=FAKE, dtype=0, dk=128, dv=128), -2),   # fp32 q/k/v: no pseudo-values out
     (dict(u_out=FAKE, u_dtype=1), -1),   # pseudo-values are fp32 or fp16
     (dict(u_prev=FAKE, u_dtype=3), -1),
 ])
