@@ -1,6 +1,7 @@
 """CPU checks of bench.py's contract: the algorithmic byte counts behind its
 roofline fractions, written out here from the tensor shapes of the batch-16,
-64-node, 32-head, d = 128 workload, and the one-GPU guard."""
+64-node, 32-head, d = 128 workload, the one-GPU guard, and that the
+committed traffic summary belongs to the fused kernel's current code."""
 import os
 import subprocess
 import sys
@@ -38,3 +39,12 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_committed_traffic_matches_the_current_fused_kernel():
+    """the committed rocprofv3 traffic summary was taken on the fused
+    kernel's current code (bench.py reports no traffic otherwise), and its
+    ratio to the algorithmic bytes stays near 1"""
+    t = bench.read_traffic(bench.HEADLINE_STEP)
+    assert t is not None, "profiles/ traffic summary is stale: re-take it"
+    assert 1.0 <= t / bench.fused_bytes(B, N, H, D, D, [139]) < 1.1
